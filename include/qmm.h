@@ -1,0 +1,195 @@
+/*
+ * qmm.h -- C ABI of libqmm: the prefill matrix multiply ("MMQ") of llama.cpp-style
+ * k-quant weights (q6_K, q4_K) against activations quantized to q8 blocks of 32,
+ * on AMD Instinct MI355X (gfx950).
+ *
+ *   out[t][j] = sum over k of  weight[j][k] * activation[t][k]
+ *
+ * computed the way the engineering log "minfer / cuda_optimization_steps"
+ * describes it (pages "48 - r45 - cp.async for the q6_K A-side staging",
+ * "59 - r56 - q6_K A-side bundle: A cp.async + W_dsc f32 plane", "61 - r58 -
+ * q4_K BT spec + cp.async-db2 transplant"): the activations are first quantized
+ * by a prepass into q8 blocks with a scale pair (r45 section 1.1), the weights
+ * are expanded once at registration into planes the kernel can copy without
+ * arithmetic (r56 sections 2.2-2.3, r58 section 3.2), and the GEMM forms exact
+ * integer dot products per 32-element block and applies the per-block scales in
+ * binary32.
+ *
+ * Conventions for every entry point:
+ *   - Return QMM_OK (0) on success or a negative QMM_E* code; qmm_last_error()
+ *     then names the problem.  No entry point ever falls back to another path.
+ *   - Every argument is validated before the first HIP call, so invalid calls
+ *     fail identically on machines with and without a GPU.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously on it; pointers the caller passes must stay
+ *     valid until that work completes.  The library keeps no caller pointer past
+ *     the call.
+ *   - Device pointers belong to the device that is current when the call is
+ *     made; a weights handle is bound to the device current at registration and
+ *     may only be used while that device is current.
+ *   - Handles are immutable after registration: concurrent qmm_mmq calls on
+ *     different streams may share one handle.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight block types. */
+#define QMM_Q4_K 4 /* 144-byte blocks of 256 weights: f16 d, f16 dmin, 12 bytes of
+                      6-bit scales and mins (8 sub-blocks of 32), 128 bytes of
+                      4-bit codes; weight = d*scale*code - dmin*min
+                      (r58 sections 2.2, 3.1). */
+#define QMM_Q6_K 6 /* 210-byte blocks of 256 weights: ql[128] low 4 bits,
+                      qh[64] high 2 bits, int8 scales[16] (one per 16 weights),
+                      f16 d; weight = d*scale*(code - 32)
+                      (r56 sections 1, 3.2; r58 section 3.2). */
+
+/* Return codes. */
+#define QMM_OK 0
+#define QMM_EINVAL (-1) /* bad argument: type, size, null or misaligned pointer */
+#define QMM_ESHAPE (-2) /* buffers that do not belong together (qact vs handle) */
+#define QMM_ENOMEM (-3) /* device memory could not be allocated; nothing leaked */
+#define QMM_EHIP (-4)   /* a HIP runtime call or kernel launch failed */
+
+/* Size limits (validated): 1 <= od <= QMM_MAX_OD, 256 <= id <= QMM_MAX_ID with
+ * id % 256 == 0, 1 <= n_tok <= QMM_MAX_TOKENS. */
+#define QMM_MAX_OD (1 << 21)
+#define QMM_MAX_ID (1 << 20)
+#define QMM_MAX_TOKENS (1 << 20)
+
+/* Tokens are padded to a multiple of this many in the qact buffer. */
+#define QMM_TOKEN_PAD 128
+
+typedef struct qmm_weights qmm_weights;
+
+typedef struct {
+    int type;            /* QMM_Q4_K or QMM_Q6_K */
+    int64_t od;          /* output rows */
+    int64_t id;          /* inner dimension */
+    int64_t od_pad;      /* rows padded with zeros to the row tile */
+    size_t raw_bytes;    /* od * (id/256) * (144 or 210): the k-quant bytes */
+    size_t plane_bytes;  /* device memory the handle holds */
+    size_t wd_offset;    /* byte offset of the d plane inside the planes */
+    size_t wm_offset;    /* byte offset of the -dmin*min plane (q4_K; else == plane_bytes) */
+} qmm_info;
+
+/*
+ * qmm_register_weights -- copy one k-quant weight matrix to the device and
+ * expand it once into the planes the GEMM reads (the registration-time planes
+ * of r56 section 2.2 and r58 section 3.2; layout: see qmm_weights_export).
+ *   type        QMM_Q4_K or QMM_Q6_K
+ *   od, id      the weight is od rows of id weights; id % 256 == 0.  Any od >= 1
+ *               (odd included) is valid: rows are padded with zeros internally.
+ *   host_bytes  host memory, od rows * (id/256) blocks, row major, exactly
+ *               nbytes = od * (id/256) * (144 or 210) bytes.  Copied; the caller
+ *               keeps ownership and may free it when the call returns.
+ *   stream      the copy and the expansion run on it; the call returns after
+ *               both completed (it synchronizes the stream).
+ *   out         receives the handle; release with qmm_release_weights.
+ * Errors: QMM_EINVAL (type, sizes, nullptrs, nbytes mismatch), QMM_ENOMEM (device
+ * memory or the cap of qmm_set_memory_cap), QMM_EHIP.  On error *out is left NULL
+ * and no device memory stays allocated.
+ */
+int qmm_register_weights(int type, int64_t od, int64_t id, const void *host_bytes,
+                         size_t nbytes, void *stream, qmm_weights **out);
+
+/* qmm_weights_info -- sizes of a handle.  QMM_EINVAL on null pointers. */
+int qmm_weights_info(const qmm_weights *w, qmm_info *out);
+
+/*
+ * qmm_weights_export -- copy a handle's device planes to host memory, for
+ * inspection and byte-exact tests (the r56 section 4 plane read-back gate).
+ * host must hold exactly bytes = info.plane_bytes.  Synchronous.
+ * Plane layout (R = od_pad/32 row blocks of 32 rows, nchunk = id/32, nsb =
+ * id/256; rows od..od_pad-1 are zero everywhere):
+ *   at 0          int8 [R][nchunk][2][2][32][16]: the scale-folded weight
+ *                 w = 64*hi + lo (lo in [0, 63]) of (row j, k) is split into
+ *                 hi (plane index p = 0) and lo (p = 1), byte at
+ *                 ((j/32*nchunk + k/32)*2 + p)*1024 + ((k%32)/16)*512
+ *                 + (j%32)*16 + k%16, with
+ *                   q6_K  w = scale[k/16] * (code - 32)
+ *                   q4_K  w = scale[(k/32) % 8] * code
+ *   at wd_offset  f32 [R][nsb][32]: d of (row, super-block)
+ *   at wm_offset  f32 [R][nchunk][32]: -(dmin * min) of (row, chunk), q4_K only
+ * Errors: QMM_EINVAL (null pointers, bytes mismatch), QMM_EHIP.
+ */
+int qmm_weights_export(const qmm_weights *w, void *host, size_t bytes);
+
+/* qmm_release_weights -- free a handle's device memory.  Not safe while work
+ * that uses the handle is still in flight: synchronize first.  NULL is a no-op. */
+void qmm_release_weights(qmm_weights *w);
+
+/*
+ * qmm_set_memory_cap -- upper bound on the device memory (bytes) that all live
+ * handles of this process may hold together; registration that would exceed
+ * it fails with QMM_ENOMEM before allocating.  0 removes the cap (default).
+ * For callers that budget HBM between several consumers.
+ */
+void qmm_set_memory_cap(size_t bytes);
+
+/*
+ * qmm_qact_bytes -- size of the quantized-activation buffer for n_tok tokens of
+ * id activations: T_pad * id * 9 / 8 with T_pad = n_tok rounded up to
+ * QMM_TOKEN_PAD.  Returns 0 if n_tok or id is out of range.
+ */
+size_t qmm_qact_bytes(int64_t n_tok, int64_t id);
+
+/*
+ * qmm_quantize_activations -- the quantize-transpose prepass (r45 section 1.1):
+ * f32 activations -> q8 blocks of 32 with a scale pair (r45 section 2.3: 32
+ * int8 values plus 4 bytes; r56 section 1: "d/ssum").
+ *   x           device f32 [n_tok][id], row major, 16-byte aligned.  Values
+ *               must be finite with |x| <= 2046 (so the scaled sum fits f16);
+ *               other values give unspecified (but memory-safe) results.
+ *   qact        device buffer of exactly qact_bytes = qmm_qact_bytes(n_tok, id)
+ *               bytes, 16-byte aligned, fully overwritten.
+ * Per token t and block c of 32 activations x_k:
+ *   amax = max |x_k|;  dh = f16(amax / 127)   (binary32 division, f16 round to
+ *   nearest even);  q_k = clamp(rint(x_k / dh), -127, 127) (binary32 division,
+ *   round half to even) or 0 when dh == 0;  s = f16(dh * sum q_k).
+ * Layout of qact (T_pad tokens; tokens >= n_tok are all zero; nchunk = id/32):
+ *   q plane at byte 0, 1024-byte fragments per (32-token block tb, chunk c):
+ *     q of (t, k) at ((t/32)*nchunk + k/32)*1024 + ((k%32)/16)*512
+ *                    + (t%32)*16 + k%16
+ *   scale plane at byte T_pad*id, 128 bytes per (tb, c):
+ *     (dh, s) of (t, c) at T_pad*id + ((t/32)*nchunk + c)*128 + (t%32)*4,
+ *     two little-endian binary16 values, dh first.
+ * Errors: QMM_EINVAL (sizes, null/misaligned pointers, qact_bytes mismatch),
+ * QMM_EHIP.
+ */
+int qmm_quantize_activations(const float *x, int64_t n_tok, int64_t id, void *qact,
+                             size_t qact_bytes, void *stream);
+
+/*
+ * qmm_mmq -- the GEMM: out[t][j] = sum over 32-blocks c of
+ *   q6_K: sum over the block's two 16-groups g of d*sc_g*dh_c*D16_g
+ *   q4_K: d*sc_c*dh_c*D32_c - dmin*min_c*s_c
+ * with D the exact integer dot of the weight codes (q6_K: code - 32) and the q8
+ * codes over the group (r56 section 2.2 for the q6_K d*sc pairs).  The integer
+ * parts are exact; the scales are applied and summed in binary32 (error within
+ * 1e-4 of the sum of the terms' magnitudes).
+ *   w           handle from qmm_register_weights (current device = its device)
+ *   qact        buffer written by qmm_quantize_activations for these n_tok and
+ *               the handle's id; qact_bytes must equal qmm_qact_bytes(n_tok,
+ *               id) or the call fails with QMM_ESHAPE.  16-byte aligned.
+ *   out         device f32 [n_tok][od], row major, 4-byte aligned; every element
+ *               is overwritten (no accumulation), nothing outside is written.
+ * Errors: QMM_EINVAL, QMM_ESHAPE, QMM_EHIP.
+ */
+int qmm_mmq(const qmm_weights *w, const void *qact, size_t qact_bytes, int64_t n_tok,
+            float *out, void *stream);
+
+/* qmm_last_error -- message for the calling thread's last failed call ("" if
+ * none).  Valid until the thread's next call into the library. */
+const char *qmm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMM_H */

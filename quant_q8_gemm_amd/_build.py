@@ -1,0 +1,46 @@
+"""Build libqmm.so (the C-ABI library) for gfx950 with hipcc, in-tree."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = [os.path.join(CSRC, "qmm_api.cpp"), os.path.join(CSRC, "qmm_kernels.hip")]
+LIB = os.path.join(HERE, "libqmm.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# Packed-FP32 VALU forms are disabled for the device code on purpose (the host
+# pass warns that it does not know the feature; that is harmless).
+DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17",
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def build(verbose: bool = False) -> str:
+    cmd = [HIPCC, *DEVICE_FLAGS, "-fPIC", "-shared", "-Wall", "-I", os.path.join(ROOT, "include"),
+           *SOURCES, "-o", LIB + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln and ln.strip()]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def device_asm(out_path: str) -> str:
+    """gfx950 assembly of the kernels (for inspection: instruction mix, VGPRs,
+    scratch), written to out_path."""
+    cmd = [HIPCC, *DEVICE_FLAGS, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"),
+           os.path.join(CSRC, "qmm_kernels.hip"), "-o", out_path]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc -S failed:\n" + r.stderr)
+    return out_path
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

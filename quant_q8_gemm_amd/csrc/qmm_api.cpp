@@ -1,0 +1,242 @@
+// qmm_api.cpp -- the C ABI declared in include/qmm.h: argument validation (all of
+// it before the first HIP call), weight-handle lifetime, device-memory
+// accounting, and the launches.  No compute happens here.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/qmm.h"
+#include "qmm_internal.h"
+
+struct qmm_weights {
+  qmm::Planes p;
+  int device;
+  size_t raw_bytes;
+  size_t plane_bytes;
+  size_t wd_offset;
+  size_t wm_offset;
+  void* alloc;  // one device allocation holding every plane
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<size_t> g_held{0};  // device bytes held by live handles
+std::atomic<size_t> g_cap{0};   // 0 = no cap
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  return fail(QMM_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void ok() { g_last_error.clear(); }
+
+size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
+
+size_t block_bytes(int type) { return type == QMM_Q4_K ? 144 : 210; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_id(int64_t id) {
+  if (id < 256 || id > QMM_MAX_ID || id % 256 != 0)
+    return fail(QMM_EINVAL, "id must be a multiple of 256 in [256, %d], got %lld", QMM_MAX_ID,
+                (long long)id);
+  return QMM_OK;
+}
+
+int check_tokens(int64_t n_tok) {
+  if (n_tok < 1 || n_tok > QMM_MAX_TOKENS)
+    return fail(QMM_EINVAL, "n_tok must be in [1, %d], got %lld", QMM_MAX_TOKENS, (long long)n_tok);
+  return QMM_OK;
+}
+
+int64_t token_pad(int64_t n_tok) { return (n_tok + qmm::kTokenPad - 1) / qmm::kTokenPad * qmm::kTokenPad; }
+
+}  // namespace
+
+extern "C" {
+
+const char* qmm_last_error(void) { return g_last_error.c_str(); }
+
+void qmm_set_memory_cap(size_t bytes) { g_cap.store(bytes); }
+
+size_t qmm_qact_bytes(int64_t n_tok, int64_t id) {
+  if (n_tok < 1 || n_tok > QMM_MAX_TOKENS || id < 256 || id > QMM_MAX_ID || id % 256 != 0) return 0;
+  return (size_t)token_pad(n_tok) * (size_t)id / 8 * 9;
+}
+
+int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_bytes, size_t nbytes,
+                         void* stream, qmm_weights** out) {
+  if (out == nullptr) return fail(QMM_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (type != QMM_Q4_K && type != QMM_Q6_K)
+    return fail(QMM_EINVAL, "type must be QMM_Q4_K (%d) or QMM_Q6_K (%d), got %d", QMM_Q4_K,
+                QMM_Q6_K, type);
+  if (od < 1 || od > QMM_MAX_OD)
+    return fail(QMM_EINVAL, "od must be in [1, %d], got %lld", QMM_MAX_OD, (long long)od);
+  if (int rc = check_id(id)) return rc;
+  if (host_bytes == nullptr) return fail(QMM_EINVAL, "host_bytes is NULL");
+  const size_t expect = (size_t)od * (size_t)(id / 256) * block_bytes(type);
+  if (nbytes != expect)
+    return fail(QMM_EINVAL, "nbytes %zu != od*(id/256)*%zu = %zu", nbytes, block_bytes(type), expect);
+
+  qmm::Planes p{};
+  p.type = type;
+  p.od = od;
+  p.id = id;
+  p.od_pad = (int64_t)round_up((size_t)od, qmm::kRowPad);
+  p.nsb = id / 256;
+  p.nchunk = id / 32;
+  const size_t off_wd = round_up(qmm::wq_bytes(p.od_pad, id), 256);
+  const size_t off_wm = off_wd + round_up(qmm::wd_bytes(p.od_pad, id), 256);
+  const size_t plane_bytes = off_wm + round_up(qmm::wm_bytes(type, p.od_pad, id), 256);
+  const size_t cap = g_cap.load();
+  if (cap != 0 && g_held.load() + plane_bytes > cap)
+    return fail(QMM_ENOMEM, "registration needs %zu device bytes; cap %zu, held %zu", plane_bytes,
+                cap, g_held.load());
+
+  // ---- first HIP call below this line ----
+  hipStream_t s = (hipStream_t)stream;
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  void* alloc = nullptr;
+  void* raw = nullptr;
+  e = hipMalloc(&alloc, plane_bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return e == hipErrorOutOfMemory ? fail(QMM_ENOMEM, "hipMalloc(%zu) failed: out of memory", plane_bytes)
+                                    : fail_hip(e, "hipMalloc(planes)");
+  }
+  e = hipMalloc(&raw, nbytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(alloc);
+    return e == hipErrorOutOfMemory ? fail(QMM_ENOMEM, "hipMalloc(%zu) failed: out of memory", nbytes)
+                                    : fail_hip(e, "hipMalloc(raw)");
+  }
+  p.wq = (int8_t*)alloc;
+  p.wd = (float*)((char*)alloc + off_wd);
+  p.wm = type == QMM_Q4_K ? (float*)((char*)alloc + off_wm) : nullptr;
+  int rc = QMM_OK;
+  if ((e = hipMemcpyAsync(raw, host_bytes, nbytes, hipMemcpyHostToDevice, s)) != hipSuccess)
+    rc = fail_hip(e, "hipMemcpyAsync(weights)");
+  else if ((e = qmm::launch_repack((const uint8_t*)raw, p, s)) != hipSuccess)
+    rc = fail_hip(e, "repack launch");
+  else if ((e = hipStreamSynchronize(s)) != hipSuccess)
+    rc = fail_hip(e, "hipStreamSynchronize(registration)");
+  (void)hipFree(raw);
+  if (rc != QMM_OK) {
+    (void)hipFree(alloc);
+    return rc;
+  }
+  qmm_weights* w = new qmm_weights;
+  w->p = p;
+  w->device = device;
+  w->raw_bytes = nbytes;
+  w->plane_bytes = plane_bytes;
+  w->wd_offset = off_wd;
+  w->wm_offset = type == QMM_Q4_K ? off_wm : plane_bytes;
+  w->alloc = alloc;
+  g_held += plane_bytes;
+  if (getenv("QMM_LOG") != nullptr)
+    fprintf(stderr, "qmm: registered %s od=%lld id=%lld od_pad=%lld raw=%zu planes=%zu device=%d\n",
+            type == QMM_Q4_K ? "q4_K" : "q6_K", (long long)od, (long long)id,
+            (long long)p.od_pad, nbytes, plane_bytes, device);
+  *out = w;
+  ok();
+  return QMM_OK;
+}
+
+int qmm_weights_info(const qmm_weights* w, qmm_info* out) {
+  if (w == nullptr || out == nullptr) return fail(QMM_EINVAL, "NULL handle or info pointer");
+  out->type = w->p.type;
+  out->od = w->p.od;
+  out->id = w->p.id;
+  out->od_pad = w->p.od_pad;
+  out->raw_bytes = w->raw_bytes;
+  out->plane_bytes = w->plane_bytes;
+  out->wd_offset = w->wd_offset;
+  out->wm_offset = w->wm_offset;
+  ok();
+  return QMM_OK;
+}
+
+int qmm_weights_export(const qmm_weights* w, void* host, size_t bytes) {
+  if (w == nullptr || host == nullptr) return fail(QMM_EINVAL, "NULL handle or host pointer");
+  if (bytes != w->plane_bytes)
+    return fail(QMM_EINVAL, "bytes %zu != plane_bytes %zu", bytes, w->plane_bytes);
+  int prev = -1;
+  hipError_t e = hipGetDevice(&prev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (prev != w->device && (e = hipSetDevice(w->device)) != hipSuccess) return fail_hip(e, "hipSetDevice");
+  e = hipMemcpy(host, w->alloc, bytes, hipMemcpyDeviceToHost);
+  if (prev != w->device) (void)hipSetDevice(prev);
+  if (e != hipSuccess) return fail_hip(e, "hipMemcpy(planes)");
+  ok();
+  return QMM_OK;
+}
+
+void qmm_release_weights(qmm_weights* w) {
+  if (w == nullptr) return;
+  int prev = -1;
+  if (hipGetDevice(&prev) == hipSuccess && prev != w->device) (void)hipSetDevice(w->device);
+  (void)hipFree(w->alloc);
+  if (prev >= 0 && prev != w->device) (void)hipSetDevice(prev);
+  g_held -= w->plane_bytes;
+  delete w;
+}
+
+int qmm_quantize_activations(const float* x, int64_t n_tok, int64_t id, void* qact,
+                             size_t qact_bytes, void* stream) {
+  if (int rc = check_tokens(n_tok)) return rc;
+  if (int rc = check_id(id)) return rc;
+  if (x == nullptr || qact == nullptr) return fail(QMM_EINVAL, "x or qact is NULL");
+  if (!aligned(x, 16) || !aligned(qact, 16)) return fail(QMM_EINVAL, "x and qact must be 16-byte aligned");
+  const size_t need = qmm_qact_bytes(n_tok, id);
+  if (qact_bytes != need)
+    return fail(QMM_EINVAL, "qact_bytes %zu != qmm_qact_bytes(%lld, %lld) = %zu", qact_bytes,
+                (long long)n_tok, (long long)id, need);
+  hipError_t e = qmm::launch_quantize(x, n_tok, token_pad(n_tok), id, (uint8_t*)qact,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "quantize launch");
+  ok();
+  return QMM_OK;
+}
+
+int qmm_mmq(const qmm_weights* w, const void* qact, size_t qact_bytes, int64_t n_tok, float* out,
+            void* stream) {
+  if (w == nullptr) return fail(QMM_EINVAL, "NULL weights handle");
+  if (int rc = check_tokens(n_tok)) return rc;
+  if (qact == nullptr || out == nullptr) return fail(QMM_EINVAL, "qact or out is NULL");
+  if (!aligned(qact, 16)) return fail(QMM_EINVAL, "qact must be 16-byte aligned");
+  if (!aligned(out, 4)) return fail(QMM_EINVAL, "out must be 4-byte aligned");
+  const size_t need = qmm_qact_bytes(n_tok, w->p.id);
+  if (qact_bytes != need)
+    return fail(QMM_ESHAPE, "qact_bytes %zu does not match n_tok=%lld and the handle's id=%lld (%zu)",
+                qact_bytes, (long long)n_tok, (long long)w->p.id, need);
+  int device = -1;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (device != w->device)
+    return fail(QMM_EINVAL, "handle belongs to device %d but device %d is current", w->device, device);
+  e = qmm::launch_mmq(w->p, (const uint8_t*)qact, n_tok, token_pad(n_tok), out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "mmq launch");
+  ok();
+  return QMM_OK;
+}
+
+}  // extern "C"

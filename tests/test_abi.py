@@ -1,0 +1,113 @@
+"""CPU-only checks of the C ABI: the library loads, exports every entry point the
+header declares, sizes the qact buffer as documented, and rejects invalid
+arguments before touching HIP (so these run on machines without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quant_q8_gemm_amd as qmm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding_list():
+    assert _declared() == sorted(qmm.EXPORTS)
+
+
+@pytest.mark.parametrize("name", _declared())
+def test_library_exports_every_declared_symbol(name):
+    lib = ctypes.CDLL(qmm.LIB_PATH)
+    assert hasattr(lib, name)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (QMM_[A-Z0-9_]+) \(?(-?\d+)\)?", text))
+    assert int(consts["QMM_Q4_K"]) == qmm.Q4_K and int(consts["QMM_Q6_K"]) == qmm.Q6_K
+    assert int(consts["QMM_EINVAL"]) == qmm.EINVAL and int(consts["QMM_ESHAPE"]) == qmm.ESHAPE
+    assert int(consts["QMM_ENOMEM"]) == qmm.ENOMEM and int(consts["QMM_EHIP"]) == qmm.EHIP
+    assert int(consts["QMM_TOKEN_PAD"]) == qmm.TOKEN_PAD
+
+
+@pytest.mark.parametrize("n_tok,id_,expect", [
+    (1, 256, 128 * 256 * 9 // 8), (128, 256, 128 * 256 * 9 // 8), (129, 512, 256 * 512 * 9 // 8),
+    (509, 11008, 512 * 11008 * 9 // 8), (3314, 4096, 3328 * 4096 * 9 // 8),
+    (0, 256, 0), (5, 100, 0), (5, 288, 0), (5, 0, 0), (-1, 256, 0)])
+def test_qact_bytes(n_tok, id_, expect):
+    assert qmm.qact_bytes(n_tok, id_) == expect
+
+
+def _reg(type_, od, id_, nbytes=None, ptr=True):
+    L = qmm._lib
+    buf = np.zeros(max(nbytes or 0, 1), np.uint8)
+    h = ctypes.c_void_p()
+    rc = L.qmm_register_weights(type_, od, id_, buf.ctypes.data_as(ctypes.c_void_p) if ptr else None,
+                                nbytes if nbytes is not None else 0, None, ctypes.byref(h))
+    return rc, h.value
+
+
+@pytest.mark.parametrize("type_,od,id_,nbytes", [
+    (5, 4, 256, 4 * 210), (qmm.Q6_K, 0, 256, 0), (qmm.Q6_K, 4, 255, 4 * 210),
+    (qmm.Q6_K, 4, 384, 4 * 210), (qmm.Q4_K, 4, 256, 4 * 210), (qmm.Q6_K, 4, 256, 4 * 210 - 1),
+    (qmm.Q6_K, (1 << 21) + 1, 256, 0), (qmm.Q4_K, 3, 1 << 21, 0)])
+def test_register_rejects_bad_arguments(type_, od, id_, nbytes):
+    rc, h = _reg(type_, od, id_, nbytes)
+    assert rc == qmm.EINVAL and h is None
+    assert qmm.last_error()
+
+
+def test_register_rejects_null_pointers():
+    rc, _ = _reg(qmm.Q6_K, 1, 256, 210, ptr=False)
+    assert rc == qmm.EINVAL
+    buf = np.zeros(210, np.uint8)
+    rc = qmm._lib.qmm_register_weights(qmm.Q6_K, 1, 256, buf.ctypes.data_as(ctypes.c_void_p), 210,
+                                       None, None)
+    assert rc == qmm.EINVAL
+
+
+def test_memory_cap_fails_before_allocating():
+    qmm.set_memory_cap(1000)
+    try:
+        rc, h = _reg(qmm.Q6_K, 4, 256, 4 * 210)
+        assert rc == qmm.ENOMEM and h is None
+        assert "cap" in qmm.last_error()
+    finally:
+        qmm.set_memory_cap(0)
+
+
+def test_quantize_rejects_bad_arguments():
+    L = qmm._lib
+    good = ctypes.c_void_p(4096)
+    n = qmm.qact_bytes(4, 256)
+    assert L.qmm_quantize_activations(good, 0, 256, good, n, None) == qmm.EINVAL
+    assert L.qmm_quantize_activations(good, 4, 300, good, n, None) == qmm.EINVAL
+    assert L.qmm_quantize_activations(None, 4, 256, good, n, None) == qmm.EINVAL
+    assert L.qmm_quantize_activations(good, 4, 256, None, n, None) == qmm.EINVAL
+    assert L.qmm_quantize_activations(ctypes.c_void_p(4100), 4, 256, good, n, None) == qmm.EINVAL
+    assert L.qmm_quantize_activations(good, 4, 256, ctypes.c_void_p(4104), n, None) == qmm.EINVAL
+    assert L.qmm_quantize_activations(good, 4, 256, good, n - 1, None) == qmm.EINVAL
+    assert "qact_bytes" in qmm.last_error()
+
+
+def test_mmq_rejects_bad_arguments():
+    L = qmm._lib
+    good = ctypes.c_void_p(4096)
+    assert L.qmm_mmq(None, good, 100, 4, good, None) == qmm.EINVAL
+
+
+def test_info_and_export_reject_null():
+    L = qmm._lib
+    info = qmm.Info()
+    assert L.qmm_weights_info(None, ctypes.byref(info)) == qmm.EINVAL
+    assert L.qmm_weights_export(None, ctypes.c_void_p(4096), 10) == qmm.EINVAL
+    L.qmm_release_weights(None)  # no-op

@@ -1,0 +1,337 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+* prepass bytes (q codes, dh, s) bit-exact, padded tokens zero;
+* registration planes byte-exact against the oracle's decode;
+* integer dots bit-exact through the production kernel (unit super-scales and
+  integer activations make every output an exact integer below 2^24);
+* f32 results within 1e-4 * sum|terms| of the oracle, on every element at small
+  sizes spanning several tiles and a ragged tail, and on sampled elements at the
+  full workload sizes in the same launch configuration the benchmark times;
+* odd row counts / token tails are bit-identical prefixes, repeat runs are
+  bit-identical, nothing outside the output is written.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import quant_q8_gemm_amd as qmm  # noqa: E402
+import synth  # noqa: E402
+from tests import layouts  # noqa: E402
+from tests.kq_blocks import q4k_block, q6k_block  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_quantize(x: np.ndarray):
+    xt = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    qact = qmm.quantize_activations(xt)
+    return qact
+
+
+def check_prepass(x: np.ndarray, qact):
+    n_tok, id_ = x.shape
+    q, dh, s = layouts.read_qact(qact.cpu().numpy(), n_tok, id_)
+    oq, odh, os_ = oracle.quantize(x)
+    assert np.array_equal(q[:n_tok], oq), "q codes differ"
+    assert np.array_equal(dh[:n_tok], odh), "dh differs"
+    assert np.array_equal(s[:n_tok], os_), "s differs"
+    assert not q[n_tok:].any() and not dh[n_tok:].any() and not s[n_tok:].any(), "padding not zero"
+    return oq, odh, os_
+
+
+def run_mmq(w, qact, n_tok, poison=True):
+    out = torch.empty((n_tok, w.od), dtype=torch.float32, device="cuda")
+    if poison:
+        out.fill_(float("nan"))
+    qmm.mmq(w, qact, n_tok, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_close(got, ref, A, where=""):
+    err = np.abs(got.astype(np.float64) - ref)
+    bad = ~(err <= TOL * A)
+    assert not np.isnan(got).any(), f"NaN in output {where}"
+    assert not bad.any(), (f"{bad.sum()} elements beyond tolerance {where}; worst "
+                           f"err={err[bad].max():.3e} A={A[bad][np.argmax(err[bad])]:.3e}")
+
+
+# --------------------------------------------------------------------------
+# prepass
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n_tok,id_,outliers", [(64, 512, False), (13, 768, True), (1, 256, False),
+                                                (509, 11008, False), (130, 4096, True)])
+def test_prepass_bytes_exact(n_tok, id_, outliers):
+    say(f"prepass n_tok={n_tok} id={id_}")
+    x = synth.activations(np.random.default_rng(n_tok), n_tok, id_, outliers)
+    check_prepass(x, gpu_quantize(x))
+
+
+def test_prepass_special_values():
+    say("prepass special values")
+    x = np.zeros((6, 256), np.float32)
+    step = np.float32(0.0625)
+    x[0, 0] = 127 * step                                   # exact scale, then half-way ties
+    x[0, 1:9] = np.array([0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, 126.5], np.float32) * step
+    x[1, :32] = 1e-6                                       # scale rounds to zero
+    x[1, 32] = 2e-5                                        # subnormal f16 scale
+    x[1, 33] = -1e-5
+    x[2, :] = 2046.0 * np.sign(np.random.default_rng(1).standard_normal(256)).astype(np.float32)
+    x[3, :] = -0.0
+    x[4, ::2] = 1.0
+    x[5, :] = np.random.default_rng(2).uniform(-2046, 2046, 256).astype(np.float32)
+    check_prepass(x, gpu_quantize(x))
+
+
+# --------------------------------------------------------------------------
+# registration planes
+# --------------------------------------------------------------------------
+
+def _full_range_q6k(rng, od, id_):
+    raw = synth.q6k_weights(rng, od, id_).reshape(-1, 210).copy()
+    raw[:, 192:208] = rng.integers(-128, 128, size=(raw.shape[0], 16), dtype=np.int8).view(np.uint8)
+    return raw.reshape(-1)
+
+
+def expected_planes(type_, raw, od, id_):
+    if type_ == synth.Q6_K:
+        w6, sc, d = oracle.decode_q6k(raw, od, id_)
+        w = w6.astype(np.int32) * np.repeat(sc.astype(np.int32), 16, axis=1)
+        return w, d, None
+    w4, sc, mn, d, dm = oracle.decode_q4k(raw, od, id_)
+    w = w4.astype(np.int32) * np.repeat(sc.astype(np.int32), 32, axis=1)
+    wm = -(np.repeat(dm, 8, axis=1) * mn.astype(np.float32))
+    return w, d, wm
+
+
+@pytest.mark.parametrize("type_,od,id_,full", [(synth.Q6_K, 5, 512, False), (synth.Q6_K, 130, 768, True),
+                                               (synth.Q4_K, 37, 512, False), (synth.Q4_K, 129, 1024, False)])
+def test_planes_byte_exact(type_, od, id_, full):
+    say(f"planes type={type_} od={od} id={id_}")
+    rng = np.random.default_rng(od)
+    raw = _full_range_q6k(rng, od, id_) if full else synth.weights(rng, type_, od, id_)
+    w = qmm.register_weights(type_, od, id_, raw)
+    assert w.od_pad % 128 == 0 and w.od_pad >= od
+    gw, gd, gwm = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.wm_offset)
+    ew, ed, ewm = expected_planes(type_, raw, od, id_)
+    assert np.array_equal(gw[:od], ew)
+    assert np.array_equal(gd[:od].view(np.uint32), ed.view(np.uint32))
+    assert not gw[od:].any() and not gd[od:].any()
+    if type_ == synth.Q4_K:
+        assert np.array_equal(gwm[:od].view(np.uint32), ewm.astype(np.float32).view(np.uint32))
+        assert not gwm[od:].any()
+    w.release()
+
+
+# --------------------------------------------------------------------------
+# integer dots through the production kernel
+# --------------------------------------------------------------------------
+
+def _int_acts(rng, T, id_):
+    x = rng.integers(-127, 128, size=(T, id_)).astype(np.float32)
+    x.reshape(T, -1, 32)[:, :, 0] = np.where(rng.random((T, id_ // 32)) < 0.5, 127, -127)
+    return x
+
+
+@pytest.mark.parametrize("type_", [synth.Q6_K, synth.Q4_K])
+def test_int_dots_exact_unit_scale(type_):
+    od, id_, T = 200, 512, 77
+    say(f"int dots unit type={type_} od={od} T={T}")
+    rng = np.random.default_rng(5)
+    nb = od * id_ // 256
+    if type_ == synth.Q6_K:
+        blocks = [q6k_block(ql=rng.integers(0, 256, 128, dtype=np.uint8),
+                            qh=rng.integers(0, 256, 64, dtype=np.uint8),
+                            sc=rng.integers(-2, 3, 16).astype(np.int8)) for _ in range(nb)]
+    else:
+        blocks = []
+        for _ in range(nb):
+            sc = np.zeros(12, np.uint8)
+            sc[0:4] = rng.integers(0, 4, 4)          # scales 0..3 of sub-blocks 0..3, mins 0
+            sc[8:12] = rng.integers(0, 4, 4)         # scales of sub-blocks 4..7
+            blocks.append(q4k_block(dmin_bits=0x3C00, scales=sc,
+                                    qs=rng.integers(0, 256, 128, dtype=np.uint8)))
+    raw = np.concatenate(blocks)
+    x = _int_acts(rng, T, id_)
+    w = qmm.register_weights(type_, od, id_, raw)
+    qact = gpu_quantize(x)
+    q, dh, s = check_prepass(x, qact)
+    assert np.all(dh == 0x3C00)
+    got = run_mmq(w, qact, T)
+    ref, _ = oracle.mmq(type_, raw, od, id_, q, dh, s)
+    assert np.all(np.abs(ref) < 2 ** 24)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("type_", [synth.Q6_K, synth.Q4_K])
+def test_int_dots_exact_full_range_one_chunk(type_):
+    """Full-range scales; each token is non-zero in one 32-block only, so every
+    output equals one scale-folded block dot J exactly."""
+    od, id_, T = 160, 768, 96
+    say(f"int dots full range type={type_}")
+    rng = np.random.default_rng(6)
+    nb = od * id_ // 256
+    if type_ == synth.Q6_K:
+        raw = _full_range_q6k(rng, od, id_).reshape(nb, 210)
+        raw[:, 208:210] = np.array([0x00, 0x3C], np.uint8)  # d = 1
+    else:
+        raw = synth.q4k_weights(rng, od, id_).reshape(nb, 144)
+        raw[:, 0:4] = np.array([0x00, 0x3C, 0x00, 0x00], np.uint8)  # d = 1, dmin = 0
+    raw = raw.reshape(-1)
+    nchunk = id_ // 32
+    x = np.zeros((T, id_), np.float32)
+    chunk = np.arange(T) % nchunk
+    for t in range(T):
+        blk = rng.integers(-127, 128, 32).astype(np.float32)
+        blk[rng.integers(0, 32)] = 127 if t % 2 else -127
+        x[t, 32 * chunk[t]: 32 * chunk[t] + 32] = blk
+    w = qmm.register_weights(type_, od, id_, raw)
+    qact = gpu_quantize(x)
+    q, dh, s = check_prepass(x, qact)
+    got = run_mmq(w, qact, T)
+    if type_ == synth.Q6_K:
+        _, J = oracle.dots_q6k(raw, od, id_, q)
+        ref = J[np.arange(T), :, chunk].astype(np.float64)
+    else:
+        D32 = oracle.dots_q4k(raw, od, id_, q)
+        _, sc, _, _, _ = oracle.decode_q4k(raw, od, id_)
+        ref = (D32[np.arange(T), :, chunk].astype(np.int64) * sc[:, chunk].T.astype(np.int64)).astype(np.float64)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+# --------------------------------------------------------------------------
+# f32 results
+# --------------------------------------------------------------------------
+
+SMALL = [("C1 q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
+         ("q4_K 300x768 T=77", synth.Q4_K, 300, 768, 77, True),
+         ("q6_K 129x1280 T=200", synth.Q6_K, 129, 1280, 200, True),
+         ("q4_K 1x256 T=1", synth.Q4_K, 1, 256, 1, False),
+         ("q6_K 33x2304 T=130", synth.Q6_K, 33, 2304, 130, False),
+         ("q4_K 520x1536 T=257", synth.Q4_K, 520, 1536, 257, False)]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_all_elements(case):
+    name, type_, od, id_, T, outl = case
+    say(f"small {name}")
+    raw, x = synth.case(type_, od, id_, T, seed=0, outliers=outl)
+    w = qmm.register_weights(type_, od, id_, raw)
+    qact = gpu_quantize(x)
+    q, dh, s = check_prepass(x, qact)
+    got = run_mmq(w, qact, T)
+    ref, A = oracle.mmq(type_, raw, od, id_, q, dh, s)
+    check_close(got, ref, A, name)
+
+
+def _sample_pairs(rng, T, od, n=3000):
+    ts = list(rng.integers(0, T, n))
+    js = list(rng.integers(0, od, n))
+    edge_t = [0, T - 1, min(T - 1, 31), min(T - 1, 32), min(T - 1, 127), min(T - 1, 128)]
+    edge_j = [0, od - 1, min(od - 1, 31), min(od - 1, 32), min(od - 1, 127), min(od - 1, 128)]
+    for a in edge_t:
+        for b in edge_j:
+            ts.append(a)
+            js.append(b)
+    order = np.argsort(js, kind="stable")
+    return np.array(ts)[order], np.array(js)[order]
+
+
+FULL = [synth.C2, synth.C2_ODD, synth.C3_QKVO, synth.C3_GU, synth.C4]
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=[c[0] for c in FULL])
+def test_full_size_sampled(cfg):
+    name, type_, od, id_, T, outl = cfg
+    say(f"full size {name}: generating")
+    raw, x = synth.case(type_, od, id_, T, seed=0, outliers=outl)
+    say(f"full size {name}: register + prepass")
+    w = qmm.register_weights(type_, od, id_, raw)
+    qact = gpu_quantize(x)
+    q, dh, s = check_prepass(x, qact)
+    say(f"full size {name}: mmq")
+    got = run_mmq(w, qact, T)
+    assert not np.isnan(got).any()
+    ts, js = _sample_pairs(np.random.default_rng(1), T, od)
+    ref, A = oracle.mmq_at(type_, raw, od, id_, q, dh, s, ts, js)
+    check_close(got[ts, js], ref, A, name)
+    w.release()
+
+
+# --------------------------------------------------------------------------
+# properties
+# --------------------------------------------------------------------------
+
+def test_odd_rows_and_token_tail_are_prefixes_and_repeatable():
+    name, type_, od, id_, T, _ = synth.C2
+    say("prefix properties at the ffn_down shape")
+    raw, x = synth.case(type_, od + 1, id_, T, seed=3)
+    w_odd = qmm.register_weights(type_, od + 1, id_, raw)
+    w_even = qmm.register_weights(type_, od, id_, raw[: od * (id_ // 256) * 210])
+    qact = gpu_quantize(x)
+    out_odd = run_mmq(w_odd, qact, T)
+    out_even = run_mmq(w_even, qact, T)
+    assert np.array_equal(out_odd[:, :od], out_even)
+    again = run_mmq(w_odd, qact, T)
+    assert np.array_equal(again, out_odd)
+    qact509 = gpu_quantize(x[:509])
+    out509 = run_mmq(w_odd, qact509, 509)
+    assert np.array_equal(out509, out_odd[:509])
+
+
+def test_writes_stay_inside_output():
+    type_, od, id_, T = synth.Q4_K, 77, 512, 45
+    say("output bounds")
+    raw, x = synth.case(type_, od, id_, T, seed=4)
+    w = qmm.register_weights(type_, od, id_, raw)
+    qact = gpu_quantize(x)
+    big = torch.full((T * od + 4096,), 12345.0, dtype=torch.float32, device="cuda")
+    big[: T * od].fill_(float("nan"))
+    qmm.mmq(w, qact, T, out=big[: T * od].view(T, od))
+    torch.cuda.synchronize()
+    b = big.cpu().numpy()
+    assert not np.isnan(b[: T * od]).any()
+    assert np.all(b[T * od:] == 12345.0)
+
+
+def test_shape_mismatch_and_memory_cap():
+    say("error paths")
+    raw, x = synth.case(synth.Q6_K, 8, 512, 4, seed=1)
+    w = qmm.register_weights(synth.Q6_K, 8, 512, raw)
+    x2 = np.zeros((4, 768), np.float32)
+    qact = gpu_quantize(x2)
+    out = torch.empty((4, 8), dtype=torch.float32, device="cuda")
+    with pytest.raises(qmm.QmmError) as e:
+        qmm.mmq(w, qact, 4, out=out)
+    assert e.value.code == qmm.ESHAPE
+    qmm.set_memory_cap(w.plane_bytes + 1)
+    try:
+        with pytest.raises(qmm.QmmError) as e:
+            qmm.register_weights(synth.Q6_K, 8, 512, raw)
+        assert e.value.code == qmm.ENOMEM
+    finally:
+        qmm.set_memory_cap(0)
+    w2 = qmm.register_weights(synth.Q6_K, 8, 512, raw)
+    w2.release()
+    w.release()
