@@ -203,145 +203,207 @@ hipError_t launch_quantize(const float* x, int64_t n_tok, int64_t t_pad, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// MMQ.  Work-group = 4 waves in a 2 x 2 arrangement; each wave owns RB 32-row
-// blocks x TB 32-token blocks of the output and streams every chunk of the
-// inner dimension straight from the fragment-order planes into registers.
+// MMQ.  Work-group = 8 waves (two per SIMD) on a 64-row x 128-token output tile:
+// a 2 x 4 grid of 32 x 32 blocks, one block per wave.  The inner dimension is
+// walked one 256-wide super-block at a time; each super-block's operands (both
+// weight planes for the 2 row blocks, the q8 codes and scale pairs for the 4
+// token blocks, d, and for q4_K the -dmin*min plane) are copied once per
+// work-group into LDS and read from there by the waves that share them.  The
+// LDS is double-buffered: the global loads for super-block b+1 are issued
+// before super-block b is computed and written to the other buffer after it,
+// so there is one barrier per super-block.
 // MFMA orientation: A = weights (rows j), B = activations (columns t), so each
 // lane's 16 outputs share one token: the activation scale dh is one register
 // per chunk, and the super-block d is applied once per 8 chunks.
 // ---------------------------------------------------------------------------
-template <int TYPE, int RB, int TB>
-__global__ void __launch_bounds__(256)
+constexpr int kWavesR = 2;                 // row blocks per work-group
+constexpr int kWavesT = 4;                 // token blocks per work-group
+constexpr int kTileRows = 32 * kWavesR;    // 64
+constexpr int kTileToks = 32 * kWavesT;    // 128
+constexpr int kThreads = 64 * kWavesR * kWavesT;
+
+struct alignas(16) Stage {
+  int8_t a[kWavesR][8][2][1024];   // weight planes: [row block][chunk][hi, lo][fragment]
+  int8_t b[kWavesT][8][1024];      // q8 codes: [token block][chunk][fragment]
+  uint32_t s[kWavesT][8][32];      // (dh, s) pairs: [token block][chunk][token]
+  float d[kWavesR][32];            // super-block d per row
+  float m[kWavesR][8][32];         // -dmin*min per (chunk, row); q4_K only
+};
+static_assert(sizeof(Stage) % 16 == 0, "stage must be a whole number of 16-byte units");
+
+// 16-byte units of each stage section, and how many each thread copies.
+constexpr int kUnitsA = kWavesR * 8 * 2 * 1024 / 16;  // 2048
+constexpr int kUnitsB = kWavesT * 8 * 1024 / 16;      // 2048
+constexpr int kUnitsS = kWavesT * 8 * 32 * 4 / 16;    // 256
+constexpr int kUnitsD = kWavesR * 32 * 4 / 16;        // 16
+constexpr int kUnitsM = kWavesR * 8 * 32 * 4 / 16;    // 128
+static_assert(kUnitsA % kThreads == 0 && kUnitsB % kThreads == 0, "even A/B split");
+constexpr int kPerA = kUnitsA / kThreads;             // 4
+constexpr int kPerB = kUnitsB / kThreads;             // 4
+
+// Work-group index -> (row tile, token tile).  Work-groups are dispatched
+// round-robin over the 8 XCDs (each with its own L2); this map gives every XCD
+// a contiguous run of tiles in row-major (row tile, token tile) order, so the
+// work-groups that stream the same weight rows share one L2.
+__device__ __forceinline__ int xcd_swizzle(int i, int n) {
+  const int q = n / 8, r = n % 8;
+  const int x = i % 8, slot = i / 8;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + slot;
+}
+
+template <int TYPE>
+__global__ void __launch_bounds__(kThreads)
 mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
            const float* __restrict__ wm, const uint8_t* __restrict__ qq,
            const uint8_t* __restrict__ qs, int nchunk, int nsb, int od, int n_tok,
-           int row_tiles, float* __restrict__ out) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rt = blockIdx.x % row_tiles;
-  const int tt = blockIdx.x / row_tiles;
-  const int rb0 = (rt * 2 + (wave >> 1)) * RB;
-  const int tb0 = (tt * 2 + (wave & 1)) * TB;
+           int tok_tiles, int vec_store, float* __restrict__ out) {
+  __shared__ Stage stage[2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = wave / kWavesT, wt = wave % kWavesT;
+  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int rt = tile / tok_tiles, tt = tile % tok_tiles;
+  const int rb0 = rt * kWavesR, tb0 = tt * kWavesT;
 
-  const int8_t* pa[RB];
-  const float* pd[RB];
-  const float* pm[RB];
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    pa[r] = wq + (size_t)(rb0 + r) * nchunk * 2048 + lane * 16;
-    pd[r] = wd + (size_t)(rb0 + r) * nsb * 32 + 4 * (lane >> 5);
-    pm[r] = TYPE == QMM_Q4_K ? wm + (size_t)(rb0 + r) * nchunk * 32 + lane : nullptr;
-  }
-  const uint8_t* pb[TB];
-  const uint8_t* ps[TB];
-  const uint8_t* pss[TB];
-#pragma unroll
-  for (int t = 0; t < TB; ++t) {
-    pb[t] = qq + (size_t)(tb0 + t) * nchunk * 1024 + lane * 16;
-    ps[t] = qs + (size_t)(tb0 + t) * nchunk * 128 + (lane & 31) * 4;
-    pss[t] = qs + (size_t)(tb0 + t) * nchunk * 128 + (lane >> 5) * 128 + (lane & 31) * 4 + 2;
-  }
+  // Global sources of one stage (super-block b adds b times the per-super-block
+  // stride).  Copy unit u of the weight section lies in row block u / 1024 (16 KB
+  // contiguous per row block); unit u of the code section in token block u / 512.
+  static_assert(kPerA == 4 && kPerB == 4, "the copy code below moves 4 + 4 units per thread");
+  const int8_t* ga0 = wq + ((size_t)(rb0 + (tid + 0 * kThreads) / 1024) * nchunk) * 2048 + (size_t)((tid + 0 * kThreads) % 1024) * 16;
+  const int8_t* ga1 = wq + ((size_t)(rb0 + (tid + 1 * kThreads) / 1024) * nchunk) * 2048 + (size_t)((tid + 1 * kThreads) % 1024) * 16;
+  const int8_t* ga2 = wq + ((size_t)(rb0 + (tid + 2 * kThreads) / 1024) * nchunk) * 2048 + (size_t)((tid + 2 * kThreads) % 1024) * 16;
+  const int8_t* ga3 = wq + ((size_t)(rb0 + (tid + 3 * kThreads) / 1024) * nchunk) * 2048 + (size_t)((tid + 3 * kThreads) % 1024) * 16;
+  const uint8_t* gb0 = qq + ((size_t)(tb0 + (tid + 0 * kThreads) / 512) * nchunk) * 1024 + (size_t)((tid + 0 * kThreads) % 512) * 16;
+  const uint8_t* gb1 = qq + ((size_t)(tb0 + (tid + 1 * kThreads) / 512) * nchunk) * 1024 + (size_t)((tid + 1 * kThreads) % 512) * 16;
+  const uint8_t* gb2 = qq + ((size_t)(tb0 + (tid + 2 * kThreads) / 512) * nchunk) * 1024 + (size_t)((tid + 2 * kThreads) % 512) * 16;
+  const uint8_t* gb3 = qq + ((size_t)(tb0 + (tid + 3 * kThreads) / 512) * nchunk) * 1024 + (size_t)((tid + 3 * kThreads) % 512) * 16;
+  const uint8_t* gs = qs + ((size_t)(tb0 + tid / 64) * nchunk) * 128 + (size_t)(tid % 64) * 16;
+  const float* gd = wd + ((size_t)(rb0 + tid / 8) * nsb) * 32 + (tid % 8) * 4;
+  const float* gm = TYPE == QMM_Q4_K
+      ? wm + ((size_t)(rb0 + (tid & 127) / 64) * nchunk) * 32 + ((tid & 127) % 64) * 4
+      : nullptr;
 
-  v16f acc[RB][TB];
-  v16f inner[RB][TB];
-#pragma unroll
-  for (int r = 0; r < RB; ++r)
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[r][t][i] = 0.0f;
+  uint4 ra0, ra1, ra2, ra3, rb_0, rb_1, rb_2, rb_3, rs, rd, rm;
+  // Global -> registers for super-block b (issued early, consumed after compute).
+#define QMM_LOAD_STAGE(b)                                                               \
+  do {                                                                                  \
+    const size_t oa = (size_t)(b) * 16384, ob = (size_t)(b) * 8192;                     \
+    ra0 = *(const uint4*)(ga0 + oa);                                                    \
+    ra1 = *(const uint4*)(ga1 + oa);                                                    \
+    ra2 = *(const uint4*)(ga2 + oa);                                                    \
+    ra3 = *(const uint4*)(ga3 + oa);                                                    \
+    rb_0 = *(const uint4*)(gb0 + ob);                                                   \
+    rb_1 = *(const uint4*)(gb1 + ob);                                                   \
+    rb_2 = *(const uint4*)(gb2 + ob);                                                   \
+    rb_3 = *(const uint4*)(gb3 + ob);                                                   \
+    if (tid < kUnitsS) rs = *(const uint4*)(gs + (size_t)(b) * 1024);                   \
+    if (tid < kUnitsD) rd = *(const uint4*)(gd + (size_t)(b) * 32);                     \
+    if (TYPE == QMM_Q4_K && tid < kUnitsM) rm = *(const uint4*)(gm + (size_t)(b) * 256); \
+  } while (0)
+  // Registers -> LDS stage st.
+#define QMM_STORE_STAGE(st)                                                             \
+  do {                                                                                  \
+    uint4* da = (uint4*)(st).a;                                                         \
+    uint4* db = (uint4*)(st).b;                                                         \
+    da[tid + 0 * kThreads] = ra0;                                                       \
+    da[tid + 1 * kThreads] = ra1;                                                       \
+    da[tid + 2 * kThreads] = ra2;                                                       \
+    da[tid + 3 * kThreads] = ra3;                                                       \
+    db[tid + 0 * kThreads] = rb_0;                                                      \
+    db[tid + 1 * kThreads] = rb_1;                                                      \
+    db[tid + 2 * kThreads] = rb_2;                                                      \
+    db[tid + 3 * kThreads] = rb_3;                                                      \
+    if (tid < kUnitsS) ((uint4*)(st).s)[tid] = rs;                                      \
+    if (tid < kUnitsD) ((uint4*)(st).d)[tid] = rd;                                      \
+    if (TYPE == QMM_Q4_K && tid < kUnitsM) ((uint4*)(st).m)[tid] = rm;                  \
+  } while (0)
 
+  v16f acc, inner;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
   const v16i zero = {};
-  for (int b = 0; b < nsb; ++b) {
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const size_t c = (size_t)b * 8 + cc;
-      v4i ahi[RB], alo[RB], bq[TB];
-      float dh[TB];
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        ahi[r] = *(const v4i*)(pa[r] + c * 2048);
-        alo[r] = *(const v4i*)(pa[r] + c * 2048 + 1024);
-      }
-#pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        bq[t] = *(const v4i*)(pb[t] + c * 1024);
-        dh[t] = f16_bits_to_float(*(const uint16_t*)(ps[t] + c * 128));
-      }
-#pragma unroll
-      for (int r = 0; r < RB; ++r)
-#pragma unroll
-        for (int t = 0; t < TB; ++t) {
-          const v16i jh = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi[r], bq[t], zero, 0, 0, 0);
-          const v16i jl = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo[r], bq[t], zero, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float f = (float)((jh[i] << 6) + jl[i]);
-            inner[r][t][i] = cc == 0 ? f * dh[t] : fmaf(f, dh[t], inner[r][t][i]);
-          }
-        }
-      if (TYPE == QMM_Q4_K && (cc & 1)) {
-        float m[RB], sv[TB];
-#pragma unroll
-        for (int r = 0; r < RB; ++r) m[r] = pm[r][(c - 1) * 32];
-#pragma unroll
-        for (int t = 0; t < TB; ++t) sv[t] = f16_bits_to_float(*(const uint16_t*)(pss[t] + (c - 1) * 128));
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-          for (int t = 0; t < TB; ++t)
-            acc[r][t] = __builtin_amdgcn_mfma_f32_32x32x2f32(m[r], sv[t], acc[r][t], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      float d[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 d4 = *(const float4*)(pd[r] + (size_t)b * 32 + 8 * g);
-        d[4 * g] = d4.x;
-        d[4 * g + 1] = d4.y;
-        d[4 * g + 2] = d4.z;
-        d[4 * g + 3] = d4.w;
-      }
-#pragma unroll
-      for (int t = 0; t < TB; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[r][t][i] = fmaf(inner[r][t][i], d[i], acc[r][t][i]);
-    }
-  }
 
+  QMM_LOAD_STAGE(0);
+  QMM_STORE_STAGE(stage[0]);
+  __syncthreads();
+
+  for (int b = 0; b < nsb; ++b) {
+    const Stage& st = stage[b & 1];
+    if (b + 1 < nsb) QMM_LOAD_STAGE(b + 1);
 #pragma unroll
-  for (int t = 0; t < TB; ++t) {
-    const int tok = (tb0 + t) * 32 + (lane & 31);
-    if (tok >= n_tok) continue;
-    float* orow = out + (size_t)tok * od;
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
+    for (int i = 0; i < 16; ++i) inner[i] = 0.0f;
+#pragma unroll 2
+    for (int cc = 0; cc < 8; ++cc) {
+      const v4i ahi = *(const v4i*)(st.a[wr][cc][0] + lane * 16);
+      const v4i alo = *(const v4i*)(st.a[wr][cc][1] + lane * 16);
+      const v4i bq = *(const v4i*)(st.b[wt][cc] + lane * 16);
+      const float dh = f16_bits_to_float(st.s[wt][cc][lane & 31] & 0xFFFF);
+      const v16i jh = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi, bq, zero, 0, 0, 0);
+      const v16i jl = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo, bq, zero, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int j = (rb0 + r) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (j < od) orow[j] = acc[r][t][i];
+        const float f = (float)((jh[i] << 6) + jl[i]);
+        inner[i] = fmaf(f, dh, inner[i]);
       }
+      if (TYPE == QMM_Q4_K && (cc & 1)) {
+        const int ck = cc - 1 + (lane >> 5);
+        const float mv = st.m[wr][ck][lane & 31];
+        const float sv = f16_bits_to_float(st.s[wt][ck][lane & 31] >> 16);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(mv, sv, acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 d4 = *(const float4*)(&st.d[wr][8 * g + 4 * (lane >> 5)]);
+      acc[4 * g + 0] = fmaf(inner[4 * g + 0], d4.x, acc[4 * g + 0]);
+      acc[4 * g + 1] = fmaf(inner[4 * g + 1], d4.y, acc[4 * g + 1]);
+      acc[4 * g + 2] = fmaf(inner[4 * g + 2], d4.z, acc[4 * g + 2]);
+      acc[4 * g + 3] = fmaf(inner[4 * g + 3], d4.w, acc[4 * g + 3]);
+    }
+    if (b + 1 < nsb) {
+      // buffer (b+1)&1 was last read in iteration b-1, which every wave finished
+      // before the barrier that ended it
+      QMM_STORE_STAGE(stage[(b + 1) & 1]);
+      __syncthreads();
+    }
+  }
+
+  const int tok = (tb0 + wt) * 32 + (lane & 31);
+  if (tok < n_tok) {
+    float* orow = out + (size_t)tok * od;
+    const int jb = (rb0 + wr) * 32 + 4 * (lane >> 5);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int j = jb + 8 * g;
+      if (vec_store && j + 3 < od) {
+        *(float4*)(orow + j) = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (j + i < od) orow[j + i] = acc[4 * g + i];
+      }
+    }
   }
 }
 
-constexpr int kRB = 1;  // 32-row blocks per wave
-constexpr int kTB = 2;  // 32-token blocks per wave
+#undef QMM_LOAD_STAGE
+#undef QMM_STORE_STAGE
 
 hipError_t launch_mmq(const Planes& p, const uint8_t* qact, int64_t n_tok, int64_t t_pad,
                       float* out, hipStream_t s) {
-  const int row_tiles = (int)(p.od_pad / (64 * kRB));
-  const int tok_tiles = (int)((n_tok + 64 * kTB - 1) / (64 * kTB));
+  const int row_tiles = (int)(p.od_pad / kTileRows);
+  const int tok_tiles = (int)((n_tok + kTileToks - 1) / kTileToks);
   const uint8_t* qs = qact + (size_t)t_pad * (size_t)p.id;
-  dim3 grid((unsigned)(row_tiles * tok_tiles)), block(256);
+  const int vec_store = (p.od % 4 == 0) && ((uintptr_t)out % 16 == 0);
+  dim3 grid((unsigned)(row_tiles * tok_tiles)), block(kThreads);
   if (p.type == QMM_Q6_K)
-    mmq_kernel<QMM_Q6_K, kRB, kTB><<<grid, block, 0, s>>>(
-        p.wq, p.wd, p.wm, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok,
-        row_tiles, out);
+    mmq_kernel<QMM_Q6_K><<<grid, block, 0, s>>>(p.wq, p.wd, p.wm, qact, qs, (int)p.nchunk,
+                                                 (int)p.nsb, (int)p.od, (int)n_tok, tok_tiles,
+                                                 vec_store, out);
   else
-    mmq_kernel<QMM_Q4_K, kRB, kTB><<<grid, block, 0, s>>>(
-        p.wq, p.wd, p.wm, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok,
-        row_tiles, out);
+    mmq_kernel<QMM_Q4_K><<<grid, block, 0, s>>>(p.wq, p.wd, p.wm, qact, qs, (int)p.nchunk,
+                                                 (int)p.nsb, (int)p.od, (int)n_tok, tok_tiles,
+                                                 vec_store, out);
   return hipGetLastError();
 }
 
