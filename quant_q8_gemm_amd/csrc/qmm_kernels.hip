@@ -46,6 +46,14 @@ size_t wm_bytes(int type, int64_t od_pad, int64_t id) {
   return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) * 4 : 0;
 }
 
+// Empty asm that claims to modify v: the value must be produced before this
+// point and cannot be recomputed after it.  Emits no instruction; used to keep
+// software-pipeline stages where they are written.
+template <class T>
+__device__ __forceinline__ void pin(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
 __device__ __forceinline__ float f16_bits_to_float(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
@@ -330,20 +338,34 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   for (int b = 0; b < nsb; ++b) {
     const Stage& st = stage[b & 1];
     if (b + 1 < nsb) QMM_LOAD_STAGE(b + 1);
+    // Software pipeline over the 8 chunks: step cc reads the LDS operands of
+    // chunk cc+2, issues the two MFMAs of chunk cc+1, then runs the scale
+    // epilogue of chunk cc on the vector ALU while the matrix core works.  The
+    // scheduling-group barriers fix that order inside every step.
+    v4i ahi0 = *(const v4i*)(st.a[wr][0][0] + lane * 16);
+    v4i alo0 = *(const v4i*)(st.a[wr][0][1] + lane * 16);
+    v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
+    v4i ahi1 = *(const v4i*)(st.a[wr][1][0] + lane * 16);
+    v4i alo1 = *(const v4i*)(st.a[wr][1][1] + lane * 16);
+    v4i bq1 = *(const v4i*)(st.b[wt][1] + lane * 16);
+    v16i jh = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi0, bq0, zero, 0, 0, 0);
+    v16i jl = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo0, bq0, zero, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) inner[i] = 0.0f;
-#pragma unroll 2
     for (int cc = 0; cc < 8; ++cc) {
-      const v4i ahi = *(const v4i*)(st.a[wr][cc][0] + lane * 16);
-      const v4i alo = *(const v4i*)(st.a[wr][cc][1] + lane * 16);
-      const v4i bq = *(const v4i*)(st.b[wt][cc] + lane * 16);
       const float dh = f16_bits_to_float(st.s[wt][cc][lane & 31] & 0xFFFF);
-      const v16i jh = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi, bq, zero, 0, 0, 0);
-      const v16i jl = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo, bq, zero, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float f = (float)((jh[i] << 6) + jl[i]);
-        inner[i] = fmaf(f, dh, inner[i]);
+      v4i ahi2, alo2, bq2;
+      if (cc < 6) {
+        ahi2 = *(const v4i*)(st.a[wr][cc + 2][0] + lane * 16);
+        alo2 = *(const v4i*)(st.a[wr][cc + 2][1] + lane * 16);
+        bq2 = *(const v4i*)(st.b[wt][cc + 2] + lane * 16);
+      }
+      v16i jh_next, jl_next;
+      if (cc < 7) {
+        jh_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi1, bq1, zero, 0, 0, 0);
+        jl_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo1, bq1, zero, 0, 0, 0);
+        pin(jh_next);
+        pin(jl_next);
       }
       if (TYPE == QMM_Q4_K && (cc & 1)) {
         const int ck = cc - 1 + (lane >> 5);
@@ -351,6 +373,24 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         const float sv = f16_bits_to_float(st.s[wt][ck][lane & 31] >> 16);
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(mv, sv, acc, 0, 0, 0);
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float f = (float)((jh[i] << 6) + jl[i]);
+        inner[i] = cc == 0 ? f * dh : fmaf(f, dh, inner[i]);
+      }
+      pin(inner);
+      if (cc < 7) {
+        jh = jh_next;
+        jl = jl_next;
+        ahi1 = ahi2;
+        alo1 = alo2;
+        bq1 = bq2;
+      }
+      // order inside the step: LDS reads, then MFMAs, then the vector epilogue
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);  // VALU
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
