@@ -239,15 +239,13 @@ struct alignas(16) Stage {
 };
 static_assert(sizeof(Stage) % 16 == 0, "stage must be a whole number of 16-byte units");
 
-// 16-byte units of each stage section, and how many each thread copies.
-constexpr int kUnitsA = kWavesR * 8 * 2 * 1024 / 16;  // 2048
-constexpr int kUnitsB = kWavesT * 8 * 1024 / 16;      // 2048
-constexpr int kUnitsS = kWavesT * 8 * 32 * 4 / 16;    // 256
-constexpr int kUnitsD = kWavesR * 32 * 4 / 16;        // 16
-constexpr int kUnitsM = kWavesR * 8 * 32 * 4 / 16;    // 128
-static_assert(kUnitsA % kThreads == 0 && kUnitsB % kThreads == 0, "even A/B split");
-constexpr int kPerA = kUnitsA / kThreads;             // 4
-constexpr int kPerB = kUnitsB / kThreads;             // 4
+// The staging code assigns whole 1 KiB fragments to waves; it is written for
+// this geometry.
+static_assert(kWavesR == 2 && kWavesT == 4, "staging assumes 2 row blocks x 4 token blocks");
+static_assert(sizeof(((Stage*)0)->a) == 32 * 1024 && sizeof(((Stage*)0)->b) == 32 * 1024,
+              "8 waves x 4 fragments of 1 KiB each for weights and codes");
+static_assert(sizeof(((Stage*)0)->s) == 4 * 1024 && sizeof(((Stage*)0)->m) == 2 * 1024 &&
+              sizeof(((Stage*)0)->d) == 256, "scale pairs, mins and d sizes");
 
 // Work-group index -> (row tile, token tile).  Work-groups are dispatched
 // round-robin over the 8 XCDs (each with its own L2); this map gives every XCD
@@ -273,57 +271,38 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   const int rt = tile / tok_tiles, tt = tile % tok_tiles;
   const int rb0 = rt * kWavesR, tb0 = tt * kWavesT;
 
-  // Global sources of one stage (super-block b adds b times the per-super-block
-  // stride).  Copy unit u of the weight section lies in row block u / 1024 (16 KB
-  // contiguous per row block); unit u of the code section in token block u / 512.
-  static_assert(kPerA == 4 && kPerB == 4, "the copy code below moves 4 + 4 units per thread");
-  const int8_t* ga0 = wq + ((size_t)(rb0 + (tid + 0 * kThreads) / 1024) * nchunk) * 2048 + (size_t)((tid + 0 * kThreads) % 1024) * 16;
-  const int8_t* ga1 = wq + ((size_t)(rb0 + (tid + 1 * kThreads) / 1024) * nchunk) * 2048 + (size_t)((tid + 1 * kThreads) % 1024) * 16;
-  const int8_t* ga2 = wq + ((size_t)(rb0 + (tid + 2 * kThreads) / 1024) * nchunk) * 2048 + (size_t)((tid + 2 * kThreads) % 1024) * 16;
-  const int8_t* ga3 = wq + ((size_t)(rb0 + (tid + 3 * kThreads) / 1024) * nchunk) * 2048 + (size_t)((tid + 3 * kThreads) % 1024) * 16;
-  const uint8_t* gb0 = qq + ((size_t)(tb0 + (tid + 0 * kThreads) / 512) * nchunk) * 1024 + (size_t)((tid + 0 * kThreads) % 512) * 16;
-  const uint8_t* gb1 = qq + ((size_t)(tb0 + (tid + 1 * kThreads) / 512) * nchunk) * 1024 + (size_t)((tid + 1 * kThreads) % 512) * 16;
-  const uint8_t* gb2 = qq + ((size_t)(tb0 + (tid + 2 * kThreads) / 512) * nchunk) * 1024 + (size_t)((tid + 2 * kThreads) % 512) * 16;
-  const uint8_t* gb3 = qq + ((size_t)(tb0 + (tid + 3 * kThreads) / 512) * nchunk) * 1024 + (size_t)((tid + 3 * kThreads) % 512) * 16;
-  const uint8_t* gs = qs + ((size_t)(tb0 + tid / 64) * nchunk) * 128 + (size_t)(tid % 64) * 16;
-  const float* gd = wd + ((size_t)(rb0 + tid / 8) * nsb) * 32 + (tid % 8) * 4;
-  const float* gm = TYPE == QMM_Q4_K
-      ? wm + ((size_t)(rb0 + (tid & 127) / 64) * nchunk) * 32 + ((tid & 127) % 64) * 4
-      : nullptr;
+  // Staging of super-block b into an LDS stage with direct global->LDS loads
+  // (global_load_lds_dwordx4: lane l's 16 bytes land at the LDS base + 16*l, so
+  // one wave instruction moves one 1 KiB fragment).  Per stage: 32 weight
+  // fragments (2 row blocks x 8 chunks x hi/lo, 16 KiB contiguous per row block
+  // in global memory), 32 code fragments (4 token blocks x 8 chunks, 8 KiB
+  // contiguous per token block), 4 KiB of scale pairs, 1 KiB of -dmin*min per
+  // row block (q4_K) and 128 bytes of d per row block.  Wave w moves weight
+  // fragments 4w..4w+3 and code fragments 4w..4w+3; waves 0-3 the scale pairs
+  // of token block w; waves 4-5 the -dmin*min of row block w-4; wave 6 the d.
+  const size_t a_row = (size_t)nchunk * 2048, b_tok = (size_t)nchunk * 1024;
+  const int8_t* ga = wq + (size_t)(rb0 + (4 * wave) / 16) * a_row + (size_t)((4 * wave) % 16) * 1024 + lane * 16;
+  const uint8_t* gb = qq + (size_t)(tb0 + (4 * wave) / 8) * b_tok + (size_t)((4 * wave) % 8) * 1024 + lane * 16;
+  const uint8_t* gs = qs + ((size_t)(tb0 + (wave & 3)) * nchunk) * 128 + lane * 16;
+  const float* gm = TYPE == QMM_Q4_K ? wm + ((size_t)(rb0 + (wave & 1)) * nchunk) * 32 + lane * 4 : nullptr;
+  const float* gd = wd + ((size_t)(rb0 + ((lane & 15) >> 3)) * nsb) * 32 + (lane & 7) * 4;
 
-  uint4 ra0, ra1, ra2, ra3, rb_0, rb_1, rb_2, rb_3, rs, rd, rm;
-  // Global -> registers for super-block b (issued early, consumed after compute).
-#define QMM_LOAD_STAGE(b)                                                               \
-  do {                                                                                  \
-    const size_t oa = (size_t)(b) * 16384, ob = (size_t)(b) * 8192;                     \
-    ra0 = *(const uint4*)(ga0 + oa);                                                    \
-    ra1 = *(const uint4*)(ga1 + oa);                                                    \
-    ra2 = *(const uint4*)(ga2 + oa);                                                    \
-    ra3 = *(const uint4*)(ga3 + oa);                                                    \
-    rb_0 = *(const uint4*)(gb0 + ob);                                                   \
-    rb_1 = *(const uint4*)(gb1 + ob);                                                   \
-    rb_2 = *(const uint4*)(gb2 + ob);                                                   \
-    rb_3 = *(const uint4*)(gb3 + ob);                                                   \
-    if (tid < kUnitsS) rs = *(const uint4*)(gs + (size_t)(b) * 1024);                   \
-    if (tid < kUnitsD) rd = *(const uint4*)(gd + (size_t)(b) * 32);                     \
-    if (TYPE == QMM_Q4_K && tid < kUnitsM) rm = *(const uint4*)(gm + (size_t)(b) * 256); \
-  } while (0)
-  // Registers -> LDS stage st.
-#define QMM_STORE_STAGE(st)                                                             \
-  do {                                                                                  \
-    uint4* da = (uint4*)(st).a;                                                         \
-    uint4* db = (uint4*)(st).b;                                                         \
-    da[tid + 0 * kThreads] = ra0;                                                       \
-    da[tid + 1 * kThreads] = ra1;                                                       \
-    da[tid + 2 * kThreads] = ra2;                                                       \
-    da[tid + 3 * kThreads] = ra3;                                                       \
-    db[tid + 0 * kThreads] = rb_0;                                                      \
-    db[tid + 1 * kThreads] = rb_1;                                                      \
-    db[tid + 2 * kThreads] = rb_2;                                                      \
-    db[tid + 3 * kThreads] = rb_3;                                                      \
-    if (tid < kUnitsS) ((uint4*)(st).s)[tid] = rs;                                      \
-    if (tid < kUnitsD) ((uint4*)(st).d)[tid] = rd;                                      \
-    if (TYPE == QMM_Q4_K && tid < kUnitsM) ((uint4*)(st).m)[tid] = rm;                  \
+#define QMM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define QMM_STAGE_LOADS(SB, ST)                                                                 \
+  do {                                                                                         \
+    const size_t sb = (size_t)(SB);                                                             \
+    int8_t* la = &(ST).a[(4 * wave) / 16][0][0][0] + ((4 * wave) % 16) * 1024;                 \
+    int8_t* lb = &(ST).b[(4 * wave) / 8][0][0] + ((4 * wave) % 8) * 1024;                      \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                            \
+      __builtin_amdgcn_global_load_lds(ga + sb * 16384 + u * 1024, QMM_LDS(la + u * 1024), 16, 0, 0); \
+      __builtin_amdgcn_global_load_lds(gb + sb * 8192 + u * 1024, QMM_LDS(lb + u * 1024), 16, 0, 0);  \
+    }                                                                                          \
+    if (wave < 4)                                                                              \
+      __builtin_amdgcn_global_load_lds(gs + sb * 1024, QMM_LDS(&(ST).s[wave][0][0]), 16, 0, 0); \
+    else if (TYPE == QMM_Q4_K && wave < 6)                                                     \
+      __builtin_amdgcn_global_load_lds(gm + sb * 256, QMM_LDS(&(ST).m[wave - 4][0][0]), 16, 0, 0); \
+    else if (wave == 6 && lane < 16)                                                           \
+      __builtin_amdgcn_global_load_lds(gd + sb * 32, QMM_LDS(&(ST).d[0][0]), 16, 0, 0);        \
   } while (0)
 
   v16f acc, inner;
@@ -331,13 +310,15 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
   const v16i zero = {};
 
-  QMM_LOAD_STAGE(0);
-  QMM_STORE_STAGE(stage[0]);
+  QMM_STAGE_LOADS(0, stage[0]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int b = 0; b < nsb; ++b) {
     const Stage& st = stage[b & 1];
-    if (b + 1 < nsb) QMM_LOAD_STAGE(b + 1);
+    // stage (b+1)&1 was last read in iteration b-1, which every wave finished
+    // before the barrier that ended it
+    if (b + 1 < nsb) QMM_STAGE_LOADS(b + 1, stage[(b + 1) & 1]);
     // Software pipeline over the 8 chunks: step cc reads the LDS operands of
     // chunk cc+2, issues the two MFMAs of chunk cc+1, then runs the scale
     // epilogue of chunk cc on the vector ALU while the matrix core works.  The
@@ -401,10 +382,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
       acc[4 * g + 3] = fmaf(inner[4 * g + 3], d4.w, acc[4 * g + 3]);
     }
     if (b + 1 < nsb) {
-      // buffer (b+1)&1 was last read in iteration b-1, which every wave finished
-      // before the barrier that ended it
-      QMM_STORE_STAGE(stage[(b + 1) & 1]);
-      __syncthreads();
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads for b+1 landed
+      __syncthreads();                                   // everyone's landed; stage b is free
     }
   }
 
@@ -426,8 +405,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   }
 }
 
-#undef QMM_LOAD_STAGE
-#undef QMM_STORE_STAGE
+#undef QMM_STAGE_LOADS
+#undef QMM_LDS
 
 hipError_t launch_mmq(const Planes& p, const uint8_t* qact, int64_t n_tok, int64_t t_pad,
                       float* out, hipStream_t s) {
