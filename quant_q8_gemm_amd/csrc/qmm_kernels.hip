@@ -211,118 +211,145 @@ hipError_t launch_quantize(const float* x, int64_t n_tok, int64_t t_pad, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// MMQ.  Work-group = 8 waves (two per SIMD) on a 64-row x 128-token output tile:
-// a 2 x 4 grid of 32 x 32 blocks, one block per wave.  The inner dimension is
-// walked one 256-wide super-block at a time; each super-block's operands (both
-// weight planes for the 2 row blocks, the q8 codes and scale pairs for the 4
-// token blocks, d, and for q4_K the -dmin*min plane) are copied once per
-// work-group into LDS and read from there by the waves that share them.  The
-// LDS is double-buffered: the global loads for super-block b+1 are issued
-// before super-block b is computed and written to the other buffer after it,
-// so there is one barrier per super-block.
+// MMQ.  A work-group of WR x WT waves owns a (32*WR rows) x (32*WT tokens)
+// output tile, one 32 x 32 block per wave.  The inner dimension is walked in
+// stages of KC chunks of 32 (KC = 4: half a 256-wide super-block, KC = 8: a
+// whole one).  Each stage's operands -- both weight planes of the WR row blocks,
+// the q8 codes and scale pairs of the WT token blocks, and d (and for q4_K the
+// -dmin*min plane) -- are copied once per work-group into LDS with direct
+// global->LDS loads (global_load_lds_dwordx4 puts lane l's 16 bytes at the LDS
+// base + 16*l, so one wave instruction moves one 1 KiB fragment), and read from
+// there by every wave that shares them.  Two LDS stages alternate: the loads of
+// stage g+1 are issued before stage g is computed; one barrier per stage.
+// A small tile and a small LDS footprint let several work-groups share a CU, so
+// one group's barrier wait is covered by the others' work.
 // MFMA orientation: A = weights (rows j), B = activations (columns t), so each
 // lane's 16 outputs share one token: the activation scale dh is one register
 // per chunk, and the super-block d is applied once per 8 chunks.
 // ---------------------------------------------------------------------------
-constexpr int kWavesR = 2;                 // row blocks per work-group
-constexpr int kWavesT = 4;                 // token blocks per work-group
-constexpr int kTileRows = 32 * kWavesR;    // 64
-constexpr int kTileToks = 32 * kWavesT;    // 128
-constexpr int kThreads = 64 * kWavesR * kWavesT;
-
+template <int WR, int WT, int KC>
 struct alignas(16) Stage {
-  int8_t a[kWavesR][8][2][1024];   // weight planes: [row block][chunk][hi, lo][fragment]
-  int8_t b[kWavesT][8][1024];      // q8 codes: [token block][chunk][fragment]
-  uint32_t s[kWavesT][8][32];      // (dh, s) pairs: [token block][chunk][token]
-  float d[kWavesR][32];            // super-block d per row
-  float m[kWavesR][8][32];         // -dmin*min per (chunk, row); q4_K only
+  int8_t a[WR][KC][2][1024];  // weight planes: [row block][chunk][hi, lo][fragment]
+  int8_t b[WT][KC][1024];     // q8 codes: [token block][chunk][fragment]
+  uint32_t s[WT][KC][32];     // (dh, s) pairs: [token block][chunk][token]
+  float m[WR][KC][32];        // -dmin*min: [row block][chunk][row]; q4_K only
+  float d[WR][32];            // super-block d: [row block][row]
+  // s, m and d are contiguous: the "small" region, copied in 16-byte units.
+  static constexpr int kUnitsS = WT * KC * 8, kUnitsM = WR * KC * 8, kUnitsD = WR * 8;
+  static constexpr int kSmallJobs = (kUnitsS + kUnitsM + kUnitsD + 63) / 64;
+  static constexpr int kJobs = WR * KC * 2 + WT * KC + kSmallJobs;  // wave instructions
 };
-static_assert(sizeof(Stage) % 16 == 0, "stage must be a whole number of 16-byte units");
 
-// The staging code assigns whole 1 KiB fragments to waves; it is written for
-// this geometry.
-static_assert(kWavesR == 2 && kWavesT == 4, "staging assumes 2 row blocks x 4 token blocks");
-static_assert(sizeof(((Stage*)0)->a) == 32 * 1024 && sizeof(((Stage*)0)->b) == 32 * 1024,
-              "8 waves x 4 fragments of 1 KiB each for weights and codes");
-static_assert(sizeof(((Stage*)0)->s) == 4 * 1024 && sizeof(((Stage*)0)->m) == 2 * 1024 &&
-              sizeof(((Stage*)0)->d) == 256, "scale pairs, mins and d sizes");
-
-// Work-group index -> (row tile, token tile).  Work-groups are dispatched
-// round-robin over the 8 XCDs (each with its own L2); this map gives every XCD
-// a contiguous run of tiles in row-major (row tile, token tile) order, so the
-// work-groups that stream the same weight rows share one L2.
+// Work-group index -> tile index.  Work-groups are dispatched round-robin over
+// the 8 XCDs (each with its own L2); this map gives every XCD a contiguous run
+// of tiles in row-major (row tile, token tile) order, so the work-groups that
+// stream the same weight rows share one L2.
 __device__ __forceinline__ int xcd_swizzle(int i, int n) {
   const int q = n / 8, r = n % 8;
   const int x = i % 8, slot = i / 8;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + slot;
 }
 
-template <int TYPE>
-__global__ void __launch_bounds__(kThreads)
+template <int TYPE, int WR, int WT, int KC>
+__global__ void __launch_bounds__(64 * WR * WT, (WR * WT == 4) ? 3 : 1)
 mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
            const float* __restrict__ wm, const uint8_t* __restrict__ qq,
            const uint8_t* __restrict__ qs, int nchunk, int nsb, int od, int n_tok,
            int tok_tiles, int vec_store, float* __restrict__ out) {
-  __shared__ Stage stage[2];
+  using St = Stage<WR, WT, KC>;
+  constexpr int kWaves = WR * WT;
+  constexpr int kRounds = (St::kJobs + kWaves - 1) / kWaves;
+  constexpr int kJobsA = WR * KC * 2, kJobsB = WT * KC;
+  static_assert(KC == 4 || KC == 8, "a stage is half or a whole super-block");
+  __shared__ St stage[2];
+
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wr = wave / kWavesT, wt = wave % kWavesT;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int wr = wave / WT, wt = wave % WT;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int rt = tile / tok_tiles, tt = tile % tok_tiles;
-  const int rb0 = rt * kWavesR, tb0 = tt * kWavesT;
+  const int rb0 = rt * WR, tb0 = tt * WT;
+  const int nstages = nchunk / KC;
 
-  // Staging of super-block b into an LDS stage with direct global->LDS loads
-  // (global_load_lds_dwordx4: lane l's 16 bytes land at the LDS base + 16*l, so
-  // one wave instruction moves one 1 KiB fragment).  Per stage: 32 weight
-  // fragments (2 row blocks x 8 chunks x hi/lo, 16 KiB contiguous per row block
-  // in global memory), 32 code fragments (4 token blocks x 8 chunks, 8 KiB
-  // contiguous per token block), 4 KiB of scale pairs, 1 KiB of -dmin*min per
-  // row block (q4_K) and 128 bytes of d per row block.  Wave w moves weight
-  // fragments 4w..4w+3 and code fragments 4w..4w+3; waves 0-3 the scale pairs
-  // of token block w; waves 4-5 the -dmin*min of row block w-4; wave 6 the d.
-  const size_t a_row = (size_t)nchunk * 2048, b_tok = (size_t)nchunk * 1024;
-  const int8_t* ga = wq + (size_t)(rb0 + (4 * wave) / 16) * a_row + (size_t)((4 * wave) % 16) * 1024 + lane * 16;
-  const uint8_t* gb = qq + (size_t)(tb0 + (4 * wave) / 8) * b_tok + (size_t)((4 * wave) % 8) * 1024 + lane * 16;
-  const uint8_t* gs = qs + ((size_t)(tb0 + (wave & 3)) * nchunk) * 128 + lane * 16;
-  const float* gm = TYPE == QMM_Q4_K ? wm + ((size_t)(rb0 + (wave & 1)) * nchunk) * 32 + lane * 4 : nullptr;
-  const float* gd = wd + ((size_t)(rb0 + ((lane & 15) >> 3)) * nsb) * 32 + (lane & 7) * 4;
+  // Copy jobs of one stage: job k (one wave instruction, 1 KiB) goes to wave
+  // k % kWaves.  Jobs [0, kJobsA) are weight fragments, then code fragments,
+  // then the small region (scale pairs, mins, d) in 16-byte units per lane.
+  const int8_t* srcA = wq + (size_t)rb0 * nchunk * 2048;  // + stage * KC * 2048
+  const uint8_t* srcB = qq + (size_t)tb0 * nchunk * 1024;  // + stage * KC * 1024
+  const int small_k0 = kJobsA + kJobsB;
+  // The small job this wave owns, if any (at most one: asserted below).
+  static_assert(St::kSmallJobs <= kWaves, "one small-region job per wave at most");
+  const int small_r = (small_k0 - wave + kWaves - 1) / kWaves;  // round of this wave's first job >= small_k0
+  const int small_k = wave + small_r * kWaves;
+  const uint8_t* small_src = nullptr;
+  int small_kind = 0;  // 0 none, 1 pairs/mins (advance per stage), 2 d (advance per super-block)
+  if (small_k < St::kJobs) {
+    const int u = (small_k - small_k0) * 64 + lane;
+    if (u < St::kUnitsS) {
+      small_src = qs + ((size_t)(tb0 + u / (KC * 8)) * nchunk) * 128 + (u % (KC * 8)) * 16;
+      small_kind = 1;
+    } else if (u < St::kUnitsS + St::kUnitsM) {
+      if (TYPE == QMM_Q4_K) {
+        const int v = u - St::kUnitsS;
+        small_src = (const uint8_t*)wm + ((size_t)(rb0 + v / (KC * 8)) * nchunk) * 128 + (v % (KC * 8)) * 16;
+        small_kind = 1;
+      }
+    } else if (u < St::kUnitsS + St::kUnitsM + St::kUnitsD) {
+      const int v = u - St::kUnitsS - St::kUnitsM;
+      small_src = (const uint8_t*)wd + ((size_t)(rb0 + v / 8) * nsb) * 128 + (v % 8) * 16;
+      small_kind = 2;
+    }
+  }
 
 #define QMM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-#define QMM_STAGE_LOADS(SB, ST)                                                                 \
-  do {                                                                                         \
-    const size_t sb = (size_t)(SB);                                                             \
-    int8_t* la = &(ST).a[(4 * wave) / 16][0][0][0] + ((4 * wave) % 16) * 1024;                 \
-    int8_t* lb = &(ST).b[(4 * wave) / 8][0][0] + ((4 * wave) % 8) * 1024;                      \
-    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                            \
-      __builtin_amdgcn_global_load_lds(ga + sb * 16384 + u * 1024, QMM_LDS(la + u * 1024), 16, 0, 0); \
-      __builtin_amdgcn_global_load_lds(gb + sb * 8192 + u * 1024, QMM_LDS(lb + u * 1024), 16, 0, 0);  \
-    }                                                                                          \
-    if (wave < 4)                                                                              \
-      __builtin_amdgcn_global_load_lds(gs + sb * 1024, QMM_LDS(&(ST).s[wave][0][0]), 16, 0, 0); \
-    else if (TYPE == QMM_Q4_K && wave < 6)                                                     \
-      __builtin_amdgcn_global_load_lds(gm + sb * 256, QMM_LDS(&(ST).m[wave - 4][0][0]), 16, 0, 0); \
-    else if (wave == 6 && lane < 16)                                                           \
-      __builtin_amdgcn_global_load_lds(gd + sb * 32, QMM_LDS(&(ST).d[0][0]), 16, 0, 0);        \
-  } while (0)
+  auto issue_stage = [&](int g, St& st) __attribute__((always_inline)) {
+    const int8_t* sa = srcA + (size_t)g * KC * 2048;
+    const uint8_t* sbp = srcB + (size_t)g * KC * 1024;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int k = wave + r * kWaves;  // uniform
+      if (k < kJobsA) {
+        const int blk = k / (KC * 2), sub = k % (KC * 2);
+        __builtin_amdgcn_global_load_lds(sa + (size_t)blk * nchunk * 2048 + sub * 1024 + lane * 16,
+                                         QMM_LDS(&st.a[0][0][0][0] + k * 1024), 16, 0, 0);
+      } else if (k < kJobsA + kJobsB) {
+        const int kb = k - kJobsA;
+        const int blk = kb / KC, sub = kb % KC;
+        __builtin_amdgcn_global_load_lds(sbp + (size_t)blk * nchunk * 1024 + sub * 1024 + lane * 16,
+                                         QMM_LDS(&st.b[0][0][0] + kb * 1024), 16, 0, 0);
+      }
+    }
+    if (small_k < St::kJobs) {
+      uint8_t* ls = (uint8_t*)&st.s[0][0][0] + (small_k - small_k0) * 1024;
+      // pairs/mins advance by KC chunks per stage; d by one super-block per 8
+      // chunks, loaded into the stage that ends the super-block
+      const bool ends_sb = ((g + 1) * KC) % 8 == 0;
+      if (small_kind == 1)
+        __builtin_amdgcn_global_load_lds(small_src + (size_t)g * KC * 128, QMM_LDS(ls), 16, 0, 0);
+      else if (small_kind == 2 && ends_sb)
+        __builtin_amdgcn_global_load_lds(small_src + (size_t)((g * KC) / 8) * 128, QMM_LDS(ls), 16, 0, 0);
+    }
+  };
 
   v16f acc, inner;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
   const v16i zero = {};
 
-  QMM_STAGE_LOADS(0, stage[0]);
+  issue_stage(0, stage[0]);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int b = 0; b < nsb; ++b) {
-    const Stage& st = stage[b & 1];
-    // stage (b+1)&1 was last read in iteration b-1, which every wave finished
+  for (int g = 0; g < nstages; ++g) {
+    St& st = stage[g & 1];
+    // stage (g+1)&1 was last read in iteration g-1, which every wave finished
     // before the barrier that ended it
-    if (b + 1 < nsb) QMM_STAGE_LOADS(b + 1, stage[(b + 1) & 1]);
-    // Software pipeline over the 8 chunks: step cc reads the LDS operands of
+    if (g + 1 < nstages) issue_stage(g + 1, stage[(g + 1) & 1]);
+    const bool starts_sb = (g * KC) % 8 == 0;
+    // Software pipeline over the KC chunks: step cc reads the LDS operands of
     // chunk cc+2, issues the two MFMAs of chunk cc+1, then runs the scale
-    // epilogue of chunk cc on the vector ALU while the matrix core works.  The
-    // scheduling-group barriers fix that order inside every step.
+    // epilogue of chunk cc on the vector ALU while the matrix core works.
     v4i ahi0 = *(const v4i*)(st.a[wr][0][0] + lane * 16);
     v4i alo0 = *(const v4i*)(st.a[wr][0][1] + lane * 16);
     v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
@@ -333,16 +360,16 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
     v16i jl = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo0, bq0, zero, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
+    for (int cc = 0; cc < KC; ++cc) {
       const float dh = f16_bits_to_float(st.s[wt][cc][lane & 31] & 0xFFFF);
       v4i ahi2, alo2, bq2;
-      if (cc < 6) {
+      if (cc + 2 < KC) {
         ahi2 = *(const v4i*)(st.a[wr][cc + 2][0] + lane * 16);
         alo2 = *(const v4i*)(st.a[wr][cc + 2][1] + lane * 16);
         bq2 = *(const v4i*)(st.b[wt][cc + 2] + lane * 16);
       }
       v16i jh_next, jl_next;
-      if (cc < 7) {
+      if (cc + 1 < KC) {
         jh_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi1, bq1, zero, 0, 0, 0);
         jl_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo1, bq1, zero, 0, 0, 0);
         pin(jh_next);
@@ -354,13 +381,15 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         const float sv = f16_bits_to_float(st.s[wt][ck][lane & 31] >> 16);
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(mv, sv, acc, 0, 0, 0);
       }
+      if (cc == 0 && starts_sb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float f = (float)((jh[i] << 6) + jl[i]);
-        inner[i] = cc == 0 ? f * dh : fmaf(f, dh, inner[i]);
+        for (int i = 0; i < 16; ++i) inner[i] = (float)((jh[i] << 6) + jl[i]) * dh;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)((jh[i] << 6) + jl[i]), dh, inner[i]);
       }
       pin(inner);
-      if (cc < 7) {
+      if (cc + 1 < KC) {
         jh = jh_next;
         jl = jl_next;
         ahi1 = ahi2;
@@ -373,57 +402,75 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
       __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);  // VALU
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (((g + 1) * KC) % 8 == 0) {  // end of a super-block: apply its d
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 d4 = *(const float4*)(&st.d[wr][8 * g + 4 * (lane >> 5)]);
-      acc[4 * g + 0] = fmaf(inner[4 * g + 0], d4.x, acc[4 * g + 0]);
-      acc[4 * g + 1] = fmaf(inner[4 * g + 1], d4.y, acc[4 * g + 1]);
-      acc[4 * g + 2] = fmaf(inner[4 * g + 2], d4.z, acc[4 * g + 2]);
-      acc[4 * g + 3] = fmaf(inner[4 * g + 3], d4.w, acc[4 * g + 3]);
+      for (int q = 0; q < 4; ++q) {
+        const float4 d4 = *(const float4*)(&st.d[wr][8 * q + 4 * (lane >> 5)]);
+        acc[4 * q + 0] = fmaf(inner[4 * q + 0], d4.x, acc[4 * q + 0]);
+        acc[4 * q + 1] = fmaf(inner[4 * q + 1], d4.y, acc[4 * q + 1]);
+        acc[4 * q + 2] = fmaf(inner[4 * q + 2], d4.z, acc[4 * q + 2]);
+        acc[4 * q + 3] = fmaf(inner[4 * q + 3], d4.w, acc[4 * q + 3]);
+      }
     }
-    if (b + 1 < nsb) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads for b+1 landed
-      __syncthreads();                                   // everyone's landed; stage b is free
+    if (g + 1 < nstages) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads for g+1 landed
+      __syncthreads();                                   // everyone's landed; stage g is free
     }
   }
+#undef QMM_LDS
 
   const int tok = (tb0 + wt) * 32 + (lane & 31);
   if (tok < n_tok) {
     float* orow = out + (size_t)tok * od;
     const int jb = (rb0 + wr) * 32 + 4 * (lane >> 5);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int j = jb + 8 * g;
+    for (int q = 0; q < 4; ++q) {
+      const int j = jb + 8 * q;
       if (vec_store && j + 3 < od) {
-        *(float4*)(orow + j) = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        *(float4*)(orow + j) = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (j + i < od) orow[j + i] = acc[4 * g + i];
+          if (j + i < od) orow[j + i] = acc[4 * q + i];
       }
     }
   }
 }
 
-#undef QMM_STAGE_LOADS
-#undef QMM_LDS
-
-hipError_t launch_mmq(const Planes& p, const uint8_t* qact, int64_t n_tok, int64_t t_pad,
-                      float* out, hipStream_t s) {
-  const int row_tiles = (int)(p.od_pad / kTileRows);
-  const int tok_tiles = (int)((n_tok + kTileToks - 1) / kTileToks);
+template <int TYPE, int WR, int WT, int KC>
+static hipError_t launch_tiled(const Planes& p, const uint8_t* qact, int64_t n_tok, int64_t t_pad,
+                               float* out, hipStream_t s) {
+  static_assert(kRowPad % (32 * WR) == 0 && kTokenPad % (32 * WT) == 0,
+                "tiles must divide the row and token padding");
+  const int row_tiles = (int)(p.od_pad / (32 * WR));
+  const int tok_tiles = (int)((n_tok + 32 * WT - 1) / (32 * WT));
   const uint8_t* qs = qact + (size_t)t_pad * (size_t)p.id;
   const int vec_store = (p.od % 4 == 0) && ((uintptr_t)out % 16 == 0);
-  dim3 grid((unsigned)(row_tiles * tok_tiles)), block(kThreads);
-  if (p.type == QMM_Q6_K)
-    mmq_kernel<QMM_Q6_K><<<grid, block, 0, s>>>(p.wq, p.wd, p.wm, qact, qs, (int)p.nchunk,
-                                                 (int)p.nsb, (int)p.od, (int)n_tok, tok_tiles,
-                                                 vec_store, out);
-  else
-    mmq_kernel<QMM_Q4_K><<<grid, block, 0, s>>>(p.wq, p.wd, p.wm, qact, qs, (int)p.nchunk,
-                                                 (int)p.nsb, (int)p.od, (int)n_tok, tok_tiles,
-                                                 vec_store, out);
+  mmq_kernel<TYPE, WR, WT, KC><<<dim3((unsigned)(row_tiles * tok_tiles)), dim3(64 * WR * WT), 0, s>>>(
+      p.wq, p.wd, p.wm, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, tok_tiles,
+      vec_store, out);
   return hipGetLastError();
+}
+
+// Tile geometry per launch.  Two shapes of the same kernel:
+//  * 2 x 4 waves (64 rows x 128 tokens), a whole super-block per stage: one
+//    work-group of 8 waves per CU (about 140 KiB of LDS), one barrier per 8
+//    chunks; best when there are too few tiles to fill the CUs several times
+//    (e.g. 512 tokens x 4096 rows = 256 work-groups);
+//  * 2 x 2 waves (64 x 64), half a super-block per stage: about 52 KiB of LDS,
+//    three work-groups per CU, so one group's barrier wait is covered by the
+//    others; best when there are many tiles.
+// The switch point (about four 64 x 64 tiles per CU) was chosen by timing
+// both on the 512-token shapes and the 2048-token output head.
+hipError_t launch_mmq(const Planes& p, const uint8_t* qact, int64_t n_tok, int64_t t_pad,
+                      float* out, hipStream_t s) {
+  const int64_t small_tiles = (p.od_pad / 64) * ((n_tok + 63) / 64);
+  const bool many = small_tiles >= 4 * 256;
+  if (p.type == QMM_Q6_K)
+    return many ? launch_tiled<QMM_Q6_K, 2, 2, 4>(p, qact, n_tok, t_pad, out, s)
+                : launch_tiled<QMM_Q6_K, 2, 4, 8>(p, qact, n_tok, t_pad, out, s);
+  return many ? launch_tiled<QMM_Q4_K, 2, 2, 4>(p, qact, n_tok, t_pad, out, s)
+              : launch_tiled<QMM_Q4_K, 2, 4, 8>(p, qact, n_tok, t_pad, out, s);
 }
 
 }  // namespace qmm

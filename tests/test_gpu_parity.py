@@ -229,7 +229,10 @@ SMALL = [("C1 q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          ("q6_K 129x1280 T=200", synth.Q6_K, 129, 1280, 200, True),
          ("q4_K 1x256 T=1", synth.Q4_K, 1, 256, 1, False),
          ("q6_K 33x2304 T=130", synth.Q6_K, 33, 2304, 130, False),
-         ("q4_K 520x1536 T=257", synth.Q4_K, 520, 1536, 257, False)]
+         ("q4_K 520x1536 T=257", synth.Q4_K, 520, 1536, 257, False),
+         # enough 64 x 64 tiles (>= 1024) to select the many-tile geometry
+         ("q6_K 1000x512 T=4100", synth.Q6_K, 1000, 512, 4100, True),
+         ("q4_K 1030x256 T=4000", synth.Q4_K, 1030, 256, 4000, False)]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
