@@ -3,18 +3,21 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
 A step is one pass of the hot path over one batch of synthetic activations that
-are already resident in HBM: the q8 quantize prepass followed by the MMQ.  The
-weight registration (the once-per-weight repack into planes) happens before the
-timed region, as a deployment does it once at model load.
+are already resident in HBM: the q8 quantize prepass of every distinct input,
+then every MMQ of the workload.  Weight registration (the once-per-weight repack
+into planes) happens before the timed region, as a deployment does it at model
+load; its device memory is reported.
 
-Prints one JSON line: effective int8 TOPS of the whole step (2*T*od*id per step
-time), the roofline of the dominant kernel (the MMQ) measured with HIP events on
-the stream it runs on, and the CPU oracle timed on the host as a reference.
+Prints one JSON line: effective int8 TOPS of the whole step (2*T*od*id summed
+over the GEMMs, per step time), the roofline of the dominant kernel (the MMQ)
+from HIP events on the stream it runs on, and the CPU oracle timed on the host
+as a reference.
 """
 from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import hashlib
 import json
 import os
 import sys
@@ -27,17 +30,41 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 
-WORKLOADS = {
-    "ffn_down": synth.C2,       # q6_K 4096 x 11008, 512 tokens
-    "ffn_down_odd": synth.C2_ODD,
-    "attn": synth.C3_QKVO,
-    "ffn_gate_up": synth.C3_GU,
-    "head": synth.C4,
-    "c1": synth.C1,
-}
-
 MFMA_INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
 HBM_PEAK_GBS = 8000.0
+
+# workload name -> (description, tokens, inputs {name: id}, gemms [(name, type, od, id, input)],
+#                   outliers)
+def _single(cfg, inp="x"):
+    name, type_, od, id_, T, outl = cfg
+    return (name, T, {inp: id_}, [(name, type_, od, id_, inp)], outl)
+
+
+WORKLOADS = {
+    "ffn_down": _single(synth.C2),            # q6_K 4096 x 11008, 512 tokens
+    "ffn_down_odd": _single(synth.C2_ODD),
+    "attn": _single(synth.C3_QKVO),
+    "ffn_gate_up": _single(synth.C3_GU),
+    "head": _single(synth.C4),
+    "c1": _single(synth.C1),
+    "layer": ("LLaMA-7B q4_K_M-style layer, 3314 tokens (q,k,o,gate,up q4_K; v,down q6_K)",
+              synth.C5_TOKENS,
+              {"attn_in": 4096, "attn_out": 4096, "ffn_in": 4096, "ffn_mid": 11008},
+              [("attn_q", synth.Q4_K, 4096, 4096, "attn_in"),
+               ("attn_k", synth.Q4_K, 4096, 4096, "attn_in"),
+               ("attn_v", synth.Q6_K, 4096, 4096, "attn_in"),
+               ("attn_output", synth.Q4_K, 4096, 4096, "attn_out"),
+               ("ffn_gate", synth.Q4_K, 11008, 4096, "ffn_in"),
+               ("ffn_up", synth.Q4_K, 11008, 4096, "ffn_in"),
+               ("ffn_down", synth.Q6_K, 4096, 11008, "ffn_mid")],
+              False),
+}
+
+# Counter summaries committed under profiles/ (HBM bytes per MMQ launch from
+# rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a plain copy's reading); valid
+# only while the kernel source is the one they were taken with.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmq_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "quant_q8_gemm_amd", "csrc", "qmm_kernels.hip")
 
 
 def _parse():
@@ -48,37 +75,61 @@ def _parse():
     ap.add_argument("--workload", default="ffn_down", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--cpu-macs", type=float, default=2.4e10,
+                    help="multiply-accumulates of the oracle sample (about 20 s of CPU work)")
     return ap.parse_args()
 
 
-def algorithmic_bytes(type_, od, id_, T, w):
-    """Compulsory HBM bytes of one MMQ launch: the weight planes once, the q8
-    activations once, the f32 output once."""
-    qact = T * id_ * 9 // 8
-    return w.plane_bytes + qact + T * od * 4
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def cpu_baseline(type_, od, id_, T, raw, x, threads):
+def measured_traffic(workload: str):
+    """HBM bytes per MMQ launch from the committed counter summary, or None if
+    there is none for this workload or the kernel changed since it was taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else w.get("bytes_per_launch")
+
+
+def cpu_baseline(gemms, raws, xs, T, threads, macs_target):
+    """The oracle, as it stands, on a bounded sample of the workload: all tokens,
+    the first rows of every GEMM (same fraction for each), rows split over threads."""
     import oracle
+    total = sum(T * od * id_ for _, _, od, id_, _ in gemms)
+    frac = min(1.0, macs_target / total)
     t0 = time.perf_counter()
-    q, dh, s = oracle.quantize(x)
+    quant = {name: oracle.quantize(x) for name, x in xs.items()}
     t1 = time.perf_counter()
-    bounds = np.linspace(0, od, threads + 1).astype(int)
+    jobs, macs = [], 0
+    for (gname, type_, od, id_, inp) in gemms:
+        rows = max(1, int(round(od * frac)))
+        macs += T * rows * id_
+        bounds = np.linspace(0, rows, threads + 1).astype(int)
+        for i in range(threads):
+            if bounds[i + 1] > bounds[i]:
+                jobs.append((type_, raws[gname], od, id_, quant[inp], int(bounds[i]), int(bounds[i + 1])))
 
-    def work(i):
-        oracle.mmq_rows(type_, raw, od, id_, q, dh, s, int(bounds[i]), int(bounds[i + 1]))
+    def work(j):
+        type_, raw, od, id_, (q, dh, s), a, b = j
+        oracle.mmq_rows(type_, raw, od, id_, q, dh, s, a, b)
 
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(work, range(threads)))
+        list(ex.map(work, jobs))
     t2 = time.perf_counter()
-    ops = 2.0 * T * od * id_
     return {
-        "value": round(ops / (t2 - t0) / 1e12, 6),
+        "value": round(2.0 * macs / (t2 - t0) / 1e12, 6),
         "unit": "effective int8 TOPS",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"the whole workload ({T} tokens x {od} rows x {id_}): q8 quantize on 1 thread "
-                   f"({t1 - t0:.2f} s) + the f64 oracle MMQ over {threads} threads of row slices "
+        "sample": (f"all {T} tokens x the first {frac * 100:.1f}% of the rows of each GEMM "
+                   f"({macs / 1e9:.1f} G multiply-accumulates): q8 quantize of every input on 1 "
+                   f"thread ({t1 - t0:.2f} s) + the f64 oracle MMQ over {threads} threads "
                    f"({t2 - t1:.2f} s wall)"),
         "seconds": round(t2 - t0, 3),
     }
@@ -94,31 +145,42 @@ def main():
     import torch
     import quant_q8_gemm_amd as qmm
 
-    name, type_, od, id_, T, outliers = WORKLOADS[args.workload]
+    desc, T, inputs, gemms, outliers = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
-    raw, x = synth.case(type_, od, id_, T, seed=0, outliers=outliers)
-    w = qmm.register_weights(type_, od, id_, raw)
-    xd = torch.from_numpy(x).cuda()
-    qact = torch.empty(qmm.qact_bytes(T, id_), dtype=torch.uint8, device="cuda")
-    out = torch.empty((T, od), dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(0)
+    raws, weights = {}, {}
+    for (gname, type_, od, id_, _) in gemms:
+        raws[gname] = synth.weights(rng, type_, od, id_)
+        weights[gname] = qmm.register_weights(type_, od, id_, raws[gname])
+    xs = {name: synth.activations(rng, T, id_, outliers) for name, id_ in inputs.items()}
+    xd = {name: torch.from_numpy(x).cuda() for name, x in xs.items()}
+    qacts = {name: torch.empty(qmm.qact_bytes(T, id_), dtype=torch.uint8, device="cuda")
+             for name, id_ in inputs.items()}
+    outs = {g[0]: torch.empty((T, g[2]), dtype=torch.float32, device="cuda") for g in gemms}
     stream = torch.cuda.current_stream()
+    n_in, n_g = len(inputs), len(gemms)
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        qmm.quantize_activations(xd, qact, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        qmm.mmq(w, qact, T, out, stream)
-        if ev is not None:
-            ev[2].record(stream)
+        for i, name in enumerate(inputs):
+            if ev is not None:
+                ev[i][0].record(stream)
+            qmm.quantize_activations(xd[name], qacts[name], stream)
+            if ev is not None:
+                ev[i][1].record(stream)
+        for k, (gname, _, _, _, inp) in enumerate(gemms):
+            if ev is not None:
+                ev[n_in + k][0].record(stream)
+            qmm.mmq(weights[gname], qacts[inp], T, outs[gname], stream)
+            if ev is not None:
+                ev[n_in + k][1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # timed region: exactly K steps, bracketed by device synchronization
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_in + n_g)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -126,13 +188,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    mmq_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    per = np.array([[e[0].elapsed_time(e[1]) for e in evk] for evk in evs])  # [steps][kernels] ms
+    pre_ms = per[:, :n_in].sum(axis=1)
+    mmq_ms = per[:, n_in:].sum(axis=1)
     ms_per_step = wall * 1e3 / args.steps
-    ops = 2.0 * T * od * id_
+    ops = sum(2.0 * T * od * id_ for _, _, od, id_, _ in gemms)
     mmq_avg_s = float(mmq_ms.mean()) / 1e3
     mmq_tops = ops / mmq_avg_s / 1e12
-    pre_bytes = T * id_ * 4 + qmm.qact_bytes(T, id_)
+    pre_bytes = sum(T * id_ * 4 + qmm.qact_bytes(T, id_) for id_ in inputs.values())
+    alg_bytes = sum(weights[g].plane_bytes + T * id_ * 9 // 8 + T * od * 4
+                    for g, _, od, id_, _ in gemms)
+    traffic = measured_traffic(args.workload)
 
     result = {
         "metric": "effective int8 TOPS (q6_K/q4_K x q8 MMQ, prepass + GEMM per step)",
@@ -147,17 +213,22 @@ def main():
         "vs_baseline": None,
         "dtype": "i8",
         "data": "synthetic",
-        "config": {"workload": name, "type": synth.TYPE_NAMES[type_], "od": od, "id": id_,
-                   "n_tok": T, "parallelism": "single GPU"},
+        "config": {"workload": desc, "n_tok": T,
+                   "gemms": [{"name": g, "type": synth.TYPE_NAMES[t], "od": od, "id": id_}
+                             for g, t, od, id_, _ in gemms],
+                   "parallelism": "single GPU"},
         "pct_int8_mfma_peak": round(100.0 * ops / (ms_per_step / 1e3) / 1e12 / MFMA_INT8_PEAK_TOPS, 2),
-        "token_rows_per_s": round(T * od / (ms_per_step / 1e3), 1),
+        "token_rows_per_s": round(sum(T * g[2] for g in gemms) / (ms_per_step / 1e3), 1),
         "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
         "mmq": {"avg_ms": round(float(mmq_ms.mean()), 4), "median_ms": round(float(np.median(mmq_ms)), 4),
                 "min_ms": round(float(mmq_ms.min()), 4), "max_ms": round(float(mmq_ms.max()), 4),
-                "effective_tops": round(mmq_tops, 2)},
+                "effective_tops": round(mmq_tops, 2),
+                "per_gemm_ms": {g[0]: round(float(per[:, n_in + k].mean()), 4) for k, g in enumerate(gemms)}},
         "prepass": {"avg_ms": round(float(pre_ms.mean()), 4),
+                    "bytes": pre_bytes,
                     "gb_per_s": round(pre_bytes / (float(pre_ms.mean()) / 1e3) / 1e9, 1),
-                    "pct_hbm_peak": round(100 * pre_bytes / (float(pre_ms.mean()) / 1e3) / 1e9 / HBM_PEAK_GBS, 1)},
+                    "pct_hbm_peak": round(100 * pre_bytes / (float(pre_ms.mean()) / 1e3) / 1e9 / HBM_PEAK_GBS, 1),
+                    "per_input_ms": {name: round(float(per[:, i].mean()), 4) for i, name in enumerate(inputs)}},
         "roofline": {
             "kernel": "mmq_kernel",
             "bound": "mfma",
@@ -165,17 +236,19 @@ def main():
             "peak": MFMA_INT8_PEAK_TOPS,
             "unit": "TOP/s",
             "frac": round(mmq_tops / MFMA_INT8_PEAK_TOPS, 4),
-            "traffic": None,
-            "algorithmic_bytes": algorithmic_bytes(type_, od, id_, T, w),
-            "algorithmic_ops": ops,
+            "traffic": traffic,
+            "algorithmic_ops_per_step": ops,
+            "algorithmic_bytes_per_step": alg_bytes,
+            "kernel_sha256_16": kernel_hash(),
         },
-        "plane_bytes": w.plane_bytes,
-        "raw_weight_bytes": w.raw_bytes,
+        "plane_bytes": sum(w.plane_bytes for w in weights.values()),
+        "raw_weight_bytes": sum(w.raw_bytes for w in weights.values()),
     }
     if not args.no_cpu:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
-        result["cpu_baseline"] = cpu_baseline(type_, od, id_, T, raw, x, threads)
-    w.release()
+        result["cpu_baseline"] = cpu_baseline(gemms, raws, xs, T, threads, args.cpu_macs)
+    for w in weights.values():
+        w.release()
     print(json.dumps(result), flush=True)
 
 

@@ -261,7 +261,10 @@ def _sample_pairs(rng, T, od, n=3000):
     return np.array(ts)[order], np.array(js)[order]
 
 
-FULL = [synth.C2, synth.C2_ODD, synth.C3_QKVO, synth.C3_GU, synth.C4]
+# the one-layer workload at 3314 tokens: its four distinct GEMM shapes
+LAYER = [(f"layer {synth.TYPE_NAMES[t]} {od}x{id_} T={synth.C5_TOKENS}", t, od, id_, synth.C5_TOKENS, False)
+         for t, od, id_ in sorted({(t, od, id_) for _, t, od, id_ in synth.C5_LAYER})]
+FULL = [synth.C2, synth.C2_ODD, synth.C3_QKVO, synth.C3_GU, synth.C4] + LAYER
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=[c[0] for c in FULL])
