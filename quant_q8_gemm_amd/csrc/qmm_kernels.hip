@@ -240,14 +240,26 @@ struct alignas(16) Stage {
   static constexpr int kJobs = WR * KC * 2 + WT * KC + kSmallJobs;  // wave instructions
 };
 
-// Work-group index -> tile index.  Work-groups are dispatched round-robin over
-// the 8 XCDs (each with its own L2); this map gives every XCD a contiguous run
-// of tiles in row-major (row tile, token tile) order, so the work-groups that
-// stream the same weight rows share one L2.
+// Work-group index -> (row tile, token tile).  Work-groups are dispatched
+// round-robin over the 8 XCDs (each with its own 4 MiB L2), so first every XCD
+// gets a contiguous run of positions; positions then walk the tiles in groups of
+// kGroupRows row tiles, row tile fastest, so the work-groups resident on one XCD
+// at a time (about 96) form a block of ~8 row tiles x ~12 token tiles that
+// share both their weight rows and their activations in that L2.
+constexpr int kGroupRows = 8;
+
 __device__ __forceinline__ int xcd_swizzle(int i, int n) {
   const int q = n / 8, r = n % 8;
   const int x = i % 8, slot = i / 8;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + slot;
+}
+
+__device__ __forceinline__ void tile_of(int pos, int row_tiles, int tok_tiles, int& rt, int& tt) {
+  const int per_group = kGroupRows * tok_tiles;
+  const int g = pos / per_group, idx = pos % per_group;
+  const int rows_here = min(kGroupRows, row_tiles - g * kGroupRows);  // last group may be short
+  rt = g * kGroupRows + idx % rows_here;
+  tt = idx / rows_here;
 }
 
 template <int TYPE, int WR, int WT, int KC>
@@ -267,8 +279,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int wr = wave / WT, wt = wave % WT;
-  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int rt = tile / tok_tiles, tt = tile % tok_tiles;
+  int rt, tt;
+  tile_of(xcd_swizzle(blockIdx.x, gridDim.x), gridDim.x / tok_tiles, tok_tiles, rt, tt);
   const int rb0 = rt * WR, tb0 = tt * WT;
   const int nstages = nchunk / KC;
 
