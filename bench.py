@@ -64,7 +64,7 @@ WORKLOADS = {
 # rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a plain copy's reading); valid
 # only while the kernel source is the one they were taken with.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmq_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "quant_q8_gemm_amd", "csrc", "qmm_kernels.hip")
+KERNEL_SRC = os.path.join(ROOT, "quant_q8_gemm_amd", "csrc", "qmm_mmq.hip")
 
 
 def _parse():
@@ -85,7 +85,8 @@ def kernel_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per MMQ launch from the committed counter summary, or None if
+    """HBM bytes of the MMQ launches of one step from the committed counter
+    summary (per launch for single-GEMM workloads), or None if
     there is none for this workload or the kernel changed since it was taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
@@ -94,7 +95,7 @@ def measured_traffic(workload: str):
     if rec.get("kernel_sha256_16") != kernel_hash():
         return None
     w = rec.get("workloads", {}).get(workload)
-    return None if w is None else w.get("bytes_per_launch")
+    return None if w is None else w.get("bytes_per_step")
 
 
 def cpu_baseline(gemms, raws, xs, T, threads, macs_target):

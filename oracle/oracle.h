@@ -20,6 +20,11 @@
  * rounding of the activation quantizer, what "sum" means in the scale pair) the
  * readings used are the ones listed in the functions below; each is the public
  * llama.cpp ("ggml") k-quant / q8_1 convention restated in prose.
+ *
+ * Parity unpinned: the element bit layouts inside the q6_K ql/qh bytes, the q4_K
+ * qs nibbles and the q4_K 12-byte scale/min packing are pinned by the tests only
+ * to their restatement here (literal spot positions and a bit bijection); no
+ * llama.cpp decoder or GGUF fixture is available to compare against.
  */
 #ifndef QMM_ORACLE_H
 #define QMM_ORACLE_H

@@ -7,7 +7,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, "qmm_api.cpp"), os.path.join(CSRC, "qmm_kernels.hip")]
+KERNELS = ["qmm_repack.hip", "qmm_prepass.hip", "qmm_mmq.hip"]
+SOURCES = [os.path.join(CSRC, "qmm_api.cpp")] + [os.path.join(CSRC, k) for k in KERNELS]
 LIB = os.path.join(HERE, "libqmm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -32,13 +33,20 @@ def build(verbose: bool = False) -> str:
 
 
 def device_asm(out_path: str) -> str:
-    """gfx950 assembly of the kernels (for inspection: instruction mix, VGPRs,
-    scratch), written to out_path."""
-    cmd = [HIPCC, *DEVICE_FLAGS, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"),
-           os.path.join(CSRC, "qmm_kernels.hip"), "-o", out_path]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc -S failed:\n" + r.stderr)
+    """gfx950 assembly of all kernels (for inspection: instruction mix, VGPRs,
+    scratch), concatenated into out_path."""
+    parts = []
+    for k in KERNELS:
+        tmp = out_path + "." + k + ".s"
+        cmd = [HIPCC, *DEVICE_FLAGS, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"),
+               os.path.join(CSRC, k), "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc -S failed:\n" + r.stderr)
+        parts.append(open(tmp).read())
+        os.remove(tmp)
+    with open(out_path, "w") as f:
+        f.write("\n".join(parts))
     return out_path
 
 

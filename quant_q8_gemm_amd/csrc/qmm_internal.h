@@ -9,7 +9,7 @@
 namespace qmm {
 
 // Device planes of one registered weight matrix (layout documented in
-// qmm_kernels.hip next to the repack kernel).
+// qmm_repack.hip next to the repack kernel).
 struct Planes {
   int type;          // QMM_Q4_K or QMM_Q6_K
   int64_t od, id;    // logical shape

@@ -1,0 +1,116 @@
+// qmm_repack.hip -- registration-time repack of q6_K / q4_K blocks into the
+// planes the MMQ streams (the once-per-weight expansion of the r56 and r58
+// pages of the engineering log "minfer / cuda_optimization_steps": r56 sections
+// 2.2-2.3, r58 section 3.2).  Instead of the pages' f32 d*scale pair plane, the
+// small integer scale of every 16/32-weight group is multiplied into the codes
+// (exact) and split into two int8 planes (hi = w >> 6, lo = w & 63), so one
+// K=32 int8 MFMA per plane yields the scale-folded block dot J = 64*J_hi + J_lo;
+// only the f16 d of the 256-weight super-block stays a float.
+#include "qmm_internal.h"
+#include "qmm_common.h"
+
+#include "../../include/qmm.h"
+
+namespace qmm {
+
+// ---------------------------------------------------------------------------
+// Plane layout (all device, all library-owned; R = od_pad/32 row blocks):
+//   wq  int8  [R][nchunk][2 planes: hi, lo][2 k-halves][32 rows][16 bytes]
+//             byte (row j, k) of plane p at
+//             ((j/32*nchunk + k/32)*2 + p)*1024 + ((k%32)/16)*512 + (j%32)*16 + k%16
+//             where the folded weight w = hi*64 + lo, lo in [0, 63]:
+//               q6_K  w = sc[k/16] * (code - 32)      in [-4064, 4096]
+//               q4_K  w = sc[k/32 % 8] * code         in [0, 945]
+//   wd  f32   [R][nsb][32 rows]      d of (row, super-block)
+//   wm  f32   [R][nchunk][32 rows]   -dmin*min of (row, chunk); q4_K only
+// Rows od..od_pad-1 are zero in every plane.
+// ---------------------------------------------------------------------------
+size_t wq_bytes(int64_t od_pad, int64_t id) { return (size_t)od_pad * (size_t)id * 2; }
+size_t wd_bytes(int64_t od_pad, int64_t id) { return (size_t)od_pad * (size_t)(id / 256) * 4; }
+size_t wm_bytes(int type, int64_t od_pad, int64_t id) {
+  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) * 4 : 0;
+}
+
+// One thread per (row j in [0, od_pad), chunk c, k-half h): 16 folded weights.
+__global__ void __launch_bounds__(256)
+repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nchunk,
+              int64_t total, int8_t* __restrict__ wq, float* __restrict__ wd,
+              float* __restrict__ wm) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const int h = (int)(gid & 1);
+  const int64_t rc = gid >> 1;
+  const int c = (int)(rc % nchunk);
+  const int j = (int)(rc / nchunk);
+  const int rb = j >> 5, jr = j & 31;
+  const int b = c >> 3, cl = c & 7;
+
+  uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
+  if (j < od) {
+    if (type == QMM_Q6_K) {
+      // 210-byte block: ql[128] | qh[64] | int8 scales[16] | f16 d (r56 section 1)
+      const uint8_t* B = raw + ((int64_t)j * nsb + b) * 210;
+      const int e0 = 32 * cl + 16 * h;          // first element inside the super-block
+      const int half = e0 >> 7;                 // which 128-element half
+      const int quarter = (e0 & 127) >> 5;      // which 32-element quarter of the half
+      const int l0 = e0 & 31;
+      const int sc = (int)(int8_t)B[192 + (e0 >> 4)];
+      const uint8_t* ql = B + 64 * half + 32 * (quarter & 1);
+      const uint8_t* qh = B + 128 + 32 * half;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int l = l0 + i;
+        const int lowbits = quarter < 2 ? (ql[l] & 15) : (ql[l] >> 4);
+        const int highbits = (qh[l] >> (2 * quarter)) & 3;
+        const int w = sc * ((lowbits | (highbits << 4)) - 32);
+        hi[i >> 2] |= (uint32_t)(uint8_t)(int8_t)(w >> 6) << (8 * (i & 3));
+        lo[i >> 2] |= (uint32_t)(w & 63) << (8 * (i & 3));
+      }
+      if (h == 0 && cl == 0)
+        wd[((int64_t)rb * nsb + b) * 32 + jr] = f16_bits_to_float(B[208] | (B[209] << 8));
+    } else {
+      // 144-byte block: f16 d | f16 dmin | 12 bytes of 6-bit scales/mins | qs[128]
+      const uint8_t* B = raw + ((int64_t)j * nsb + b) * 144;
+      const uint8_t* P = B + 4;
+      int sc, mn;
+      if (cl < 4) {
+        sc = P[cl] & 63;
+        mn = P[cl + 4] & 63;
+      } else {
+        sc = (P[cl + 4] & 15) | ((P[cl - 4] >> 6) << 4);
+        mn = (P[cl + 4] >> 4) | ((P[cl] >> 6) << 4);
+      }
+      // 32-element sub-block cl: codes in qs[32*(cl/2) + 0..31], low nibble for
+      // even sub-blocks, high nibble for odd ones
+      const uint8_t* qs = B + 16 + 32 * (cl >> 1) + 16 * h;
+      const int shift = (cl & 1) * 4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int w = sc * ((qs[i] >> shift) & 15);
+        hi[i >> 2] |= (uint32_t)(w >> 6) << (8 * (i & 3));
+        lo[i >> 2] |= (uint32_t)(w & 63) << (8 * (i & 3));
+      }
+      if (h == 0) {
+        const float dmin = f16_bits_to_float(B[2] | (B[3] << 8));
+        wm[((int64_t)rb * nchunk + c) * 32 + jr] = -(dmin * (float)mn);
+        if (cl == 0) wd[((int64_t)rb * nsb + b) * 32 + jr] = f16_bits_to_float(B[0] | (B[1] << 8));
+      }
+    }
+  } else if (h == 0) {
+    if (type == QMM_Q4_K) wm[((int64_t)rb * nchunk + c) * 32 + jr] = 0.0f;
+    if (cl == 0) wd[((int64_t)rb * nsb + b) * 32 + jr] = 0.0f;
+  }
+  int8_t* dst = wq + ((int64_t)rb * nchunk + c) * 2048 + h * 512 + jr * 16;
+  *(uint4*)dst = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  *(uint4*)(dst + 1024) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+}
+
+hipError_t launch_repack(const uint8_t* raw, const Planes& p, hipStream_t s) {
+  const int64_t total = p.od_pad * p.nchunk * 2;
+  const int64_t blocks = (total + 255) / 256;
+  repack_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+      raw, p.type, (int)p.od, (int)p.nsb, (int)p.nchunk, total, p.wq, p.wd, p.wm);
+  return hipGetLastError();
+}
+
+}  // namespace qmm
