@@ -34,7 +34,8 @@ namespace qmm {
 // global->LDS loads (global_load_lds_dwordx4 puts lane l's 16 bytes at the LDS
 // base + 16*l, so one wave instruction moves one 1 KiB fragment), and read from
 // there by every wave that shares them.  Two LDS stages alternate: the loads of
-// stage g+1 are issued before stage g is computed; one barrier per stage.
+// stage g+1 are issued during stage g, a few per chunk step; one barrier per
+// stage.
 // A small tile and a small LDS footprint let several work-groups share a CU, so
 // one group's barrier wait is covered by the others' work.
 // MFMA orientation: A = weights (rows j), B = activations (columns t), so each
@@ -84,7 +85,6 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
            int tok_tiles, int vec_store, float* __restrict__ out) {
   using St = Stage<WR, WT, KC>;
   constexpr int kWaves = WR * WT;
-  constexpr int kRounds = (St::kJobs + kWaves - 1) / kWaves;
   constexpr int kJobsA = WR * KC * 2, kJobsB = WT * KC;
   static_assert(KC == 4 || KC == 8, "a stage is half or a whole super-block");
   __shared__ St stage[2];
@@ -98,20 +98,22 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   const int rb0 = rt * WR, tb0 = tt * WT;
   const int nstages = nchunk / KC;
 
-  // Copy jobs of one stage: job k (one wave instruction, 1 KiB) goes to wave
-  // k % kWaves.  Jobs [0, kJobsA) are weight fragments, then code fragments,
-  // then the small region (scale pairs, mins, d) in 16-byte units per lane.
-  const int8_t* srcA = wq + (size_t)rb0 * nchunk * 2048;  // + stage * KC * 2048
-  const uint8_t* srcB = qq + (size_t)tb0 * nchunk * 1024;  // + stage * KC * 1024
-  const int small_k0 = kJobsA + kJobsB;
-  // The small job this wave owns, if any (at most one: asserted below).
+  // Copy jobs of one stage (one wave instruction, 1 KiB each): the weight
+  // fragments, then the code fragments, split into equal contiguous runs per
+  // wave (a run stays inside one row / token block, so its source is one
+  // uniform base plus immediate 1 KiB steps); then the small region (scale
+  // pairs, mins, d) in 16-byte units per lane, one job each for the first waves.
+  static_assert(kJobsA % kWaves == 0 && kJobsB % kWaves == 0, "equal copy runs per wave");
+  constexpr int kRunA = kJobsA / kWaves, kRunB = kJobsB / kWaves;
+  static_assert((KC * 2) % kRunA == 0 && KC % kRunB == 0, "a run stays inside one block");
   static_assert(St::kSmallJobs <= kWaves, "one small-region job per wave at most");
-  const int small_r = (small_k0 - wave + kWaves - 1) / kWaves;  // round of this wave's first job >= small_k0
-  const int small_k = wave + small_r * kWaves;
+  const int ka0 = wave * kRunA, kb0 = wave * kRunB;
+  const int8_t* srcA = wq + (size_t)(rb0 + ka0 / (KC * 2)) * nchunk * 2048 + (ka0 % (KC * 2)) * 1024;
+  const uint8_t* srcB = qq + (size_t)(tb0 + kb0 / KC) * nchunk * 1024 + (kb0 % KC) * 1024;
   const uint8_t* small_src = nullptr;
   int small_kind = 0;  // 0 none, 1 pairs/mins (advance per stage), 2 d (advance per super-block)
-  if (small_k < St::kJobs) {
-    const int u = (small_k - small_k0) * 64 + lane;
+  if (wave < St::kSmallJobs) {
+    const int u = wave * 64 + lane;
     if (u < St::kUnitsS) {
       small_src = qs + ((size_t)(tb0 + u / (KC * 8)) * nchunk) * 128 + (u % (KC * 8)) * 16;
       small_kind = 1;
@@ -129,33 +131,31 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   }
 
 #define QMM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-  auto issue_stage = [&](int g, St& st) __attribute__((always_inline)) {
-    const int8_t* sa = srcA + (size_t)g * KC * 2048;
-    const uint8_t* sbp = srcB + (size_t)g * KC * 1024;
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const int k = wave + r * kWaves;  // uniform
-      if (k < kJobsA) {
-        const int blk = k / (KC * 2), sub = k % (KC * 2);
-        __builtin_amdgcn_global_load_lds(sa + (size_t)blk * nchunk * 2048 + sub * 1024 + lane * 16,
-                                         QMM_LDS(&st.a[0][0][0][0] + k * 1024), 16, 0, 0);
-      } else if (k < kJobsA + kJobsB) {
-        const int kb = k - kJobsA;
-        const int blk = kb / KC, sub = kb % KC;
-        __builtin_amdgcn_global_load_lds(sbp + (size_t)blk * nchunk * 1024 + sub * 1024 + lane * 16,
-                                         QMM_LDS(&st.b[0][0][0] + kb * 1024), 16, 0, 0);
-      }
-    }
-    if (small_k < St::kJobs) {
-      uint8_t* ls = (uint8_t*)&st.s[0][0][0] + (small_k - small_k0) * 1024;
-      // pairs/mins advance by KC chunks per stage; d by one super-block per 8
-      // chunks, loaded into the stage that ends the super-block
+  // This wave's copy jobs for one stage, numbered: its weight run, its code run,
+  // its small-region job.  The jobs of stage g+1 are spread over the chunk steps
+  // of stage g (a few per step) rather than issued in one burst, so the copies'
+  // LDS writes interleave with the steps' LDS reads instead of stalling them.
+  constexpr int kWaveJobs = kRunA + kRunB + 1;
+  auto issue_job = [&](int g, St& st, int j) __attribute__((always_inline)) {
+    if (j < kRunA) {
+      __builtin_amdgcn_global_load_lds(srcA + (size_t)g * KC * 2048 + lane * 16 + j * 1024,
+                                       QMM_LDS(&st.a[0][0][0][0] + (ka0 + j) * 1024), 16, 0, 0);
+    } else if (j < kRunA + kRunB) {
+      const int u = j - kRunA;
+      __builtin_amdgcn_global_load_lds(srcB + (size_t)g * KC * 1024 + lane * 16 + u * 1024,
+                                       QMM_LDS(&st.b[0][0][0] + (kb0 + u) * 1024), 16, 0, 0);
+    } else if (wave < St::kSmallJobs) {
+      uint8_t* ls = (uint8_t*)&st.s[0][0][0] + wave * 1024;
       const bool ends_sb = ((g + 1) * KC) % 8 == 0;
       if (small_kind == 1)
         __builtin_amdgcn_global_load_lds(small_src + (size_t)g * KC * 128, QMM_LDS(ls), 16, 0, 0);
       else if (small_kind == 2 && ends_sb)
         __builtin_amdgcn_global_load_lds(small_src + (size_t)((g * KC) / 8) * 128, QMM_LDS(ls), 16, 0, 0);
     }
+  };
+  auto issue_stage = [&](int g, St& st) __attribute__((always_inline)) {  // all at once (prologue)
+#pragma unroll
+    for (int j = 0; j < kWaveJobs; ++j) issue_job(g, st, j);
   };
 
   v16f acc, inner;
@@ -169,9 +169,6 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
 
   for (int g = 0; g < nstages; ++g) {
     St& st = stage[g & 1];
-    // stage (g+1)&1 was last read in iteration g-1, which every wave finished
-    // before the barrier that ended it
-    if (g + 1 < nstages) issue_stage(g + 1, stage[(g + 1) & 1]);
     const bool starts_sb = (g * KC) % 8 == 0;
     // Software pipeline over the KC chunks: step cc reads the LDS operands of
     // chunk cc+2, issues the two MFMAs of chunk cc+1, then runs the scale
@@ -187,6 +184,14 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int cc = 0; cc < KC; ++cc) {
+      // stage (g+1)&1 was last read in iteration g-1, which every wave finished
+      // before the barrier that ended it
+      if (g + 1 < nstages) {
+        constexpr int per = (kWaveJobs + KC - 1) / KC;
+#pragma unroll
+        for (int q = 0; q < per; ++q)
+          if (cc * per + q < kWaveJobs) issue_job(g + 1, stage[(g + 1) & 1], cc * per + q);
+      }
       const float dh = f16_bits_to_float(st.s[wt][cc][lane & 31] & 0xFFFF);
       v4i ahi2, alo2, bq2;
       if (cc + 2 < KC) {
@@ -222,7 +227,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         alo1 = alo2;
         bq1 = bq2;
       }
-      // order inside the step: LDS reads, then MFMAs, then the vector epilogue
+      // order inside the step: stage copies, LDS reads, MFMAs, the vector epilogue
+      __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);   // VMEM (stage copies)
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
       __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);  // VALU
