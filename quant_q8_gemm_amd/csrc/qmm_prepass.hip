@@ -14,13 +14,23 @@ namespace qmm {
 // A wave covers 8 consecutive tokens of one chunk, so its q bytes land as two
 // contiguous 128-byte runs of the fragment and its scale pairs as 32 bytes.
 // ---------------------------------------------------------------------------
-constexpr int kQuantChunks = 8;
+constexpr int kQuantChunks = 4;
 
-__device__ __forceinline__ int quant1(float v, float dhf) {
+// q = clamp(rint(v / dh), -127, 127) where v / dh is the correctly rounded f32
+// quotient (IEEE division) and rint rounds half to even.  The correctly rounded
+// division costs about a dozen instructions, so the quotient is first formed as
+// v * rcp(dh): with |v / dh| <= 127.1 (|v| <= amax, dh = f16(amax/127)) the
+// reciprocal (1 ulp) and the product (0.5 ulp) put it within 2.3e-5 of the
+// exact quotient, and the correctly rounded quotient is within 3.8e-6 of it.
+// So unless the product lies within 1e-4 of a half-integer, both round to the
+// same integer; in that rare case the quotient is divided exactly.
+__device__ __forceinline__ int quant1(float v, float dhf, float inv) {
   if (dhf == 0.0f) return 0;
-  float r = __builtin_rintf(v / dhf);  // IEEE division, round half to even
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int)r;
+  const float r = v * inv;
+  float n = __builtin_rintf(r);
+  if (fabsf(r - n) > 0.5f - 1e-4f) n = __builtin_rintf(v / dhf);
+  n = fminf(fmaxf(n, -127.0f), 127.0f);
+  return (int)n;
 }
 
 __global__ void __launch_bounds__(256)
@@ -52,8 +62,9 @@ quantize_kernel(const float* __restrict__ x, int n_tok, int id, int nchunk,
     const float d32 = amax / 127.0f;
     const _Float16 dh = (_Float16)d32;  // round to nearest even
     const float dhf = (float)dh;
-    const int q0 = quant1(v[i].x, dhf), q1 = quant1(v[i].y, dhf);
-    const int q2 = quant1(v[i].z, dhf), q3 = quant1(v[i].w, dhf);
+    const float inv = __builtin_amdgcn_rcpf(dhf);
+    const int q0 = quant1(v[i].x, dhf, inv), q1 = quant1(v[i].y, dhf, inv);
+    const int q2 = quant1(v[i].z, dhf, inv), q3 = quant1(v[i].w, dhf, inv);
     int S = q0 + q1 + q2 + q3;
     S += __shfl_xor(S, 1);
     S += __shfl_xor(S, 2);

@@ -104,6 +104,25 @@ def test_prepass_special_values():
     check_prepass(x, gpu_quantize(x))
 
 
+def test_prepass_near_ties():
+    """Quotients x/dh a few f32 ulps either side of half-integers (and exactly on
+    them): the rounding decision must match the correctly rounded division."""
+    say("prepass near ties")
+    rng = np.random.default_rng(11)
+    T, id_ = 64, 1024
+    x = np.zeros((T, id_), np.float32)
+    xb = x.reshape(T, -1, 32)
+    steps = (np.abs(rng.standard_normal(xb.shape[:2])) * 0.05 + 1e-3).astype(np.float16).astype(np.float32)
+    # element 0 of each block fixes amax = 127 * step, so dh = f16(step * 127 / 127) = step
+    xb[:, :, 0] = 127 * steps
+    k = rng.integers(-126, 126, size=xb[:, :, 1:].shape).astype(np.float32)
+    ulps = rng.integers(-3, 4, size=k.shape)
+    target = ((k + 0.5) * steps[:, :, None]).astype(np.float32)
+    xb[:, :, 1:] = np.nextafter(target, np.where(ulps > 0, np.inf, -np.inf).astype(np.float32))
+    xb[:, :, 1:] = np.where(ulps == 0, target, xb[:, :, 1:])
+    check_prepass(x, gpu_quantize(x))
+
+
 # --------------------------------------------------------------------------
 # registration planes
 # --------------------------------------------------------------------------
