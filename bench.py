@@ -59,6 +59,17 @@ WORKLOADS = {
                ("ffn_up", synth.Q4_K, 11008, 4096, "ffn_in"),
                ("ffn_down", synth.Q6_K, 4096, 11008, "ffn_mid")],
               False),
+    # the same layer with same-type GEMMs that share an input fused by row
+    # concatenation at registration: q||k (od 8192) and gate||up (od 22016)
+    "layer_fused": ("LLaMA-7B q4_K_M-style layer, 3314 tokens, q||k and gate||up fused",
+                    synth.C5_TOKENS,
+                    {"attn_in": 4096, "attn_out": 4096, "ffn_in": 4096, "ffn_mid": 11008},
+                    [("attn_qk", synth.Q4_K, 8192, 4096, "attn_in"),
+                     ("attn_v", synth.Q6_K, 4096, 4096, "attn_in"),
+                     ("attn_output", synth.Q4_K, 4096, 4096, "attn_out"),
+                     ("ffn_gate_up", synth.Q4_K, 22016, 4096, "ffn_in"),
+                     ("ffn_down", synth.Q6_K, 4096, 11008, "ffn_mid")],
+                    False),
 }
 
 # Counter summaries committed under profiles/ (HBM bytes per MMQ launch from

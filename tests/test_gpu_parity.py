@@ -325,6 +325,29 @@ def test_odd_rows_and_token_tail_are_prefixes_and_repeatable():
     assert np.array_equal(out509, out_odd[:509])
 
 
+@pytest.mark.parametrize("T", [512, 3314])
+def test_fused_same_type_gemms_match_separate(T):
+    """Row-concatenated registration (gate||up, q||k) gives, column block by
+    column block, bit-identical results to the separate GEMMs on one shared qact,
+    whichever tile geometry each launch selects."""
+    say(f"fused gate||up and q||k, T={T}")
+    rng = np.random.default_rng(21)
+    id_ = 4096
+    x = synth.activations(rng, T, id_)
+    qact = gpu_quantize(x)
+    for od in (11008, 4096):
+        raw_a = synth.q4k_weights(rng, od, id_)
+        raw_b = synth.q4k_weights(rng, od, id_)
+        wa = qmm.register_weights(synth.Q4_K, od, id_, raw_a)
+        wb = qmm.register_weights(synth.Q4_K, od, id_, raw_b)
+        wf = qmm.register_weights(synth.Q4_K, 2 * od, id_, np.concatenate([raw_a, raw_b]))
+        fused = run_mmq(wf, qact, T)
+        assert np.array_equal(fused[:, :od], run_mmq(wa, qact, T))
+        assert np.array_equal(fused[:, od:], run_mmq(wb, qact, T))
+        for w in (wa, wb, wf):
+            w.release()
+
+
 def test_writes_stay_inside_output():
     type_, od, id_, T = synth.Q4_K, 77, 512, 45
     say("output bounds")
