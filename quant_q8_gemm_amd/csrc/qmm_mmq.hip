@@ -25,8 +25,12 @@
 namespace qmm {
 
 // ---------------------------------------------------------------------------
-// MMQ.  A work-group of WR x WT waves owns a (32*WR rows) x (32*WT tokens)
-// output tile, one 32 x 32 block per wave.  The inner dimension is walked in
+// MMQ.  A work-group of KS x WR x WT waves owns a (32*WR rows) x (32*WT tokens)
+// output tile, one 32 x 32 block per wave and k-group.  With KS = 2 the two
+// k-groups take the first and the second half of the super-blocks, each with
+// its own LDS stages, and their sums are added once at the end (k-group 0's
+// plus k-group 1's, always in that order): twice the waves per tile for shapes
+// with too few tiles to keep the CUs busy.  The inner dimension is walked in
 // stages of KC chunks of 32 (KC = 4: half a 256-wide super-block, KC = 8: a
 // whole one).  Each stage's operands -- both weight planes of the WR row blocks,
 // the q8 codes and scale pairs of the WT token blocks, and d (and for q4_K the
@@ -77,8 +81,8 @@ __device__ __forceinline__ void tile_of(int pos, int row_tiles, int tok_tiles, i
   tt = idx / rows_here;
 }
 
-template <int TYPE, int WR, int WT, int KC>
-__global__ void __launch_bounds__(64 * WR * WT, (WR * WT == 4) ? 3 : 1)
+template <int TYPE, int WR, int WT, int KC, int KS>
+__global__ void __launch_bounds__(64 * WR * WT * KS, (WR * WT * KS == 4) ? 3 : 1)
 mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
            const float* __restrict__ wm, const uint8_t* __restrict__ qq,
            const uint8_t* __restrict__ qs, int nchunk, int nsb, int od, int n_tok,
@@ -87,16 +91,26 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   constexpr int kWaves = WR * WT;
   constexpr int kJobsA = WR * KC * 2, kJobsB = WT * KC;
   static_assert(KC == 4 || KC == 8, "a stage is half or a whole super-block");
-  __shared__ St stage[2];
+  static_assert(KS == 1 || KS == 2, "one or two k-groups");
+  static_assert(KS == 1 || sizeof(St) >= (size_t)kWaves * 16 * 64 * 4, "room to combine k-groups");
+  __shared__ St stage_all[KS][2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int ks = wave_all / kWaves;      // k-group
+  const int wave = wave_all % kWaves;    // wave within the k-group
   const int wr = wave / WT, wt = wave % WT;
+  St* stage = stage_all[ks];
   int rt, tt;
   tile_of(xcd_swizzle(blockIdx.x, gridDim.x), gridDim.x / tok_tiles, tok_tiles, rt, tt);
   const int rb0 = rt * WR, tb0 = tt * WT;
-  const int nstages = nchunk / KC;
+  // k-group ks owns super-blocks [ks*nsb/KS, (ks+1)*nsb/KS); the last group has
+  // the most, so every wave runs its group's stages inside that many iterations.
+  constexpr int kStagesPerSb = 8 / KC;
+  const int gbeg = (ks * nsb / KS) * kStagesPerSb;
+  const int nstages = ((ks + 1) * nsb / KS) * kStagesPerSb - gbeg;
+  const int niter = (nsb - (KS - 1) * nsb / KS) * kStagesPerSb;
 
   // Copy jobs of one stage (one wave instruction, 1 KiB each): the weight
   // fragments, then the code fragments, split into equal contiguous runs per
@@ -108,24 +122,28 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   static_assert((KC * 2) % kRunA == 0 && KC % kRunB == 0, "a run stays inside one block");
   static_assert(St::kSmallJobs <= kWaves, "one small-region job per wave at most");
   const int ka0 = wave * kRunA, kb0 = wave * kRunB;
-  const int8_t* srcA = wq + (size_t)(rb0 + ka0 / (KC * 2)) * nchunk * 2048 + (ka0 % (KC * 2)) * 1024;
-  const uint8_t* srcB = qq + (size_t)(tb0 + kb0 / KC) * nchunk * 1024 + (kb0 % KC) * 1024;
+  const int8_t* srcA = wq + (size_t)(rb0 + ka0 / (KC * 2)) * nchunk * 2048 + (ka0 % (KC * 2)) * 1024 +
+                      (size_t)gbeg * KC * 2048;
+  const uint8_t* srcB = qq + (size_t)(tb0 + kb0 / KC) * nchunk * 1024 + (kb0 % KC) * 1024 +
+                        (size_t)gbeg * KC * 1024;
   const uint8_t* small_src = nullptr;
   int small_kind = 0;  // 0 none, 1 pairs/mins (advance per stage), 2 d (advance per super-block)
   if (wave < St::kSmallJobs) {
     const int u = wave * 64 + lane;
     if (u < St::kUnitsS) {
-      small_src = qs + ((size_t)(tb0 + u / (KC * 8)) * nchunk) * 128 + (u % (KC * 8)) * 16;
+      small_src = qs + ((size_t)(tb0 + u / (KC * 8)) * nchunk + gbeg * KC) * 128 + (u % (KC * 8)) * 16;
       small_kind = 1;
     } else if (u < St::kUnitsS + St::kUnitsM) {
       if (TYPE == QMM_Q4_K) {
         const int v = u - St::kUnitsS;
-        small_src = (const uint8_t*)wm + ((size_t)(rb0 + v / (KC * 8)) * nchunk) * 128 + (v % (KC * 8)) * 16;
+        small_src = (const uint8_t*)wm + ((size_t)(rb0 + v / (KC * 8)) * nchunk + gbeg * KC) * 128 +
+                    (v % (KC * 8)) * 16;
         small_kind = 1;
       }
     } else if (u < St::kUnitsS + St::kUnitsM + St::kUnitsD) {
       const int v = u - St::kUnitsS - St::kUnitsM;
-      small_src = (const uint8_t*)wd + ((size_t)(rb0 + v / 8) * nsb) * 128 + (v % 8) * 16;
+      small_src = (const uint8_t*)wd + ((size_t)(rb0 + v / 8) * nsb + gbeg / kStagesPerSb) * 128 +
+                  (v % 8) * 16;
       small_kind = 2;
     }
   }
@@ -163,96 +181,119 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
   const v16i zero = {};
 
-  issue_stage(0, stage[0]);
+  if (nstages > 0) issue_stage(0, stage[0]);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int g = 0; g < nstages; ++g) {
-    St& st = stage[g & 1];
-    const bool starts_sb = (g * KC) % 8 == 0;
-    // Software pipeline over the KC chunks: step cc reads the LDS operands of
-    // chunk cc+2, issues the two MFMAs of chunk cc+1, then runs the scale
-    // epilogue of chunk cc on the vector ALU while the matrix core works.
-    v4i ahi0 = *(const v4i*)(st.a[wr][0][0] + lane * 16);
-    v4i alo0 = *(const v4i*)(st.a[wr][0][1] + lane * 16);
-    v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
-    v4i ahi1 = *(const v4i*)(st.a[wr][1][0] + lane * 16);
-    v4i alo1 = *(const v4i*)(st.a[wr][1][1] + lane * 16);
-    v4i bq1 = *(const v4i*)(st.b[wt][1] + lane * 16);
-    v16i jh = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi0, bq0, zero, 0, 0, 0);
-    v16i jl = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo0, bq0, zero, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int cc = 0; cc < KC; ++cc) {
-      // stage (g+1)&1 was last read in iteration g-1, which every wave finished
-      // before the barrier that ended it
-      if (g + 1 < nstages) {
-        constexpr int per = (kWaveJobs + KC - 1) / KC;
-#pragma unroll
-        for (int q = 0; q < per; ++q)
-          if (cc * per + q < kWaveJobs) issue_job(g + 1, stage[(g + 1) & 1], cc * per + q);
-      }
-      const float dh = f16_bits_to_float(st.s[wt][cc][lane & 31] & 0xFFFF);
-      v4i ahi2, alo2, bq2;
-      if (cc + 2 < KC) {
-        ahi2 = *(const v4i*)(st.a[wr][cc + 2][0] + lane * 16);
-        alo2 = *(const v4i*)(st.a[wr][cc + 2][1] + lane * 16);
-        bq2 = *(const v4i*)(st.b[wt][cc + 2] + lane * 16);
-      }
-      v16i jh_next, jl_next;
-      if (cc + 1 < KC) {
-        jh_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi1, bq1, zero, 0, 0, 0);
-        jl_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo1, bq1, zero, 0, 0, 0);
-        pin(jh_next);
-        pin(jl_next);
-      }
-      if (TYPE == QMM_Q4_K && (cc & 1)) {
-        const int ck = cc - 1 + (lane >> 5);
-        const float mv = st.m[wr][ck][lane & 31];
-        const float sv = f16_bits_to_float(st.s[wt][ck][lane & 31] >> 16);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(mv, sv, acc, 0, 0, 0);
-      }
-      if (cc == 0 && starts_sb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) inner[i] = (float)((jh[i] << 6) + jl[i]) * dh;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)((jh[i] << 6) + jl[i]), dh, inner[i]);
-      }
-      pin(inner);
-      if (cc + 1 < KC) {
-        jh = jh_next;
-        jl = jl_next;
-        ahi1 = ahi2;
-        alo1 = alo2;
-        bq1 = bq2;
-      }
-      // order inside the step: stage copies, LDS reads, MFMAs, the vector epilogue
-      __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);   // VMEM (stage copies)
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);  // VALU
+  for (int g = 0; g < niter; ++g) {
+    if (g < nstages) {  // uniform per k-group
+      St& st = stage[g & 1];
+      const bool starts_sb = (g * KC) % 8 == 0;
+      // Software pipeline over the KC chunks: step cc issues the two MFMAs of
+      // chunk cc+1 (operands read one step earlier), then the LDS reads of chunk
+      // cc+2 and of chunk cc+1's activation scale, then the scale epilogue of
+      // chunk cc on the vector ALU while the matrix core works.  Every LDS value
+      // is consumed one step after its read, so a wait for it never waits for
+      // the reads just issued.
+      uint32_t dhr = st.s[wt][0][lane & 31];
+      v4i ahi0 = *(const v4i*)(st.a[wr][0][0] + lane * 16);
+      v4i alo0 = *(const v4i*)(st.a[wr][0][1] + lane * 16);
+      v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
+      v4i ahi1 = *(const v4i*)(st.a[wr][1][0] + lane * 16);
+      v4i alo1 = *(const v4i*)(st.a[wr][1][1] + lane * 16);
+      v4i bq1 = *(const v4i*)(st.b[wt][1] + lane * 16);
+      v16i jh = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi0, bq0, zero, 0, 0, 0);
+      v16i jl = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo0, bq0, zero, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if (((g + 1) * KC) % 8 == 0) {  // end of a super-block: apply its d
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 d4 = *(const float4*)(&st.d[wr][8 * q + 4 * (lane >> 5)]);
-        acc[4 * q + 0] = fmaf(inner[4 * q + 0], d4.x, acc[4 * q + 0]);
-        acc[4 * q + 1] = fmaf(inner[4 * q + 1], d4.y, acc[4 * q + 1]);
-        acc[4 * q + 2] = fmaf(inner[4 * q + 2], d4.z, acc[4 * q + 2]);
-        acc[4 * q + 3] = fmaf(inner[4 * q + 3], d4.w, acc[4 * q + 3]);
+      for (int cc = 0; cc < KC; ++cc) {
+        v16i jh_next, jl_next;
+        if (cc + 1 < KC) {
+          jh_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi1, bq1, zero, 0, 0, 0);
+          jl_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo1, bq1, zero, 0, 0, 0);
+          pin(jh_next);
+          pin(jl_next);
+        }
+        // stage (g+1)&1 was last read in iteration g-1, which every wave finished
+        // before the barrier that ended it
+        if (g + 1 < nstages) {
+          constexpr int per = (kWaveJobs + KC - 1) / KC;
+#pragma unroll
+          for (int q = 0; q < per; ++q)
+            if (cc * per + q < kWaveJobs) issue_job(g + 1, stage[(g + 1) & 1], cc * per + q);
+        }
+        v4i ahi2, alo2, bq2;
+        if (cc + 2 < KC) {
+          ahi2 = *(const v4i*)(st.a[wr][cc + 2][0] + lane * 16);
+          alo2 = *(const v4i*)(st.a[wr][cc + 2][1] + lane * 16);
+          bq2 = *(const v4i*)(st.b[wt][cc + 2] + lane * 16);
+        }
+        uint32_t dhr_next = 0;
+        if (cc + 1 < KC) dhr_next = st.s[wt][cc + 1][lane & 31];
+        if (TYPE == QMM_Q4_K && (cc & 1)) {
+          const int ck = cc - 1 + (lane >> 5);
+          const float mv = st.m[wr][ck][lane & 31];
+          const float sv = f16_bits_to_float(st.s[wt][ck][lane & 31] >> 16);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(mv, sv, acc, 0, 0, 0);
+        }
+        const float dh = f16_bits_to_float(dhr & 0xFFFF);
+        if (cc == 0 && starts_sb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) inner[i] = (float)((jh[i] << 6) + jl[i]) * dh;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)((jh[i] << 6) + jl[i]), dh, inner[i]);
+        }
+        pin(inner);
+        if (cc + 1 < KC) {
+          jh = jh_next;
+          jl = jl_next;
+          ahi1 = ahi2;
+          alo1 = alo2;
+          bq1 = bq2;
+          dhr = dhr_next;
+        }
+        // order inside the step: MFMAs, stage copies, LDS reads, the vector epilogue
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA (next chunk)
+        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);   // VMEM (stage copies)
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA (q4_K min term)
+        __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);  // VALU
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (((g + 1) * KC) % 8 == 0) {  // end of a super-block: apply its d
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 d4 = *(const float4*)(&st.d[wr][8 * q + 4 * (lane >> 5)]);
+          acc[4 * q + 0] = fmaf(inner[4 * q + 0], d4.x, acc[4 * q + 0]);
+          acc[4 * q + 1] = fmaf(inner[4 * q + 1], d4.y, acc[4 * q + 1]);
+          acc[4 * q + 2] = fmaf(inner[4 * q + 2], d4.z, acc[4 * q + 2]);
+          acc[4 * q + 3] = fmaf(inner[4 * q + 3], d4.w, acc[4 * q + 3]);
+        }
       }
     }
-    if (g + 1 < nstages) {
+    if (g + 1 < niter) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads for g+1 landed
       __syncthreads();                                   // everyone's landed; stage g is free
     }
   }
 #undef QMM_LDS
+  if (KS > 1) {  // add k-group 1's partial sums to k-group 0's, in that order
+    __syncthreads();  // every wave is done with the stage buffers
+    float* red = (float*)&stage_all[0][0] + wave * 1024 + lane;
+    if (ks == 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[i * 64] = acc[i];
+    }
+    __syncthreads();
+    if (ks == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += red[i * 64];
+    }
+  }
 
   const int tok = (tb0 + wt) * 32 + (lane & 31);
-  if (tok < n_tok) {
+  if (ks == 0 && tok < n_tok) {
     float* orow = out + (size_t)tok * od;
     const int jb = (rb0 + wr) * 32 + 4 * (lane >> 5);
 #pragma unroll
@@ -269,7 +310,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   }
 }
 
-template <int TYPE, int WR, int WT, int KC>
+template <int TYPE, int WR, int WT, int KC, int KS>
 static hipError_t launch_tiled(const Planes& p, const uint8_t* qact, int64_t n_tok, int64_t t_pad,
                                float* out, hipStream_t s) {
   static_assert(kRowPad % (32 * WR) == 0 && kTokenPad % (32 * WT) == 0,
@@ -278,31 +319,32 @@ static hipError_t launch_tiled(const Planes& p, const uint8_t* qact, int64_t n_t
   const int tok_tiles = (int)((n_tok + 32 * WT - 1) / (32 * WT));
   const uint8_t* qs = qact + (size_t)t_pad * (size_t)p.id;
   const int vec_store = (p.od % 4 == 0) && ((uintptr_t)out % 16 == 0);
-  mmq_kernel<TYPE, WR, WT, KC><<<dim3((unsigned)(row_tiles * tok_tiles)), dim3(64 * WR * WT), 0, s>>>(
+  const dim3 grid((unsigned)(row_tiles * tok_tiles)), block(64 * WR * WT * KS);
+  mmq_kernel<TYPE, WR, WT, KC, KS><<<grid, block, 0, s>>>(
       p.wq, p.wd, p.wm, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, tok_tiles,
       vec_store, out);
   return hipGetLastError();
 }
 
 // Tile geometry per launch.  Two shapes of the same kernel:
-//  * 2 x 4 waves (64 rows x 128 tokens), a whole super-block per stage: one
-//    work-group of 8 waves per CU (about 140 KiB of LDS), one barrier per 8
-//    chunks; best when there are too few tiles to fill the CUs several times
-//    (e.g. 512 tokens x 4096 rows = 256 work-groups);
-//  * 2 x 2 waves (64 x 64), half a super-block per stage: about 52 KiB of LDS,
-//    three work-groups per CU, so one group's barrier wait is covered by the
-//    others; best when there are many tiles.
-// The switch point (about four 64 x 64 tiles per CU) was chosen by timing
-// both on the 512-token shapes and the 2048-token output head.
+//  * 2 x 2 waves (64 x 64 tile), one k-group, half-super-block stages: about
+//    52 KiB of LDS, three work-groups (12 waves) per CU, so one group's barrier
+//    wait is covered by the others; for shapes with many tiles;
+//  * 2 x 4 waves (64 rows x 128 tokens) in two k-groups (16 waves), half-super-
+//    block stages, about 140 KiB of LDS, one work-group per CU; for shapes with
+//    too few tiles to fill the CUs several times (e.g. 512 tokens x 4096 rows =
+//    256 work-groups), where the second k-group doubles the waves per CU.
+// The switch point (about four 64 x 64 tiles per CU) was chosen by timing both
+// on the 512-token shapes, the 3314-token layer shapes and the 2048-token head.
 hipError_t launch_mmq(const Planes& p, const uint8_t* qact, int64_t n_tok, int64_t t_pad,
                       float* out, hipStream_t s) {
   const int64_t small_tiles = (p.od_pad / 64) * ((n_tok + 63) / 64);
   const bool many = small_tiles >= 4 * 256;
   if (p.type == QMM_Q6_K)
-    return many ? launch_tiled<QMM_Q6_K, 2, 2, 4>(p, qact, n_tok, t_pad, out, s)
-                : launch_tiled<QMM_Q6_K, 2, 4, 8>(p, qact, n_tok, t_pad, out, s);
-  return many ? launch_tiled<QMM_Q4_K, 2, 2, 4>(p, qact, n_tok, t_pad, out, s)
-              : launch_tiled<QMM_Q4_K, 2, 4, 8>(p, qact, n_tok, t_pad, out, s);
+    return many ? launch_tiled<QMM_Q6_K, 2, 2, 4, 1>(p, qact, n_tok, t_pad, out, s)
+                : launch_tiled<QMM_Q6_K, 2, 4, 4, 2>(p, qact, n_tok, t_pad, out, s);
+  return many ? launch_tiled<QMM_Q4_K, 2, 2, 4, 1>(p, qact, n_tok, t_pad, out, s)
+              : launch_tiled<QMM_Q4_K, 2, 4, 4, 2>(p, qact, n_tok, t_pad, out, s);
 }
 
 }  // namespace qmm
