@@ -9,10 +9,15 @@ into planes) happens before the timed region, as a deployment does it at model
 load; its device memory is reported.
 
 Prints one JSON line: effective int8 TOPS of the whole step (2*T*od*id summed
-over the GEMMs, per step time), the roofline of the dominant kernel (the MMQ)
-from HIP events on the stream it runs on (recorded in a second pass of K steps,
-so the timed steps carry nothing but the kernels), and the CPU oracle timed on
-the host as a reference.
+over the GEMMs, per step time); the spread of the step time and the roofline of
+the dominant kernel (the MMQ) from HIP events on the stream the kernels run on,
+at each step's start, between its prepass and its MMQs, and at its end, in a
+second pass of K steps (so the timed steps carry nothing but the kernels); each
+kernel's time alone (K back-to-back launches between two events, a third pass);
+the MMQs with the weights cold (a fourth pass rotating over
+copies of the weights whose planes together exceed the 256 MB last-level
+cache), and the CPU oracle timed on the host as a reference (all host threads,
+and one thread).
 """
 from __future__ import annotations
 
@@ -33,6 +38,7 @@ import synth  # noqa: E402
 
 MFMA_INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
 HBM_PEAK_GBS = 8000.0
+COLD_BYTES = 512 << 20         # weight planes cycled per cold pass: twice the 256 MB cache
 
 # workload name -> (description, tokens, inputs {name: id}, gemms [(name, type, od, id, input)],
 #                   outliers)
@@ -86,6 +92,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ffn_down", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-weights pass")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--cpu-macs", type=float, default=2.4e10,
                     help="multiply-accumulates of the oracle sample (about 20 s of CPU work)")
@@ -132,20 +139,40 @@ def cpu_baseline(gemms, raws, xs, T, threads, macs_target):
         type_, raw, od, id_, (q, dh, s), a, b = j
         oracle.mmq_rows(type_, raw, od, id_, q, dh, s, a, b)
 
+    reps = 0
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(work, jobs))
+        while True:  # the whole sample, again until about 10 s have passed
+            list(ex.map(work, jobs))
+            reps += 1
+            if time.perf_counter() - t1 >= 10.0 or reps >= 100:
+                break
     t2 = time.perf_counter()
+    macs *= reps
     return {
         "value": round(2.0 * macs / (t2 - t0) / 1e12, 6),
         "unit": "effective int8 TOPS",
         "cores": threads,
         "kind": "oracle",
         "sample": (f"all {T} tokens x the first {frac * 100:.1f}% of the rows of each GEMM "
-                   f"({macs / 1e9:.1f} G multiply-accumulates): q8 quantize of every input on 1 "
-                   f"thread ({t1 - t0:.2f} s) + the f64 oracle MMQ over {threads} threads "
-                   f"({t2 - t1:.2f} s wall)"),
+                   f"({macs / reps / 1e9:.1f} G multiply-accumulates), run {reps} time(s): q8 quantize "
+                   f"of every input on 1 thread ({t1 - t0:.2f} s, once) + the f64 oracle MMQ over "
+                   f"{threads} threads ({t2 - t1:.2f} s wall)"),
         "seconds": round(t2 - t0, 3),
     }
+
+
+def cpu_single_thread(gemms, raws, xs, T, macs_target):
+    """The oracle MMQ on one thread over a sample of macs_target multiply-accumulates
+    (rows of the first GEMM, activations quantized outside the timing)."""
+    import oracle
+    gname, type_, od, id_, inp = gemms[0]
+    q, dh, s = oracle.quantize(xs[inp])
+    rows = max(1, min(od, int(round(macs_target / (T * id_)))))
+    t0 = time.perf_counter()
+    oracle.mmq_rows(type_, raws[gname], od, id_, q, dh, s, 0, rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * T * rows * id_ / dt / 1e12, 6), "unit": "effective int8 TOPS",
+            "cores": 1, "sample": f"{gname}: all {T} tokens x the first {rows} rows", "seconds": round(dt, 3)}
 
 
 def main():
@@ -173,19 +200,18 @@ def main():
     stream = torch.cuda.current_stream()
     n_in, n_g = len(inputs), len(gemms)
 
-    def step(ev=None):
-        for i, name in enumerate(inputs):
-            if ev is not None:
-                ev[i][0].record(stream)
-            qmm.quantize_activations(xd[name], qacts[name], stream)
-            if ev is not None:
-                ev[i][1].record(stream)
-        for k, (gname, _, _, _, inp) in enumerate(gemms):
-            if ev is not None:
-                ev[n_in + k][0].record(stream)
-            qmm.mmq(weights[gname], qacts[inp], T, outs[gname], stream)
-            if ev is not None:
-                ev[n_in + k][1].record(stream)
+    def prepass(name):
+        qmm.quantize_activations(xd[name], qacts[name], stream)
+
+    def gemm(g, w=None):
+        gname, _, _, _, inp = g
+        qmm.mmq(w or weights[gname], qacts[inp], T, outs[gname], stream)
+
+    def step():
+        for name in inputs:
+            prepass(name)
+        for g in gemms:
+            gemm(g)
 
     for _ in range(args.warmup):
         step()
@@ -201,26 +227,80 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # kernel durations: K more steps with HIP events around every kernel, on the
-    # stream the kernels run on
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_in + n_g)]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
+    def event_pair():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(2)]
 
-    per = np.array([[e[0].elapsed_time(e[1]) for e in evk] for evk in evs])  # [steps][kernels] ms
-    pre_ms = per[:, :n_in].sum(axis=1)
-    mmq_ms = per[:, n_in:].sum(axis=1)
+    # step spread and the MMQs' time inside the step: K more steps with HIP events
+    # (on the stream the kernels run on) at each step's start, between its
+    # prepass and its MMQs, and at its end
+    evs = [event_pair() + [torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        evs[k][0].record(stream)
+        for name in inputs:
+            prepass(name)
+        evs[k][2].record(stream)
+        for g in gemms:
+            gemm(g)
+        evs[k][1].record(stream)
+    torch.cuda.synchronize()
+    span = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    mmq_in_step = np.array([e[2].elapsed_time(e[1]) for e in evs])
+
+    # per-kernel durations: every kernel of the step launched K times back to
+    # back between two events (an event pair around each single launch would add
+    # the event's own cost to every launch)
+    kev = [event_pair() for _ in range(n_in + n_g)]
+    for i, name in enumerate(inputs):
+        kev[i][0].record(stream)
+        for _ in range(args.steps):
+            prepass(name)
+        kev[i][1].record(stream)
+    for k, g in enumerate(gemms):
+        kev[n_in + k][0].record(stream)
+        for _ in range(args.steps):
+            gemm(g)
+        kev[n_in + k][1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([e[0].elapsed_time(e[1]) / args.steps for e in kev])  # [kernel] ms per launch
+
+    # cold weights: copies of every weight, enough that the planes cycled through
+    # exceed the last-level cache, one copy per step in turn
+    plane_total = sum(w.plane_bytes for w in weights.values())
+    n_copies = int(min(8, max(1, -(-COLD_BYTES // plane_total))))
+    cold = None
+    if n_copies > 1 and not args.no_cold:
+        copies = [weights] + [{g: qmm.register_weights(t, od, id_, raws[g]) for g, t, od, id_, _ in gemms}
+                              for _ in range(n_copies - 1)]
+        for k in range(n_copies):  # one untimed round over the copies
+            for g in gemms:
+                gemm(g, copies[k][g[0]])
+        torch.cuda.synchronize()
+        cev = event_pair()
+        cev[0].record(stream)
+        for k in range(args.steps):
+            for g in gemms:
+                gemm(g, copies[k % n_copies][g[0]])
+        cev[1].record(stream)
+        torch.cuda.synchronize()
+        cold_ms = cev[0].elapsed_time(cev[1]) / args.steps
+        for c in copies[1:]:
+            for w in c.values():
+                w.release()
+        cold = {"copies": n_copies, "planes_cycled_bytes": n_copies * plane_total,
+                "mmq_avg_ms": round(float(cold_ms), 4)}
+    pre_ms = float(per[:n_in].sum())
+    mmq_b2b_ms = float(per[n_in:].sum())
+    mmq_ms = float(mmq_in_step.mean())
     ms_per_step = wall * 1e3 / args.steps
     ops = sum(2.0 * T * od * id_ for _, _, od, id_, _ in gemms)
-    mmq_avg_s = float(mmq_ms.mean()) / 1e3
+    mmq_avg_s = mmq_ms / 1e3
     mmq_tops = ops / mmq_avg_s / 1e12
     pre_bytes = sum(T * id_ * 4 + qmm.qact_bytes(T, id_) for id_ in inputs.values())
     alg_bytes = sum(weights[g].plane_bytes + T * id_ * 9 // 8 + T * od * 4
                     for g, _, od, id_, _ in gemms)
     traffic = measured_traffic(args.workload)
+    if cold is not None:
+        cold["effective_tops"] = round(ops / (cold["mmq_avg_ms"] / 1e3) / 1e12, 2)
 
     result = {
         "metric": "effective int8 TOPS (q6_K/q4_K x q8 MMQ, prepass + GEMM per step)",
@@ -242,15 +322,21 @@ def main():
         "pct_int8_mfma_peak": round(100.0 * ops / (ms_per_step / 1e3) / 1e12 / MFMA_INT8_PEAK_TOPS, 2),
         "token_rows_per_s": round(sum(T * g[2] for g in gemms) / (ms_per_step / 1e3), 1),
         "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
-        "mmq": {"avg_ms": round(float(mmq_ms.mean()), 4), "median_ms": round(float(np.median(mmq_ms)), 4),
-                "min_ms": round(float(mmq_ms.min()), 4), "max_ms": round(float(mmq_ms.max()), 4),
+        "step_ms_events": {"median": round(float(np.median(span)), 4), "min": round(float(span.min()), 4),
+                           "max": round(float(span.max()), 4)},
+        "mmq": {"avg_ms": round(mmq_ms, 4), "median_ms": round(float(np.median(mmq_in_step)), 4),
+                "min_ms": round(float(mmq_in_step.min()), 4), "max_ms": round(float(mmq_in_step.max()), 4),
                 "effective_tops": round(mmq_tops, 2),
-                "per_gemm_ms": {g[0]: round(float(per[:, n_in + k].mean()), 4) for k, g in enumerate(gemms)}},
-        "prepass": {"avg_ms": round(float(pre_ms.mean()), 4),
+                "back_to_back_ms": round(mmq_b2b_ms, 4),
+                "back_to_back_tops": round(ops / (mmq_b2b_ms / 1e3) / 1e12, 2),
+                "per_gemm_ms": {g[0]: round(float(per[n_in + k]), 4) for k, g in enumerate(gemms)},
+                "algorithmic_gb_per_s": round(alg_bytes / mmq_avg_s / 1e9, 1),
+                "cold_weights": cold},
+        "prepass": {"avg_ms": round(pre_ms, 4),
                     "bytes": pre_bytes,
-                    "gb_per_s": round(pre_bytes / (float(pre_ms.mean()) / 1e3) / 1e9, 1),
-                    "pct_hbm_peak": round(100 * pre_bytes / (float(pre_ms.mean()) / 1e3) / 1e9 / HBM_PEAK_GBS, 1),
-                    "per_input_ms": {name: round(float(per[:, i].mean()), 4) for i, name in enumerate(inputs)}},
+                    "gb_per_s": round(pre_bytes / (pre_ms / 1e3) / 1e9, 1),
+                    "pct_hbm_peak": round(100 * pre_bytes / (pre_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 1),
+                    "per_input_ms": {name: round(float(per[i]), 4) for i, name in enumerate(inputs)}},
         "roofline": {
             "kernel": "mmq_kernel",
             "bound": "mfma",
@@ -269,6 +355,8 @@ def main():
     if not args.no_cpu:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         result["cpu_baseline"] = cpu_baseline(gemms, raws, xs, T, threads, args.cpu_macs)
+        result["cpu_baseline"]["single_thread"] = cpu_single_thread(gemms, raws, xs, T,
+                                                                    args.cpu_macs / 4)
     for w in weights.values():
         w.release()
     print(json.dumps(result), flush=True)
