@@ -7,7 +7,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/qmm.h"
 #include "qmm_internal.h"
@@ -27,6 +29,18 @@ namespace {
 thread_local std::string g_last_error;
 std::atomic<size_t> g_held{0};  // device bytes held by live handles
 std::atomic<size_t> g_cap{0};   // 0 = no cap
+
+// Scratch for the MMQ's tail partials: one buffer per (device, stream), of the
+// largest size any call can need on that device (32 KiB per compute unit).
+// Calls on one stream run in order, so they share it; it lives until the
+// process ends.
+struct Scratch {
+  int device;
+  hipStream_t stream;
+  void* ptr;
+};
+std::mutex g_scratch_mu;
+std::vector<Scratch> g_scratch;
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -233,7 +247,28 @@ int qmm_mmq(const qmm_weights* w, const void* qact, size_t qact_bytes, int64_t n
   if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
   if (device != w->device)
     return fail(QMM_EINVAL, "handle belongs to device %d but device %d is current", w->device, device);
-  e = qmm::launch_mmq(w->p, (const uint8_t*)qact, n_tok, token_pad(n_tok), out, (hipStream_t)stream);
+  int num_cus = 0;
+  e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(multiprocessor count)");
+  const qmm::MmqPlan plan = qmm::plan_mmq(w->p, n_tok, num_cus);
+  const hipStream_t s = (hipStream_t)stream;
+  void* scratch = nullptr;
+  if (plan.scratch_bytes > 0) {
+    const size_t max_bytes = qmm::mmq_scratch_max_bytes(num_cus);
+    if (plan.scratch_bytes > max_bytes) return fail(QMM_EINVAL, "internal: tail scratch exceeds its bound");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    for (const Scratch& sc : g_scratch)
+      if (sc.device == device && sc.stream == s) scratch = sc.ptr;
+    if (scratch == nullptr) {
+      e = hipMalloc(&scratch, max_bytes);
+      if (e != hipSuccess)
+        return e == hipErrorOutOfMemory
+                   ? fail(QMM_ENOMEM, "hipMalloc(%zu) for the tail partials failed", max_bytes)
+                   : fail_hip(e, "hipMalloc(tail partials)");
+      g_scratch.push_back({device, s, scratch});
+    }
+  }
+  e = qmm::launch_mmq(w->p, plan, (const uint8_t*)qact, n_tok, token_pad(n_tok), out, (float*)scratch, s);
   if (e != hipSuccess) return fail_hip(e, "mmq launch");
   ok();
   return QMM_OK;

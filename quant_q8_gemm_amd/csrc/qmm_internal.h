@@ -33,7 +33,20 @@ size_t wm_bytes(int type, int64_t od_pad, int64_t id);
 hipError_t launch_repack(const uint8_t* raw, const Planes& p, hipStream_t s);
 hipError_t launch_quantize(const float* x, int64_t n_tok, int64_t t_pad, int64_t id,
                            uint8_t* qact, hipStream_t s);
-hipError_t launch_mmq(const Planes& p, const uint8_t* qact, int64_t n_tok, int64_t t_pad,
-                      float* out, hipStream_t s);
+// MMQ launch plan: tile geometry, and for a ragged last wave the K split of the
+// tail tiles and the scratch they need (n_tail tiles x split partials).
+struct MmqPlan {
+  bool many;          // many tiles: 64 x 64 tiles, else 64 x 128 tiles in two k-groups
+  int row_tiles, tok_tiles;
+  int dp_row_tiles;   // row tiles computed whole
+  int n_tail;         // tiles after them, each split along K
+  int split;          // K slices per tail tile (1: no tail)
+  size_t scratch_bytes;
+};
+MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus);
+// Upper bound of MmqPlan::scratch_bytes on a device with num_cus compute units.
+size_t mmq_scratch_max_bytes(int num_cus);
+hipError_t launch_mmq(const Planes& p, const MmqPlan& plan, const uint8_t* qact, int64_t n_tok,
+                      int64_t t_pad, float* out, float* scratch, hipStream_t s);
 
 }  // namespace qmm

@@ -20,6 +20,8 @@
 #include "qmm_internal.h"
 #include "qmm_common.h"
 
+#include <algorithm>
+
 #include "../../include/qmm.h"
 
 namespace qmm {
@@ -81,12 +83,48 @@ __device__ __forceinline__ void tile_of(int pos, int row_tiles, int tok_tiles, i
   tt = idx / rows_here;
 }
 
+// Output layout of a wave's 32 x 32 block: lane holds token (lane & 31) and,
+// in acc[4*q + i], row 4*(lane >> 5) + 8*q + i.  store_quad writes the four
+// rows of one q into out[t][od], masked at od and n_tok.
+__device__ __forceinline__ void store_quad(float* __restrict__ out, float4 v, int rblock, int tblock, int lane,
+                                           int q, int od, int n_tok, int vec_store) {
+  const int tok = tblock * 32 + (lane & 31);
+  if (tok >= n_tok) return;
+  float* orow = out + (size_t)tok * od;
+  const int j = rblock * 32 + 4 * (lane >> 5) + 8 * q;
+  if (vec_store && j + 3 < od) {
+    *(float4*)(orow + j) = v;
+  } else {
+    if (j < od) orow[j] = v.x;
+    if (j + 1 < od) orow[j + 1] = v.y;
+    if (j + 2 < od) orow[j + 2] = v.z;
+    if (j + 3 < od) orow[j + 3] = v.w;
+  }
+}
+
+__device__ __forceinline__ void store_block(float* __restrict__ out, const v16f& acc, int rblock, int tblock,
+                                            int lane, int od, int n_tok, int vec_store) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    store_quad(out, make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]), rblock, tblock,
+               lane, q, od, n_tok, vec_store);
+}
+
+// Ragged last wave ("tail").  When the tiles fill the CUs k times and a few
+// more, the first k waves' worth of row tiles run whole (data-parallel) and
+// each of the remaining tail tiles is split along K into S slices of
+// super-blocks, so the tail runs S times wider.  A slice writes its partial
+// tile, in the work-group's register order, to a scratch buffer; the fixup
+// kernel adds a tile's S partials in slice order and stores the tile.  The
+// tail is whole row tiles at the end, so the rows before it keep exactly the
+// summation order they have without a tail.
 template <int TYPE, int WR, int WT, int KC, int KS>
 __global__ void __launch_bounds__(64 * WR * WT * KS, (WR * WT * KS == 4) ? 3 : 1)
 mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
            const float* __restrict__ wm, const uint8_t* __restrict__ qq,
            const uint8_t* __restrict__ qs, int nchunk, int nsb, int od, int n_tok,
-           int tok_tiles, int vec_store, float* __restrict__ out) {
+           int tok_tiles, int dp_row_tiles, int split, int vec_store, float* __restrict__ out,
+           float* __restrict__ part) {
   using St = Stage<WR, WT, KC>;
   constexpr int kWaves = WR * WT;
   constexpr int kJobsA = WR * KC * 2, kJobsB = WT * KC;
@@ -102,15 +140,28 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   const int wave = wave_all % kWaves;    // wave within the k-group
   const int wr = wave / WT, wt = wave % WT;
   St* stage = stage_all[ks];
-  int rt, tt;
-  tile_of(xcd_swizzle(blockIdx.x, gridDim.x), gridDim.x / tok_tiles, tok_tiles, rt, tt);
+  // role: a whole tile of the data-parallel part, or one K slice of a tail tile
+  const int dp_tiles = dp_row_tiles * tok_tiles;
+  const int tail_idx = (int)blockIdx.x - dp_tiles;  // >= 0: index into the partials
+  int rt, tt, sb0 = 0, sb1 = nsb;
+  if (tail_idx < 0) {
+    tile_of(xcd_swizzle(blockIdx.x, dp_tiles), dp_row_tiles, tok_tiles, rt, tt);
+  } else {
+    const int u = tail_idx / split, sl = tail_idx % split;
+    rt = dp_row_tiles + u / tok_tiles;
+    tt = u % tok_tiles;
+    sb0 = sl * nsb / split;
+    sb1 = (sl + 1) * nsb / split;
+  }
   const int rb0 = rt * WR, tb0 = tt * WT;
-  // k-group ks owns super-blocks [ks*nsb/KS, (ks+1)*nsb/KS); the last group has
-  // the most, so every wave runs its group's stages inside that many iterations.
+  // k-group ks owns super-blocks [sb0 + ks*n/KS, sb0 + (ks+1)*n/KS) of the n in
+  // this work-group's range; the last group has the most, so every wave runs its
+  // group's stages inside that many iterations.
   constexpr int kStagesPerSb = 8 / KC;
-  const int gbeg = (ks * nsb / KS) * kStagesPerSb;
-  const int nstages = ((ks + 1) * nsb / KS) * kStagesPerSb - gbeg;
-  const int niter = (nsb - (KS - 1) * nsb / KS) * kStagesPerSb;
+  const int nsb_here = sb1 - sb0;
+  const int gbeg = (sb0 + ks * nsb_here / KS) * kStagesPerSb;
+  const int nstages = (sb0 + (ks + 1) * nsb_here / KS) * kStagesPerSb - gbeg;
+  const int niter = (nsb_here - (KS - 1) * nsb_here / KS) * kStagesPerSb;
 
   // Copy jobs of one stage (one wave instruction, 1 KiB each): the weight
   // fragments, then the code fragments, split into equal contiguous runs per
@@ -292,37 +343,54 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
     }
   }
 
-  const int tok = (tb0 + wt) * 32 + (lane & 31);
-  if (ks == 0 && tok < n_tok) {
-    float* orow = out + (size_t)tok * od;
-    const int jb = (rb0 + wr) * 32 + 4 * (lane >> 5);
+  if (ks != 0) return;
+  if (tail_idx < 0) {
+    store_block(out, acc, rb0 + wr, tb0 + wt, lane, od, n_tok, vec_store);
+  } else {
+    float* dst = part + ((size_t)tail_idx * kWaves + wave) * 1024 + lane;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = jb + 8 * q;
-      if (vec_store && j + 3 < od) {
-        *(float4*)(orow + j) = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (j + i < od) orow[j + i] = acc[4 * q + i];
-      }
-    }
+    for (int i = 0; i < 16; ++i) dst[i * 64] = acc[i];
   }
 }
 
+// Adds each tail tile's `split` partials in slice order and stores the tile.
+// One work-group per (tail tile, 32 x 32 block); thread (q, lane) sums the four
+// values acc[4*q .. 4*q+3] of that lane over the slices.
+template <int WR, int WT>
+__global__ void __launch_bounds__(256)
+mmq_fixup_kernel(const float* __restrict__ part, int split, int dp_row_tiles, int tok_tiles, int od,
+                 int n_tok, int vec_store, float* __restrict__ out) {
+  constexpr int kWaves = WR * WT;
+  const int u = blockIdx.x / kWaves, w = blockIdx.x % kWaves;
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const float* src = part + ((size_t)u * split * kWaves + w) * 1024 + (4 * q) * 64 + lane;
+  float4 v = make_float4(src[0], src[64], src[128], src[192]);
+  for (int sl = 1; sl < split; ++sl) {
+    src += (size_t)kWaves * 1024;
+    v.x += src[0];
+    v.y += src[64];
+    v.z += src[128];
+    v.w += src[192];
+  }
+  const int rt = dp_row_tiles + u / tok_tiles, tt = u % tok_tiles;
+  store_quad(out, v, rt * WR + w / WT, tt * WT + w % WT, lane, q, od, n_tok, vec_store);
+}
+
 template <int TYPE, int WR, int WT, int KC, int KS>
-static hipError_t launch_tiled(const Planes& p, const uint8_t* qact, int64_t n_tok, int64_t t_pad,
-                               float* out, hipStream_t s) {
+static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8_t* qact, int64_t n_tok,
+                               int64_t t_pad, float* out, float* scratch, hipStream_t s) {
   static_assert(kRowPad % (32 * WR) == 0 && kTokenPad % (32 * WT) == 0,
                 "tiles must divide the row and token padding");
-  const int row_tiles = (int)(p.od_pad / (32 * WR));
-  const int tok_tiles = (int)((n_tok + 32 * WT - 1) / (32 * WT));
   const uint8_t* qs = qact + (size_t)t_pad * (size_t)p.id;
   const int vec_store = (p.od % 4 == 0) && ((uintptr_t)out % 16 == 0);
-  const dim3 grid((unsigned)(row_tiles * tok_tiles)), block(64 * WR * WT * KS);
-  mmq_kernel<TYPE, WR, WT, KC, KS><<<grid, block, 0, s>>>(
-      p.wq, p.wd, p.wm, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, tok_tiles,
-      vec_store, out);
+  const int wgs = plan.dp_row_tiles * plan.tok_tiles + plan.n_tail * plan.split;
+  mmq_kernel<TYPE, WR, WT, KC, KS><<<dim3((unsigned)wgs), dim3(64 * WR * WT * KS), 0, s>>>(
+      p.wq, p.wd, p.wm, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
+      plan.dp_row_tiles, plan.split, vec_store, out, scratch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.n_tail == 0) return e;
+  mmq_fixup_kernel<WR, WT><<<dim3((unsigned)(plan.n_tail * WR * WT)), dim3(256), 0, s>>>(
+      scratch, plan.split, plan.dp_row_tiles, plan.tok_tiles, (int)p.od, (int)n_tok, vec_store, out);
   return hipGetLastError();
 }
 
@@ -333,18 +401,46 @@ static hipError_t launch_tiled(const Planes& p, const uint8_t* qact, int64_t n_t
 //  * 2 x 4 waves (64 rows x 128 tokens) in two k-groups (16 waves), half-super-
 //    block stages, about 140 KiB of LDS, one work-group per CU; for shapes with
 //    too few tiles to fill the CUs several times (e.g. 512 tokens x 4096 rows =
-//    256 work-groups), where the second k-group doubles the waves per CU.
+//    256 work-groups), where the second k-group doubles the waves per CU.  Here
+//    a ragged last wave (e.g. 4097 rows: 264 tiles on 256 CUs) is split along K.
 // The switch point (about four 64 x 64 tiles per CU) was chosen by timing both
 // on the 512-token shapes, the 3314-token layer shapes and the 2048-token head.
-hipError_t launch_mmq(const Planes& p, const uint8_t* qact, int64_t n_tok, int64_t t_pad,
-                      float* out, hipStream_t s) {
+MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
+  MmqPlan plan{};
   const int64_t small_tiles = (p.od_pad / 64) * ((n_tok + 63) / 64);
-  const bool many = small_tiles >= 4 * 256;
+  plan.many = small_tiles >= 4 * 256;
+  const int wt = plan.many ? 2 : 4;
+  plan.row_tiles = (int)(p.od_pad / 64);
+  plan.tok_tiles = (int)((n_tok + 32 * wt - 1) / (32 * wt));
+  plan.dp_row_tiles = plan.row_tiles;
+  plan.split = 1;
+  const int64_t tiles = (int64_t)plan.row_tiles * plan.tok_tiles;
+  if (!plan.many && num_cus > 0 && tiles > num_cus && tiles % num_cus != 0) {
+    // one work-group per CU: whole waves stay data-parallel (whole row tiles),
+    // the row tiles after them form the tail
+    const int dp_rows = (int)((tiles / num_cus) * num_cus / plan.tok_tiles);
+    const int n_tail = (plan.row_tiles - dp_rows) * plan.tok_tiles;
+    const int split = (int)std::min<int64_t>(num_cus / n_tail, p.nsb);
+    if (split >= 2) {
+      plan.dp_row_tiles = dp_rows;
+      plan.n_tail = n_tail;
+      plan.split = split;
+      plan.scratch_bytes = (size_t)n_tail * split * (64 * 128) * sizeof(float);
+    }
+  }
+  return plan;
+}
+
+// n_tail * split <= num_cus work-groups, each one 64 x 128 partial tile.
+size_t mmq_scratch_max_bytes(int num_cus) { return (size_t)num_cus * (64 * 128) * sizeof(float); }
+
+hipError_t launch_mmq(const Planes& p, const MmqPlan& plan, const uint8_t* qact, int64_t n_tok,
+                      int64_t t_pad, float* out, float* scratch, hipStream_t s) {
   if (p.type == QMM_Q6_K)
-    return many ? launch_tiled<QMM_Q6_K, 2, 2, 4, 1>(p, qact, n_tok, t_pad, out, s)
-                : launch_tiled<QMM_Q6_K, 2, 4, 4, 2>(p, qact, n_tok, t_pad, out, s);
-  return many ? launch_tiled<QMM_Q4_K, 2, 2, 4, 1>(p, qact, n_tok, t_pad, out, s)
-              : launch_tiled<QMM_Q4_K, 2, 4, 4, 2>(p, qact, n_tok, t_pad, out, s);
+    return plan.many ? launch_tiled<QMM_Q6_K, 2, 2, 4, 1>(p, plan, qact, n_tok, t_pad, out, scratch, s)
+                     : launch_tiled<QMM_Q6_K, 2, 4, 4, 2>(p, plan, qact, n_tok, t_pad, out, scratch, s);
+  return plan.many ? launch_tiled<QMM_Q4_K, 2, 2, 4, 1>(p, plan, qact, n_tok, t_pad, out, scratch, s)
+                   : launch_tiled<QMM_Q4_K, 2, 4, 4, 2>(p, plan, qact, n_tok, t_pad, out, scratch, s);
 }
 
 }  // namespace qmm

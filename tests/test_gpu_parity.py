@@ -251,6 +251,10 @@ SMALL = [("C1 q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          ("q6_K 70x256 T=33", synth.Q6_K, 70, 256, 33, True),
          ("q6_K 33x2304 T=130", synth.Q6_K, 33, 2304, 130, False),
          ("q4_K 520x1536 T=257", synth.Q4_K, 520, 1536, 257, False),
+         # a ragged last wave on 256 CUs (264 tiles of 64 x 128 each): the
+         # tail tiles are split along K and added by the fixup kernel
+         ("q4_K 4160x1024 T=512", synth.Q4_K, 4160, 1024, 512, False),
+         ("q6_K 4200x768 T=500", synth.Q6_K, 4200, 768, 500, True),
          # enough 64 x 64 tiles (>= 1024) to select the many-tile geometry
          ("q6_K 1000x512 T=4100", synth.Q6_K, 1000, 512, 4100, True),
          ("q4_K 1030x256 T=4000", synth.Q4_K, 1030, 256, 4000, False)]
