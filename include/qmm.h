@@ -77,6 +77,7 @@ typedef struct {
     size_t plane_bytes;  /* device memory the handle holds */
     size_t wd_offset;    /* byte offset of the d plane inside the planes */
     size_t wm_offset;    /* byte offset of the -dmin*min plane (q4_K; else == plane_bytes) */
+    size_t sc_offset;    /* byte offset of the scale-byte plane (q4_K; else == plane_bytes) */
 } qmm_info;
 
 /*
@@ -108,15 +109,20 @@ int qmm_weights_info(const qmm_weights *w, qmm_info *out);
  * host must hold exactly bytes = info.plane_bytes.  Synchronous.
  * Plane layout (R = od_pad/32 row blocks of 32 rows, nchunk = id/32, nsb =
  * id/256; rows od..od_pad-1 are zero everywhere):
- *   at 0          int8 [R][nchunk][2][2][32][16]: the scale-folded weight
- *                 w = 64*hi + lo (lo in [0, 63]) of (row j, k) is split into
- *                 hi (plane index p = 0) and lo (p = 1), byte at
+ *   at 0          q6_K: int8 [R][nchunk][2][2][32][16]: the scale-folded weight
+ *                 w = scale[k/16] * (code - 32) of (row j, k) as w = 64*hi + lo
+ *                 (lo in [0, 63]), hi (plane index p = 0) and lo (p = 1) at byte
  *                 ((j/32*nchunk + k/32)*2 + p)*1024 + ((k%32)/16)*512
- *                 + (j%32)*16 + k%16, with
- *                   q6_K  w = scale[k/16] * (code - 32)
- *                   q4_K  w = scale[(k/32) % 8] * code
+ *                 + (j%32)*16 + k%16
+ *                 q4_K: uint8 [R][nchunk][2][32][8]: the 4-bit codes, two per
+ *                 byte; with h = (k%32)/16 and b = k%8, code (j, k) is in byte
+ *                 (j/32*nchunk + k/32)*512 + h*256 + (j%32)*8 + b, the low
+ *                 nibble if k%16 < 8, else the high nibble
  *   at wd_offset  f32 [R][nsb][32]: d of (row, super-block)
  *   at wm_offset  f32 [R][nchunk][32]: -(dmin * min) of (row, chunk), q4_K only
+ *   at sc_offset  uint8 [R][nchunk][32]: the 6-bit scale of (row j, chunk c),
+ *                 q4_K only, at byte (j/32*nchunk + c)*32 + 16*((j/4)%2)
+ *                 + 4*((j%32)/8) + j%4
  * Errors: QMM_EINVAL (null pointers, bytes mismatch), QMM_EHIP.
  */
 int qmm_weights_export(const qmm_weights *w, void *host, size_t bytes);

@@ -21,6 +21,7 @@ struct qmm_weights {
   size_t plane_bytes;
   size_t wd_offset;
   size_t wm_offset;
+  size_t sc_offset;
   void* alloc;  // one device allocation holding every plane
 };
 
@@ -114,9 +115,10 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   p.od_pad = (int64_t)round_up((size_t)od, qmm::kRowPad);
   p.nsb = id / 256;
   p.nchunk = id / 32;
-  const size_t off_wd = round_up(qmm::wq_bytes(p.od_pad, id), 256);
+  const size_t off_wd = round_up(qmm::wq_bytes(type, p.od_pad, id), 256);
   const size_t off_wm = off_wd + round_up(qmm::wd_bytes(p.od_pad, id), 256);
-  const size_t plane_bytes = off_wm + round_up(qmm::wm_bytes(type, p.od_pad, id), 256);
+  const size_t off_sc = off_wm + round_up(qmm::wm_bytes(type, p.od_pad, id), 256);
+  const size_t plane_bytes = off_sc + round_up(qmm::wsc_bytes(type, p.od_pad, id), 256);
   const size_t cap = g_cap.load();
   if (cap != 0 && g_held.load() + plane_bytes > cap)
     return fail(QMM_ENOMEM, "registration needs %zu device bytes; cap %zu, held %zu", plane_bytes,
@@ -145,6 +147,7 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   p.wq = (int8_t*)alloc;
   p.wd = (float*)((char*)alloc + off_wd);
   p.wm = type == QMM_Q4_K ? (float*)((char*)alloc + off_wm) : nullptr;
+  p.wsc = type == QMM_Q4_K ? (uint8_t*)alloc + off_sc : nullptr;
   int rc = QMM_OK;
   if ((e = hipMemcpyAsync(raw, host_bytes, nbytes, hipMemcpyHostToDevice, s)) != hipSuccess)
     rc = fail_hip(e, "hipMemcpyAsync(weights)");
@@ -164,6 +167,7 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   w->plane_bytes = plane_bytes;
   w->wd_offset = off_wd;
   w->wm_offset = type == QMM_Q4_K ? off_wm : plane_bytes;
+  w->sc_offset = type == QMM_Q4_K ? off_sc : plane_bytes;
   w->alloc = alloc;
   g_held += plane_bytes;
   if (getenv("QMM_LOG") != nullptr)
@@ -185,6 +189,7 @@ int qmm_weights_info(const qmm_weights* w, qmm_info* out) {
   out->plane_bytes = w->plane_bytes;
   out->wd_offset = w->wd_offset;
   out->wm_offset = w->wm_offset;
+  out->sc_offset = w->sc_offset;
   ok();
   return QMM_OK;
 }

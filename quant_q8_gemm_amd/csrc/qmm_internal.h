@@ -16,18 +16,21 @@ struct Planes {
   int64_t od_pad;    // rows padded to kRowPad
   int64_t nsb;       // id / 256
   int64_t nchunk;    // id / 32
-  int8_t* wq;        // folded int8 hi/lo planes, MFMA fragment order
+  int8_t* wq;        // weight fragments in MFMA order: q6_K folded hi/lo, q4_K packed codes
   float* wd;         // d per (row, super-block)
   float* wm;         // -dmin*min per (row, chunk); q4_K only, else nullptr
+  uint8_t* wsc;      // 6-bit scale per (row, chunk) as bytes; q4_K only, else nullptr
 };
 
 constexpr int kRowPad = 128;     // weight rows are padded to a multiple of this
 constexpr int kTokenPad = 128;   // tokens are padded to a multiple of this
+constexpr int kQ4CodeFrag = 512; // q4_K code bytes per (32-row block, chunk): two codes per byte
 
 // Byte sizes of the planes for a shape (all offsets 256-byte aligned).
-size_t wq_bytes(int64_t od_pad, int64_t id);
+size_t wq_bytes(int type, int64_t od_pad, int64_t id);
 size_t wd_bytes(int64_t od_pad, int64_t id);
 size_t wm_bytes(int type, int64_t od_pad, int64_t id);
+size_t wsc_bytes(int type, int64_t od_pad, int64_t id);
 
 // Kernel launchers: return the hipGetLastError() after the launch.
 hipError_t launch_repack(const uint8_t* raw, const Planes& p, hipStream_t s);

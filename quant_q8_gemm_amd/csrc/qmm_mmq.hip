@@ -7,12 +7,16 @@
 // per 32-block on int8 matrix cores and applies the per-block scales in f32.
 //
 // MI355X design (differs from the pages' GB10 kernels on purpose):
-//  * the d*scale pair plane of r56 section 2.2 becomes an integer fold: the
-//    small integer scale of every 16/32-weight group is multiplied into the
-//    weight codes at registration (exact), split into two int8 planes
-//    (hi = w >> 6, lo = w & 63) so one K=32 int8 MFMA per plane yields the
-//    scale-folded block dot J = 64*J_hi + J_lo exactly; only the f16 d of the
-//    256-weight super-block stays a float, applied once per super-block;
+//  * the d*scale pair plane of r56 section 2.2 becomes integer arithmetic: the
+//    block dot J of a 32-block already carries the small integer group scales,
+//    exactly, and only the f16 d of the 256-weight super-block stays a float,
+//    applied once per super-block.  q6_K (two 16-groups per 32-block, int8
+//    scales): the scale is multiplied into the codes at registration and the
+//    folded weight split into two int8 planes (hi = w >> 6, lo = w & 63), so one
+//    K=32 int8 MFMA per plane gives J = 64*J_hi + J_lo.  q4_K (one 6-bit scale
+//    per 32-block): the 4-bit codes stay codes (packed two per byte), one K=32
+//    MFMA gives the code dot D, and J = sc*D is one 24-bit integer multiply
+//    whose scale byte the instruction selects itself (SDWA);
 //  * planes are stored in MFMA fragment order, so every lane's operand is one
 //    contiguous 16-byte load and a wave's load is one contiguous 1 KiB;
 //  * the q4_K min term sum_c dmin*min_c*s_c is a true small matrix product over
@@ -48,17 +52,70 @@ namespace qmm {
 // lane's 16 outputs share one token: the activation scale dh is one register
 // per chunk, and the super-block d is applied once per 8 chunks.
 // ---------------------------------------------------------------------------
-template <int WR, int WT, int KC>
+// Weight fragment bytes per (32-row block, chunk): q6_K hi and lo planes of
+// 1 KiB each; q4_K packed codes (8 bytes per lane).
+template <int TYPE>
+constexpr int kFragA = TYPE == QMM_Q6_K ? 2048 : kQ4CodeFrag;
+
+template <int TYPE, int WR, int WT, int KC>
 struct alignas(16) Stage {
-  int8_t a[WR][KC][2][1024];  // weight planes: [row block][chunk][hi, lo][fragment]
-  int8_t b[WT][KC][1024];     // q8 codes: [token block][chunk][fragment]
-  uint32_t s[WT][KC][32];     // (dh, s) pairs: [token block][chunk][token]
-  float m[WR][KC][32];        // -dmin*min: [row block][chunk][row]; q4_K only
-  float d[WR][32];            // super-block d: [row block][row]
-  // s, m and d are contiguous: the "small" region, copied in 16-byte units.
-  static constexpr int kUnitsS = WT * KC * 8, kUnitsM = WR * KC * 8, kUnitsD = WR * 8;
-  static constexpr int kSmallJobs = (kUnitsS + kUnitsM + kUnitsD + 63) / 64;
-  static constexpr int kJobs = WR * KC * 2 + WT * KC + kSmallJobs;  // wave instructions
+  int8_t a[WR][KC][kFragA<TYPE>];  // weight fragments: [row block][chunk]
+  int8_t b[WT][KC][1024];          // q8 codes: [token block][chunk][fragment]
+  uint32_t s[WT][KC][32];          // (dh, s) pairs: [token block][chunk][token]
+  float m[WR][KC][32];             // -dmin*min: [row block][chunk][row]; q4_K only
+  uint8_t sc[WR][KC][32];          // scale bytes: [row block][chunk][lane half][16]; q4_K only
+  float d[WR][32];                 // super-block d: [row block][row]
+  // s, m, sc and d are contiguous: the "small" region, copied in 16-byte units.
+  static constexpr int kUnitsS = WT * KC * 8, kUnitsM = WR * KC * 8, kUnitsSc = WR * KC * 2,
+                       kUnitsD = WR * 8;
+  static constexpr int kSmallJobs = (kUnitsS + kUnitsM + kUnitsSc + kUnitsD + 63) / 64;
+};
+
+// The weight side of one chunk: the MFMA operand(s) read from a stage, the
+// MFMA(s) against the activation fragment, and the scale-carrying block dot J
+// of output element i.
+template <int TYPE>
+struct WeightOps;
+
+template <>
+struct WeightOps<QMM_Q6_K> {
+  struct A { v4i hi, lo; };
+  struct D { v16i hi, lo; };
+  static constexpr int kMfma = 2;
+  __device__ static A load(const int8_t* frag, int lane) {
+    return {*(const v4i*)(frag + lane * 16), *(const v4i*)(frag + 1024 + lane * 16)};
+  }
+  __device__ static D mma(const A& a, v4i bq) {
+    const v16i zero = {};
+    return {__builtin_amdgcn_mfma_i32_32x32x32_i8(a.hi, bq, zero, 0, 0, 0),
+            __builtin_amdgcn_mfma_i32_32x32x32_i8(a.lo, bq, zero, 0, 0, 0)};
+  }
+  __device__ static void keep(D& d) { pin(d.hi); pin(d.lo); }
+  __device__ static int dot(const D& d, v4i, int i) { return (d.hi[i] << 6) + d.lo[i]; }
+};
+
+template <>
+struct WeightOps<QMM_Q4_K> {
+  struct A { v4i c; };
+  struct D { v16i c; };
+  static constexpr int kMfma = 1;
+  __device__ static A load(const int8_t* frag, int lane) {
+    // 8 bytes per lane: byte b holds code k0+b (low nibble) and k0+8+b (high)
+    const v2i p = *(const v2i*)(frag + lane * 8);
+    const int m = 0x0F0F0F0F;
+    return {{p[0] & m, p[1] & m, (p[0] >> 4) & m, (p[1] >> 4) & m}};
+  }
+  __device__ static D mma(const A& a, v4i bq) {
+    const v16i zero = {};
+    return {__builtin_amdgcn_mfma_i32_32x32x32_i8(a.c, bq, zero, 0, 0, 0)};
+  }
+  __device__ static void keep(D& d) { pin(d.c); }
+  // |D| <= 32*15*127 fits 24 bits; the scale is byte i of the lane's 16 bytes
+  __device__ static int dot(const D& d, v4i sc, int i) {
+    const int dc = (d.c[i] << 8) >> 8;
+    const int s = (int)(((uint32_t)sc[i >> 2] >> (8 * (i & 3))) & 0xFF);
+    return dc * s;
+  }
 };
 
 // Work-group index -> (row tile, token tile).  Work-groups are dispatched
@@ -121,16 +178,18 @@ __device__ __forceinline__ void store_block(float* __restrict__ out, const v16f&
 template <int TYPE, int WR, int WT, int KC, int KS>
 __global__ void __launch_bounds__(64 * WR * WT * KS, (WR * WT * KS == 4) ? 3 : 1)
 mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
-           const float* __restrict__ wm, const uint8_t* __restrict__ qq,
+           const float* __restrict__ wm, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ qq,
            const uint8_t* __restrict__ qs, int nchunk, int nsb, int od, int n_tok,
            int tok_tiles, int dp_row_tiles, int split, int vec_store, float* __restrict__ out,
            float* __restrict__ part) {
-  using St = Stage<WR, WT, KC>;
+  using St = Stage<TYPE, WR, WT, KC>;
+  using W = WeightOps<TYPE>;
   constexpr int kWaves = WR * WT;
-  constexpr int kJobsA = WR * KC * 2, kJobsB = WT * KC;
+  constexpr int kJobsA = WR * KC * kFragA<TYPE> / 1024, kJobsB = WT * KC;
   static_assert(KC == 4 || KC == 8, "a stage is half or a whole super-block");
   static_assert(KS == 1 || KS == 2, "one or two k-groups");
-  static_assert(KS == 1 || sizeof(St) >= (size_t)kWaves * 16 * 64 * 4, "room to combine k-groups");
+  // k-group 1's sums pass to k-group 0 through k-group 0's two stages
+  static_assert(KS == 1 || 2 * sizeof(St) >= (size_t)kWaves * 16 * 64 * 4, "room to combine k-groups");
   __shared__ St stage_all[KS][2];
 
   const int tid = threadIdx.x;
@@ -166,19 +225,24 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   // Copy jobs of one stage (one wave instruction, 1 KiB each): the weight
   // fragments, then the code fragments, split into equal contiguous runs per
   // wave (a run stays inside one row / token block, so its source is one
-  // uniform base plus immediate 1 KiB steps); then the small region (scale
-  // pairs, mins, d) in 16-byte units per lane, one job each for the first waves.
-  static_assert(kJobsA % kWaves == 0 && kJobsB % kWaves == 0, "equal copy runs per wave");
-  constexpr int kRunA = kJobsA / kWaves, kRunB = kJobsB / kWaves;
-  static_assert((KC * 2) % kRunA == 0 && KC % kRunB == 0, "a run stays inside one block");
+  // uniform base plus immediate 1 KiB steps; with fewer weight jobs than waves,
+  // the first waves take one each); then the small region (scale pairs, mins,
+  // scale bytes, d) in 16-byte units per lane, one job each for the first waves.
+  constexpr int kFrag = kFragA<TYPE>;
+  constexpr int kPerRbA = KC * kFrag / 1024;  // weight jobs per row block and stage
+  static_assert(kJobsA % kWaves == 0 || kJobsA < kWaves, "equal weight runs per wave");
+  static_assert(kJobsB % kWaves == 0, "equal code runs per wave");
+  constexpr int kRunA = kJobsA >= kWaves ? kJobsA / kWaves : 1, kRunB = kJobsB / kWaves;
+  static_assert(kPerRbA % kRunA == 0 && KC % kRunB == 0, "a run stays inside one block");
   static_assert(St::kSmallJobs <= kWaves, "one small-region job per wave at most");
+  const bool has_a = kJobsA >= kWaves || wave < kJobsA;
   const int ka0 = wave * kRunA, kb0 = wave * kRunB;
-  const int8_t* srcA = wq + (size_t)(rb0 + ka0 / (KC * 2)) * nchunk * 2048 + (ka0 % (KC * 2)) * 1024 +
-                      (size_t)gbeg * KC * 2048;
+  const int8_t* srcA = wq + (size_t)(rb0 + ka0 / kPerRbA) * nchunk * kFrag + (ka0 % kPerRbA) * 1024 +
+                      (size_t)gbeg * KC * kFrag;
   const uint8_t* srcB = qq + (size_t)(tb0 + kb0 / KC) * nchunk * 1024 + (kb0 % KC) * 1024 +
                         (size_t)gbeg * KC * 1024;
   const uint8_t* small_src = nullptr;
-  int small_kind = 0;  // 0 none, 1 pairs/mins (advance per stage), 2 d (advance per super-block)
+  int small_kind = 0;  // 0 none, 1 pairs/mins (per stage), 2 d (per super-block), 3 scale bytes (per stage)
   if (wave < St::kSmallJobs) {
     const int u = wave * 64 + lane;
     if (u < St::kUnitsS) {
@@ -191,8 +255,14 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
                     (v % (KC * 8)) * 16;
         small_kind = 1;
       }
-    } else if (u < St::kUnitsS + St::kUnitsM + St::kUnitsD) {
-      const int v = u - St::kUnitsS - St::kUnitsM;
+    } else if (u < St::kUnitsS + St::kUnitsM + St::kUnitsSc) {
+      if (TYPE == QMM_Q4_K) {
+        const int v = u - St::kUnitsS - St::kUnitsM;
+        small_src = wsc + ((size_t)(rb0 + v / (KC * 2)) * nchunk + gbeg * KC) * 32 + (v % (KC * 2)) * 16;
+        small_kind = 3;
+      }
+    } else if (u < St::kUnitsS + St::kUnitsM + St::kUnitsSc + St::kUnitsD) {
+      const int v = u - St::kUnitsS - St::kUnitsM - St::kUnitsSc;
       small_src = (const uint8_t*)wd + ((size_t)(rb0 + v / 8) * nsb + gbeg / kStagesPerSb) * 128 +
                   (v % 8) * 16;
       small_kind = 2;
@@ -207,8 +277,9 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   constexpr int kWaveJobs = kRunA + kRunB + 1;
   auto issue_job = [&](int g, St& st, int j) __attribute__((always_inline)) {
     if (j < kRunA) {
-      __builtin_amdgcn_global_load_lds(srcA + (size_t)g * KC * 2048 + lane * 16 + j * 1024,
-                                       QMM_LDS(&st.a[0][0][0][0] + (ka0 + j) * 1024), 16, 0, 0);
+      if (has_a)
+        __builtin_amdgcn_global_load_lds(srcA + (size_t)g * KC * kFrag + lane * 16 + j * 1024,
+                                         QMM_LDS(&st.a[0][0][0] + (ka0 + j) * 1024), 16, 0, 0);
     } else if (j < kRunA + kRunB) {
       const int u = j - kRunA;
       __builtin_amdgcn_global_load_lds(srcB + (size_t)g * KC * 1024 + lane * 16 + u * 1024,
@@ -218,6 +289,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
       const bool ends_sb = ((g + 1) * KC) % 8 == 0;
       if (small_kind == 1)
         __builtin_amdgcn_global_load_lds(small_src + (size_t)g * KC * 128, QMM_LDS(ls), 16, 0, 0);
+      else if (small_kind == 3)
+        __builtin_amdgcn_global_load_lds(small_src + (size_t)g * KC * 32, QMM_LDS(ls), 16, 0, 0);
       else if (small_kind == 2 && ends_sb)
         __builtin_amdgcn_global_load_lds(small_src + (size_t)((g * KC) / 8) * 128, QMM_LDS(ls), 16, 0, 0);
     }
@@ -230,7 +303,6 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   v16f acc, inner;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-  const v16i zero = {};
 
   if (nstages > 0) issue_stage(0, stage[0]);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -240,30 +312,28 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
     if (g < nstages) {  // uniform per k-group
       St& st = stage[g & 1];
       const bool starts_sb = (g * KC) % 8 == 0;
-      // Software pipeline over the KC chunks: step cc issues the two MFMAs of
+      // Software pipeline over the KC chunks: step cc issues the MFMA(s) of
       // chunk cc+1 (operands read one step earlier), then the LDS reads of chunk
-      // cc+2 and of chunk cc+1's activation scale, then the scale epilogue of
-      // chunk cc on the vector ALU while the matrix core works.  Every LDS value
-      // is consumed one step after its read, so a wait for it never waits for
-      // the reads just issued.
+      // cc+2 and of chunk cc+1's activation scale (and q4_K scale bytes), then
+      // the scale epilogue of chunk cc on the vector ALU while the matrix core
+      // works.  Every LDS value is consumed one step after its read, so a wait
+      // for it never waits for the reads just issued.
+      const int sc_off = 16 * (lane >> 5);
       uint32_t dhr = st.s[wt][0][lane & 31];
-      v4i ahi0 = *(const v4i*)(st.a[wr][0][0] + lane * 16);
-      v4i alo0 = *(const v4i*)(st.a[wr][0][1] + lane * 16);
+      v4i scv = {};
+      if constexpr (TYPE == QMM_Q4_K) scv = *(const v4i*)(&st.sc[wr][0][sc_off]);
+      typename W::A a0 = W::load(st.a[wr][0], lane);
       v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
-      v4i ahi1 = *(const v4i*)(st.a[wr][1][0] + lane * 16);
-      v4i alo1 = *(const v4i*)(st.a[wr][1][1] + lane * 16);
+      typename W::A a1 = W::load(st.a[wr][1], lane);
       v4i bq1 = *(const v4i*)(st.b[wt][1] + lane * 16);
-      v16i jh = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi0, bq0, zero, 0, 0, 0);
-      v16i jl = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo0, bq0, zero, 0, 0, 0);
+      typename W::D dj = W::mma(a0, bq0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int cc = 0; cc < KC; ++cc) {
-        v16i jh_next, jl_next;
+        typename W::D dj_next;
         if (cc + 1 < KC) {
-          jh_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi1, bq1, zero, 0, 0, 0);
-          jl_next = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo1, bq1, zero, 0, 0, 0);
-          pin(jh_next);
-          pin(jl_next);
+          dj_next = W::mma(a1, bq1);
+          W::keep(dj_next);
         }
         // stage (g+1)&1 was last read in iteration g-1, which every wave finished
         // before the barrier that ended it
@@ -273,14 +343,18 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
           for (int q = 0; q < per; ++q)
             if (cc * per + q < kWaveJobs) issue_job(g + 1, stage[(g + 1) & 1], cc * per + q);
         }
-        v4i ahi2, alo2, bq2;
+        typename W::A a2;
+        v4i bq2;
         if (cc + 2 < KC) {
-          ahi2 = *(const v4i*)(st.a[wr][cc + 2][0] + lane * 16);
-          alo2 = *(const v4i*)(st.a[wr][cc + 2][1] + lane * 16);
+          a2 = W::load(st.a[wr][cc + 2], lane);
           bq2 = *(const v4i*)(st.b[wt][cc + 2] + lane * 16);
         }
         uint32_t dhr_next = 0;
-        if (cc + 1 < KC) dhr_next = st.s[wt][cc + 1][lane & 31];
+        v4i scv_next = {};
+        if (cc + 1 < KC) {
+          dhr_next = st.s[wt][cc + 1][lane & 31];
+          if constexpr (TYPE == QMM_Q4_K) scv_next = *(const v4i*)(&st.sc[wr][cc + 1][sc_off]);
+        }
         if (TYPE == QMM_Q4_K && (cc & 1)) {
           const int ck = cc - 1 + (lane >> 5);
           const float mv = st.m[wr][ck][lane & 31];
@@ -290,26 +364,25 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         const float dh = f16_bits_to_float(dhr & 0xFFFF);
         if (cc == 0 && starts_sb) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) inner[i] = (float)((jh[i] << 6) + jl[i]) * dh;
+          for (int i = 0; i < 16; ++i) inner[i] = (float)W::dot(dj, scv, i) * dh;
         } else {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)((jh[i] << 6) + jl[i]), dh, inner[i]);
+          for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)W::dot(dj, scv, i), dh, inner[i]);
         }
         pin(inner);
         if (cc + 1 < KC) {
-          jh = jh_next;
-          jl = jl_next;
-          ahi1 = ahi2;
-          alo1 = alo2;
+          dj = dj_next;
+          a1 = a2;
           bq1 = bq2;
           dhr = dhr_next;
+          scv = scv_next;
         }
         // order inside the step: MFMAs, stage copies, LDS reads, the vector epilogue
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA (next chunk)
-        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);   // VMEM (stage copies)
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA (q4_K min term)
-        __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, W::kMfma, 0);  // MFMA (next chunk)
+        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);         // VMEM (stage copies)
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);         // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA (q4_K min term)
+        __builtin_amdgcn_sched_group_barrier(0x002, 72, 0);        // VALU
         __builtin_amdgcn_sched_barrier(0);
       }
       if (((g + 1) * KC) % 8 == 0) {  // end of a super-block: apply its d
@@ -385,7 +458,7 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
   const int vec_store = (p.od % 4 == 0) && ((uintptr_t)out % 16 == 0);
   const int wgs = plan.dp_row_tiles * plan.tok_tiles + plan.n_tail * plan.split;
   mmq_kernel<TYPE, WR, WT, KC, KS><<<dim3((unsigned)wgs), dim3(64 * WR * WT * KS), 0, s>>>(
-      p.wq, p.wd, p.wm, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
+      p.wq, p.wd, p.wm, p.wsc, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
       plan.dp_row_tiles, plan.split, vec_store, out, scratch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_tail == 0) return e;

@@ -1,11 +1,13 @@
 // qmm_repack.hip -- registration-time repack of q6_K / q4_K blocks into the
 // planes the MMQ streams (the once-per-weight expansion of the r56 and r58
 // pages of the engineering log "minfer / cuda_optimization_steps": r56 sections
-// 2.2-2.3, r58 section 3.2).  Instead of the pages' f32 d*scale pair plane, the
-// small integer scale of every 16/32-weight group is multiplied into the codes
-// (exact) and split into two int8 planes (hi = w >> 6, lo = w & 63), so one
-// K=32 int8 MFMA per plane yields the scale-folded block dot J = 64*J_hi + J_lo;
-// only the f16 d of the 256-weight super-block stays a float.
+// 2.2-2.3, r58 section 3.2).  Instead of the pages' f32 d*scale pair plane the
+// small integer group scales stay integers: q6_K's int8 scale of every 16
+// weights is multiplied into the codes (exact) and the folded weight split into
+// two int8 planes (hi = w >> 6, lo = w & 63), so one K=32 int8 MFMA per plane
+// yields the block dot J = 64*J_hi + J_lo; q4_K's 6-bit scale of every 32 weights
+// goes to a byte plane that the GEMM multiplies into the code dot, and its codes
+// stay 4-bit, two per byte.  Only the f16 d of the super-block stays a float.
 #include "qmm_internal.h"
 #include "qmm_common.h"
 
@@ -15,27 +17,38 @@ namespace qmm {
 
 // ---------------------------------------------------------------------------
 // Plane layout (all device, all library-owned; R = od_pad/32 row blocks):
-//   wq  int8  [R][nchunk][2 planes: hi, lo][2 k-halves][32 rows][16 bytes]
+//   wq  q6_K: int8 [R][nchunk][2 planes: hi, lo][2 k-halves][32 rows][16 bytes]
 //             byte (row j, k) of plane p at
 //             ((j/32*nchunk + k/32)*2 + p)*1024 + ((k%32)/16)*512 + (j%32)*16 + k%16
-//             where the folded weight w = hi*64 + lo, lo in [0, 63]:
-//               q6_K  w = sc[k/16] * (code - 32)      in [-4064, 4096]
-//               q4_K  w = sc[k/32 % 8] * code         in [0, 945]
+//             where the folded weight w = sc[k/16] * (code - 32) = hi*64 + lo,
+//             w in [-4064, 4096], lo in [0, 63]
+//       q4_K: uint8 [R][nchunk][2 k-halves][32 rows][8 bytes]: lane (k-half h,
+//             row) gets 8 bytes, byte b holding code k = 16h + b in its low and
+//             k = 16h + 8 + b in its high nibble (so masking and shifting the
+//             two words gives the 16 codes in MFMA order)
 //   wd  f32   [R][nsb][32 rows]      d of (row, super-block)
 //   wm  f32   [R][nchunk][32 rows]   -dmin*min of (row, chunk); q4_K only
+//   wsc uint8 [R][nchunk][32]        6-bit scale of (row, chunk), q4_K only, at
+//             16*((j/4)%2) + 4*((j%32)/8) + j%4: the 16 bytes a lane half of
+//             the MFMA output layout needs, in its register order
 // Rows od..od_pad-1 are zero in every plane.
 // ---------------------------------------------------------------------------
-size_t wq_bytes(int64_t od_pad, int64_t id) { return (size_t)od_pad * (size_t)id * 2; }
+size_t wq_bytes(int type, int64_t od_pad, int64_t id) {
+  return type == QMM_Q6_K ? (size_t)od_pad * (size_t)id * 2 : (size_t)od_pad * (size_t)id / 2;
+}
 size_t wd_bytes(int64_t od_pad, int64_t id) { return (size_t)od_pad * (size_t)(id / 256) * 4; }
 size_t wm_bytes(int type, int64_t od_pad, int64_t id) {
   return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) * 4 : 0;
 }
+size_t wsc_bytes(int type, int64_t od_pad, int64_t id) {
+  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) : 0;
+}
 
-// One thread per (row j in [0, od_pad), chunk c, k-half h): 16 folded weights.
+// One thread per (row j in [0, od_pad), chunk c, k-half h): 16 weights.
 __global__ void __launch_bounds__(256)
 repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nchunk,
               int64_t total, int8_t* __restrict__ wq, float* __restrict__ wd,
-              float* __restrict__ wm) {
+              float* __restrict__ wm, uint8_t* __restrict__ wsc) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total) return;
   const int h = (int)(gid & 1);
@@ -45,7 +58,8 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
   const int rb = j >> 5, jr = j & 31;
   const int b = c >> 3, cl = c & 7;
 
-  uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
+  uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};  // q6_K planes; q4_K codes in lo[0..1]
+  int sc4 = 0;                                            // q4_K scale
   if (j < od) {
     if (type == QMM_Q6_K) {
       // 210-byte block: ql[128] | qh[64] | int8 scales[16] | f16 d (r56 section 1)
@@ -85,11 +99,11 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
       const uint8_t* qs = B + 16 + 32 * (cl >> 1) + 16 * h;
       const int shift = (cl & 1) * 4;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int w = sc * ((qs[i] >> shift) & 15);
-        hi[i >> 2] |= (uint32_t)(w >> 6) << (8 * (i & 3));
-        lo[i >> 2] |= (uint32_t)(w & 63) << (8 * (i & 3));
+      for (int b8 = 0; b8 < 8; ++b8) {
+        const uint32_t packed = ((qs[b8] >> shift) & 15) | (((qs[b8 + 8] >> shift) & 15) << 4);
+        lo[b8 >> 2] |= packed << (8 * (b8 & 3));
       }
+      sc4 = sc;
       if (h == 0) {
         const float dmin = f16_bits_to_float(B[2] | (B[3] << 8));
         wm[((int64_t)rb * nchunk + c) * 32 + jr] = -(dmin * (float)mn);
@@ -100,16 +114,23 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
     if (type == QMM_Q4_K) wm[((int64_t)rb * nchunk + c) * 32 + jr] = 0.0f;
     if (cl == 0) wd[((int64_t)rb * nsb + b) * 32 + jr] = 0.0f;
   }
-  int8_t* dst = wq + ((int64_t)rb * nchunk + c) * 2048 + h * 512 + jr * 16;
-  *(uint4*)dst = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  *(uint4*)(dst + 1024) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  if (type == QMM_Q6_K) {
+    int8_t* dst = wq + ((int64_t)rb * nchunk + c) * 2048 + h * 512 + jr * 16;
+    *(uint4*)dst = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *(uint4*)(dst + 1024) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  } else {
+    int8_t* dst = wq + ((int64_t)rb * nchunk + c) * kQ4CodeFrag + h * 256 + jr * 8;
+    *(uint2*)dst = make_uint2(lo[0], lo[1]);
+    if (h == 0)
+      wsc[((int64_t)rb * nchunk + c) * 32 + 16 * ((jr >> 2) & 1) + 4 * (jr >> 3) + (jr & 3)] = (uint8_t)sc4;
+  }
 }
 
 hipError_t launch_repack(const uint8_t* raw, const Planes& p, hipStream_t s) {
   const int64_t total = p.od_pad * p.nchunk * 2;
   const int64_t blocks = (total + 255) / 256;
   repack_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-      raw, p.type, (int)p.od, (int)p.nsb, (int)p.nchunk, total, p.wq, p.wd, p.wm);
+      raw, p.type, (int)p.od, (int)p.nsb, (int)p.nchunk, total, p.wq, p.wd, p.wm, p.wsc);
   return hipGetLastError();
 }
 

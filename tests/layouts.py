@@ -22,17 +22,32 @@ def read_qact(buf: np.ndarray, n_tok: int, id_: int):
     return q, sp[:, :, 0].copy(), sp[:, :, 1].copy()
 
 
-def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: int, wm_offset: int):
-    """exported planes -> (w [od_pad][id] int32 folded weights, d [od_pad][nsb] f32,
-    wm [od_pad][nchunk] f32 or None)."""
+def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: int, wm_offset: int,
+                sc_offset: int):
+    """exported planes -> (w [od_pad][id] int32 scale-carrying weights: q6_K the
+    folded 64*hi + lo, q4_K scale * code; d [od_pad][nsb] f32; wm [od_pad][nchunk]
+    f32 or None)."""
     nchunk, nsb = id_ // 32, id_ // 256
     R = od_pad // 32
     buf = np.asarray(buf, np.uint8)
-    wq = buf[: od_pad * id_ * 2].view(np.int8).reshape(R, nchunk, 2, 2, 32, 16)
-    hi = wq[:, :, 0].transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
-    lo = wq[:, :, 1].transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
-    assert lo.min() >= 0 and lo.max() <= 63
-    w = hi * 64 + lo
+    if type_ == 6:
+        wq = buf[: od_pad * id_ * 2].view(np.int8).reshape(R, nchunk, 2, 2, 32, 16)
+        hi = wq[:, :, 0].transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
+        lo = wq[:, :, 1].transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
+        assert lo.min() >= 0 and lo.max() <= 63
+        w = hi * 64 + lo
+    else:
+        # [R][nchunk][k-half h][row][byte b]: code k = 16h + b (low nibble), 16h + 8 + b (high)
+        pk = buf[: od_pad * id_ // 2].reshape(R, nchunk, 2, 32, 8)
+        codes = np.concatenate([pk & 15, pk >> 4], axis=-1)          # [R][nchunk][h][row][16]
+        codes = codes.transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
+        # scale byte of row j at 16*((j/4)%2) + 4*((j%32)/8) + j%4
+        scb = buf[sc_offset: sc_offset + od_pad * nchunk].reshape(R, nchunk, 32)
+        j = np.arange(32)
+        pos = 16 * ((j // 4) % 2) + 4 * (j // 8) + j % 4
+        sc = scb[:, :, pos].transpose(0, 2, 1).reshape(od_pad, nchunk).astype(np.int32)
+        assert sc.max() <= 63
+        w = codes * np.repeat(sc, 32, axis=1)
     d = buf[wd_offset: wd_offset + od_pad * nsb * 4].view("<f4").reshape(R, nsb, 32)
     d = d.transpose(0, 2, 1).reshape(od_pad, nsb)
     wm = None

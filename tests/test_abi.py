@@ -111,3 +111,13 @@ def test_info_and_export_reject_null():
     assert L.qmm_weights_info(None, ctypes.byref(info)) == qmm.EINVAL
     assert L.qmm_weights_export(None, ctypes.c_void_p(4096), 10) == qmm.EINVAL
     L.qmm_release_weights(None)  # no-op
+
+
+def test_info_struct_matches_header():
+    """The binding's qmm_info mirror has the header's fields, in order."""
+    import re
+    hdr = open(os.path.join(ROOT, "include", "qmm.h")).read()
+    body = re.search(r"typedef struct \{(.*?)\} qmm_info;", hdr, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"(\w+)\s*;", body)
+    assert names == [f[0] for f in qmm.Info._fields_]

@@ -152,7 +152,8 @@ def test_planes_byte_exact(type_, od, id_, full):
     raw = _full_range_q6k(rng, od, id_) if full else synth.weights(rng, type_, od, id_)
     w = qmm.register_weights(type_, od, id_, raw)
     assert w.od_pad % 128 == 0 and w.od_pad >= od
-    gw, gd, gwm = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.wm_offset)
+    gw, gd, gwm = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.wm_offset,
+                                      w.sc_offset)
     ew, ed, ewm = expected_planes(type_, raw, od, id_)
     assert np.array_equal(gw[:od], ew)
     assert np.array_equal(gd[:od].view(np.uint32), ed.view(np.uint32))
