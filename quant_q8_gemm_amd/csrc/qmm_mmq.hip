@@ -37,12 +37,13 @@ namespace qmm {
 // its own LDS stages, and their sums are added once at the end (k-group 0's
 // plus k-group 1's, always in that order): twice the waves per tile for shapes
 // with too few tiles to keep the CUs busy.  The inner dimension is walked in
-// stages of KC chunks of 32 (KC = 4: half a 256-wide super-block, KC = 8: a
-// whole one).  Each stage's operands -- both weight planes of the WR row blocks,
-// the q8 codes and scale pairs of the WT token blocks, and d (and for q4_K the
-// -dmin*min plane) -- are copied once per work-group into LDS with direct
-// global->LDS loads (global_load_lds_dwordx4 puts lane l's 16 bytes at the LDS
-// base + 16*l, so one wave instruction moves one 1 KiB fragment), and read from
+// stages of KC chunks of 32 (KC = 2, 4 or 8: a quarter, half or whole 256-wide
+// super-block).  Each stage's operands -- the weight fragments of the WR row
+// blocks, the q8 codes and scale pairs of the WT token blocks, and d (and for
+// q4_K the -dmin*min plane and the scale bytes) -- are copied once per
+// work-group into LDS with direct global->LDS loads (global_load_lds_dwordx4
+// puts lane l's 16 bytes at the LDS base + 16*l, so one wave instruction moves
+// one 1 KiB fragment), and read from
 // there by every wave that shares them.  Two LDS stages alternate: the loads of
 // stage g+1 are issued during stage g, a few per chunk step; one barrier per
 // stage.
@@ -143,8 +144,8 @@ __device__ __forceinline__ void tile_of(int pos, int row_tiles, int tok_tiles, i
 // Output layout of a wave's 32 x 32 block: lane holds token (lane & 31) and,
 // in acc[4*q + i], row 4*(lane >> 5) + 8*q + i.  store_quad writes the four
 // rows of one q into out[t][od], masked at od and n_tok.
-__device__ __forceinline__ void store_quad(float* __restrict__ out, float4 v, int rblock, int tblock, int lane,
-                                           int q, int od, int n_tok, int vec_store) {
+__device__ __forceinline__ void store_quad(float* __restrict__ out, float4 v, int rblock, int tblock,
+                                           int lane, int q, int od, int n_tok, int vec_store) {
   const int tok = tblock * 32 + (lane & 31);
   if (tok >= n_tok) return;
   float* orow = out + (size_t)tok * od;
@@ -186,7 +187,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   using W = WeightOps<TYPE>;
   constexpr int kWaves = WR * WT;
   constexpr int kJobsA = WR * KC * kFragA<TYPE> / 1024, kJobsB = WT * KC;
-  static_assert(KC == 4 || KC == 8, "a stage is half or a whole super-block");
+  static_assert(KC == 2 || KC == 4 || KC == 8, "a stage is a quarter, half or a whole super-block");
   static_assert(KS == 1 || KS == 2, "one or two k-groups");
   // k-group 1's sums pass to k-group 0 through k-group 0's two stages
   static_assert(KS == 1 || 2 * sizeof(St) >= (size_t)kWaves * 16 * 64 * 4, "room to combine k-groups");
@@ -468,9 +469,12 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
 }
 
 // Tile geometry per launch.  Two shapes of the same kernel:
-//  * 2 x 2 waves (64 x 64 tile), one k-group, half-super-block stages: about
-//    52 KiB of LDS, three work-groups (12 waves) per CU, so one group's barrier
-//    wait is covered by the others; for shapes with many tiles;
+//  * 2 x 2 waves (64 x 64 tile), one k-group, for shapes with many tiles:
+//    several work-groups per CU, so one group's barrier wait is covered by the
+//    others.  Four per CU (16 waves) for both types: q4_K with half-super-block
+//    stages (30 KiB of LDS, 108 VGPRs), q6_K with quarter-super-block stages
+//    (27 KiB, 113 VGPRs; half-super-block stages take 53 KiB, which fits only
+//    three per CU and ran 7-9% slower);
 //  * 2 x 4 waves (64 rows x 128 tokens) in two k-groups (16 waves), half-super-
 //    block stages, about 140 KiB of LDS, one work-group per CU; for shapes with
 //    too few tiles to fill the CUs several times (e.g. 512 tokens x 4096 rows =
@@ -510,7 +514,7 @@ size_t mmq_scratch_max_bytes(int num_cus) { return (size_t)num_cus * (64 * 128) 
 hipError_t launch_mmq(const Planes& p, const MmqPlan& plan, const uint8_t* qact, int64_t n_tok,
                       int64_t t_pad, float* out, float* scratch, hipStream_t s) {
   if (p.type == QMM_Q6_K)
-    return plan.many ? launch_tiled<QMM_Q6_K, 2, 2, 4, 1>(p, plan, qact, n_tok, t_pad, out, scratch, s)
+    return plan.many ? launch_tiled<QMM_Q6_K, 2, 2, 2, 1>(p, plan, qact, n_tok, t_pad, out, scratch, s)
                      : launch_tiled<QMM_Q6_K, 2, 4, 4, 2>(p, plan, qact, n_tok, t_pad, out, scratch, s);
   return plan.many ? launch_tiled<QMM_Q4_K, 2, 2, 4, 1>(p, plan, qact, n_tok, t_pad, out, scratch, s)
                    : launch_tiled<QMM_Q4_K, 2, 4, 4, 2>(p, plan, qact, n_tok, t_pad, out, scratch, s);
