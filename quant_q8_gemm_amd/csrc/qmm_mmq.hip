@@ -232,11 +232,13 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   constexpr int kFrag = kFragA<TYPE>;
   constexpr int kPerRbA = KC * kFrag / 1024;  // weight jobs per row block and stage
   static_assert(kJobsA % kWaves == 0 || kJobsA < kWaves, "equal weight runs per wave");
-  static_assert(kJobsB % kWaves == 0, "equal code runs per wave");
-  constexpr int kRunA = kJobsA >= kWaves ? kJobsA / kWaves : 1, kRunB = kJobsB / kWaves;
+  static_assert(kJobsB % kWaves == 0 || kJobsB < kWaves, "equal code runs per wave");
+  constexpr int kRunA = kJobsA >= kWaves ? kJobsA / kWaves : 1;
+  constexpr int kRunB = kJobsB >= kWaves ? kJobsB / kWaves : 1;
   static_assert(kPerRbA % kRunA == 0 && KC % kRunB == 0, "a run stays inside one block");
   static_assert(St::kSmallJobs <= kWaves, "one small-region job per wave at most");
   const bool has_a = kJobsA >= kWaves || wave < kJobsA;
+  const bool has_b = kJobsB >= kWaves || wave < kJobsB;
   const int ka0 = wave * kRunA, kb0 = wave * kRunB;
   const int8_t* srcA = wq + (size_t)(rb0 + ka0 / kPerRbA) * nchunk * kFrag + (ka0 % kPerRbA) * 1024 +
                       (size_t)gbeg * KC * kFrag;
@@ -283,8 +285,9 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
                                          QMM_LDS(&st.a[0][0][0] + (ka0 + j) * 1024), 16, 0, 0);
     } else if (j < kRunA + kRunB) {
       const int u = j - kRunA;
-      __builtin_amdgcn_global_load_lds(srcB + (size_t)g * KC * 1024 + lane * 16 + u * 1024,
-                                       QMM_LDS(&st.b[0][0][0] + (kb0 + u) * 1024), 16, 0, 0);
+      if (has_b)
+        __builtin_amdgcn_global_load_lds(srcB + (size_t)g * KC * 1024 + lane * 16 + u * 1024,
+                                         QMM_LDS(&st.b[0][0][0] + (kb0 + u) * 1024), 16, 0, 0);
     } else if (wave < St::kSmallJobs) {
       uint8_t* ls = (uint8_t*)&st.s[0][0][0] + wave * 1024;
       const bool ends_sb = ((g + 1) * KC) % 8 == 0;
