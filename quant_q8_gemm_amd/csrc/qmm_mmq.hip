@@ -312,10 +312,16 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int g = 0; g < niter; ++g) {
+  // Super-blocks in turn, the stages of one unrolled, so where a super-block
+  // starts and ends (first chunk: inner = J*dh; last: apply d) is known at
+  // compile time.
+  for (int sbi = 0; sbi < niter / kStagesPerSb; ++sbi) {
+#pragma unroll
+  for (int h = 0; h < kStagesPerSb; ++h) {
+    const int g = sbi * kStagesPerSb + h;
     if (g < nstages) {  // uniform per k-group
       St& st = stage[g & 1];
-      const bool starts_sb = (g * KC) % 8 == 0;
+      const bool starts_sb = h == 0;
       // Software pipeline over the KC chunks: step cc issues the MFMA(s) of
       // chunk cc+1 (operands read one step earlier), then the LDS reads of chunk
       // cc+2 and of chunk cc+1's activation scale (and q4_K scale bytes), then
@@ -389,7 +395,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         __builtin_amdgcn_sched_group_barrier(0x002, 72, 0);        // VALU
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (((g + 1) * KC) % 8 == 0) {  // end of a super-block: apply its d
+      if (h == kStagesPerSb - 1) {  // end of a super-block: apply its d
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float4 d4 = *(const float4*)(&st.d[wr][8 * q + 4 * (lane >> 5)]);
@@ -404,6 +410,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads for g+1 landed
       __syncthreads();                                   // everyone's landed; stage g is free
     }
+  }
   }
 #undef QMM_LDS
   if (KS > 1) {  // add k-group 1's partial sums to k-group 0's, in that order

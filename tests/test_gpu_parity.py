@@ -367,6 +367,29 @@ def test_fused_same_type_gemms_match_separate(T):
             w.release()
 
 
+def test_concurrent_streams_share_a_handle():
+    """One handle used on two streams at once, on a shape whose ragged last wave
+    needs the tail scratch (one buffer per stream): both results equal the
+    single-stream result, repeatedly."""
+    say("two streams, one handle, tail scratch")
+    type_, od, id_, T = synth.Q6_K, 4200, 768, 500
+    raw, x = synth.case(type_, od, id_, T, seed=5)
+    w = qmm.register_weights(type_, od, id_, raw)
+    qact = gpu_quantize(x)
+    ref = run_mmq(w, qact, T)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.full((T, od), float("nan"), device="cuda") for _ in streams]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for st, o in zip(streams, outs):
+            with torch.cuda.stream(st):
+                qmm.mmq(w, qact, T, out=o, stream=st)
+        torch.cuda.synchronize()
+        for o in outs:
+            assert np.array_equal(o.cpu().numpy(), ref)
+    w.release()
+
+
 def test_writes_stay_inside_output():
     type_, od, id_, T = synth.Q4_K, 77, 512, 45
     say("output bounds")
