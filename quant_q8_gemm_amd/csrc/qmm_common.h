@@ -20,6 +20,14 @@ __device__ __forceinline__ void pin(T& v) {
   asm volatile("" : "+v"(v));
 }
 
+// A pointer every lane of the wave holds, moved to scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float f16_bits_to_float(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }

@@ -53,6 +53,25 @@ namespace qmm {
 // lane's 16 outputs share one token: the activation scale dh is one register
 // per chunk, and the super-block d is applied once per 8 chunks.
 // ---------------------------------------------------------------------------
+// Direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4: lane
+// l's bytes land at the LDS byte address held in M0 plus 16*l).  Written out so
+// that a wave-uniform source is addressed as scalar base + the lane's offset;
+// the builtin form lets the compiler turn the source into a per-lane 64-bit
+// induction variable, a few vector instructions per copy.  M0 is set by each
+// copy itself; a kernel uses either these or the builtin, never both, so no
+// compiler-generated M0 value is live across them.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+__device__ __forceinline__ void copy16_uniform(const void* base, uint32_t lane_off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(lane_off), "s"(base), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void copy16_lane(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds) : "memory");
+}
+
 // Weight fragment bytes per (32-row block, chunk): q6_K hi and lo planes of
 // 1 KiB each; q4_K packed codes (8 bytes per lane).
 template <int TYPE>
@@ -240,10 +259,13 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   const bool has_a = kJobsA >= kWaves || wave < kJobsA;
   const bool has_b = kJobsB >= kWaves || wave < kJobsB;
   const int ka0 = wave * kRunA, kb0 = wave * kRunB;
+  // wave-uniform sources: the copies address them as a scalar base plus the
+  // lane's 16-byte offset, with no per-copy vector arithmetic
   const int8_t* srcA = wq + (size_t)(rb0 + ka0 / kPerRbA) * nchunk * kFrag + (ka0 % kPerRbA) * 1024 +
                       (size_t)gbeg * KC * kFrag;
   const uint8_t* srcB = qq + (size_t)(tb0 + kb0 / KC) * nchunk * 1024 + (kb0 % KC) * 1024 +
                         (size_t)gbeg * KC * 1024;
+  const uint32_t lane_off = (uint32_t)lane * 16;
   const uint8_t* small_src = nullptr;
   int small_kind = 0;  // 0 none, 1 pairs/mins (per stage), 2 d (per super-block), 3 scale bytes (per stage)
   if (wave < St::kSmallJobs) {
@@ -272,31 +294,45 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
     }
   }
 
-#define QMM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
   // This wave's copy jobs for one stage, numbered: its weight run, its code run,
   // its small-region job.  The jobs of stage g+1 are spread over the chunk steps
   // of stage g (a few per step) rather than issued in one burst, so the copies'
   // LDS writes interleave with the steps' LDS reads instead of stalling them.
   constexpr int kWaveJobs = kRunA + kRunB + 1;
+  // One 1 KiB copy job: a wave-uniform source (weight or code fragments) or a
+  // per-lane source (the small region).  The written-out form measured 4-7%
+  // faster for half- and whole-super-block stages and 1-2% slower for quarter
+  // stages (q6_K, many tiles), which keep the builtin.
+  auto copy_uniform = [&](const void* src, void* dst) __attribute__((always_inline)) {
+    if constexpr (KC >= 4)
+      copy16_uniform(uniform_ptr(src), lane_off, __builtin_amdgcn_readfirstlane(lds_addr(dst)));
+    else
+      __builtin_amdgcn_global_load_lds((const uint8_t*)src + lane_off,
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
+  auto copy_lane = [&](const void* src, void* dst) __attribute__((always_inline)) {
+    if constexpr (KC >= 4)
+      copy16_lane(src, __builtin_amdgcn_readfirstlane(lds_addr(dst)));
+    else
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
   auto issue_job = [&](int g, St& st, int j) __attribute__((always_inline)) {
     if (j < kRunA) {
       if (has_a)
-        __builtin_amdgcn_global_load_lds(srcA + (size_t)g * KC * kFrag + lane * 16 + j * 1024,
-                                         QMM_LDS(&st.a[0][0][0] + (ka0 + j) * 1024), 16, 0, 0);
+        copy_uniform(srcA + (size_t)g * KC * kFrag + j * 1024, &st.a[0][0][0] + (ka0 + j) * 1024);
     } else if (j < kRunA + kRunB) {
       const int u = j - kRunA;
       if (has_b)
-        __builtin_amdgcn_global_load_lds(srcB + (size_t)g * KC * 1024 + lane * 16 + u * 1024,
-                                         QMM_LDS(&st.b[0][0][0] + (kb0 + u) * 1024), 16, 0, 0);
+        copy_uniform(srcB + (size_t)g * KC * 1024 + u * 1024, &st.b[0][0][0] + (kb0 + u) * 1024);
     } else if (wave < St::kSmallJobs) {
       uint8_t* ls = (uint8_t*)&st.s[0][0][0] + wave * 1024;
       const bool ends_sb = ((g + 1) * KC) % 8 == 0;
       if (small_kind == 1)
-        __builtin_amdgcn_global_load_lds(small_src + (size_t)g * KC * 128, QMM_LDS(ls), 16, 0, 0);
+        copy_lane(small_src + (size_t)g * KC * 128, ls);
       else if (small_kind == 3)
-        __builtin_amdgcn_global_load_lds(small_src + (size_t)g * KC * 32, QMM_LDS(ls), 16, 0, 0);
+        copy_lane(small_src + (size_t)g * KC * 32, ls);
       else if (small_kind == 2 && ends_sb)
-        __builtin_amdgcn_global_load_lds(small_src + (size_t)((g * KC) / 8) * 128, QMM_LDS(ls), 16, 0, 0);
+        copy_lane(small_src + (size_t)((g * KC) / 8) * 128, ls);
     }
   };
   auto issue_stage = [&](int g, St& st) __attribute__((always_inline)) {  // all at once (prologue)
@@ -412,7 +448,6 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
     }
   }
   }
-#undef QMM_LDS
   if (KS > 1) {  // add k-group 1's partial sums to k-group 0's, in that order
     __syncthreads();  // every wave is done with the stage buffers
     float* red = (float*)&stage_all[0][0] + wave * 1024 + lane;
