@@ -37,6 +37,9 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 MFMA_INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
+# The vector-ALU roof of the scale epilogue: each (token, row, 32-block) takes 64
+# int8 MFMA ops and 3 VALU instructions, 256 CUs x 64 lanes x 2.4 GHz lane-ops/s.
+VALU_EPILOGUE_PEAK_TOPS = 256 * 64 * 2.4e9 * 64 / 3 / 1e12
 HBM_PEAK_GBS = 8000.0
 COLD_BYTES = 512 << 20         # weight planes cycled per cold pass: twice the 256 MB cache
 
@@ -348,6 +351,10 @@ def main():
             "algorithmic_ops_per_step": ops,
             "algorithmic_bytes_per_step": alg_bytes,
             "kernel_sha256_16": kernel_hash(),
+            # the roof that binds by design: the per-32-block scale epilogue
+            "epilogue_roof": {"bound": "alu", "peak": round(VALU_EPILOGUE_PEAK_TOPS, 1),
+                              "unit": "TOP/s (int8-equivalent)",
+                              "frac": round(mmq_tops / VALU_EPILOGUE_PEAK_TOPS, 4)},
         },
         "plane_bytes": sum(w.plane_bytes for w in weights.values()),
         "raw_weight_bytes": sum(w.raw_bytes for w in weights.values()),
