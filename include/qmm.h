@@ -189,8 +189,8 @@ int qmm_quantize_activations(const float *x, int64_t n_tok, int64_t id, void *qa
  * When the output tiles fill the GPU's compute units a whole number of times
  * plus a small remainder, the remainder's tiles are split along the inner
  * dimension into partial sums that a second kernel adds in a fixed order.  Their
- * scratch is one device buffer per (device, stream) of 32 KiB per compute unit
- * (8 MiB on MI355X), allocated with hipMalloc by the first call on that stream
+ * scratch is one device buffer per (device, stream) of 64 KiB per compute unit
+ * (16 MiB on MI355X), allocated with hipMalloc by the first call on that stream
  * that needs it and kept until the process ends; calls on one stream share it
  * in stream order.  Synchronize a stream before destroying it if an MMQ on it
  * may still run.  Results are deterministic: the same call gives the same bits.

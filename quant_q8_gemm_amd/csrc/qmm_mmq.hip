@@ -523,8 +523,11 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
 //  * 2 x 4 waves (64 rows x 128 tokens) in two k-groups (16 waves), half-super-
 //    block stages, about 140 KiB of LDS, one work-group per CU; for shapes with
 //    too few tiles to fill the CUs several times (e.g. 512 tokens x 4096 rows =
-//    256 work-groups), where the second k-group doubles the waves per CU.  Here
-//    a ragged last wave (e.g. 4097 rows: 264 tiles on 256 CUs) is split along K.
+//    256 work-groups), where the second k-group doubles the waves per CU.
+// In both, a ragged second wave (tiles = slots + r with r <= slots / 2, the
+// slots being the work-groups resident at once; e.g. 4097 rows x 512 tokens:
+// 264 tiles on 256 CUs, 11008 rows x 512 tokens: 1376 tiles on 1024 slots) is
+// split along K.
 // The switch point (about four 64 x 64 tiles per CU) was chosen by timing both
 // on the 512-token shapes, the 3314-token layer shapes and the 2048-token head.
 MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
@@ -537,24 +540,30 @@ MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
   plan.dp_row_tiles = plan.row_tiles;
   plan.split = 1;
   const int64_t tiles = (int64_t)plan.row_tiles * plan.tok_tiles;
-  if (!plan.many && num_cus > 0 && tiles > num_cus && tiles % num_cus != 0) {
-    // one work-group per CU: whole waves stay data-parallel (whole row tiles),
-    // the row tiles after them form the tail
-    const int dp_rows = (int)((tiles / num_cus) * num_cus / plan.tok_tiles);
+  // work-groups resident at once: one per CU (few tiles), four (many tiles)
+  const int64_t slots = (int64_t)num_cus * (plan.many ? 4 : 1);
+  // Only after a single full wave: behind several (e.g. 3328 tiles on 1024
+  // slots) the tail's work-groups already overlap the last full wave's end, and
+  // the split measured 0.5-1% slower there instead of 9% faster.
+  if (num_cus > 0 && tiles > slots && tiles < 2 * slots) {
+    // the full wave stays data-parallel (whole row tiles), the row tiles after
+    // it form the tail
+    const int dp_rows = (int)((tiles / slots) * slots / plan.tok_tiles);
     const int n_tail = (plan.row_tiles - dp_rows) * plan.tok_tiles;
-    const int split = (int)std::min<int64_t>(num_cus / n_tail, p.nsb);
+    const int split = (int)std::min<int64_t>(slots / n_tail, p.nsb);
     if (split >= 2) {
       plan.dp_row_tiles = dp_rows;
       plan.n_tail = n_tail;
       plan.split = split;
-      plan.scratch_bytes = (size_t)n_tail * split * (64 * 128) * sizeof(float);
+      plan.scratch_bytes = (size_t)n_tail * split * (64 * 32 * wt) * sizeof(float);
     }
   }
   return plan;
 }
 
-// n_tail * split <= num_cus work-groups, each one 64 x 128 partial tile.
-size_t mmq_scratch_max_bytes(int num_cus) { return (size_t)num_cus * (64 * 128) * sizeof(float); }
+// n_tail * split work-groups, at most one per slot: num_cus 64 x 128 partial
+// tiles or 4 * num_cus 64 x 64 ones.
+size_t mmq_scratch_max_bytes(int num_cus) { return (size_t)num_cus * (64 * 256) * sizeof(float); }
 
 hipError_t launch_mmq(const Planes& p, const MmqPlan& plan, const uint8_t* qact, int64_t n_tok,
                       int64_t t_pad, float* out, float* scratch, hipStream_t s) {

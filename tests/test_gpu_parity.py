@@ -336,11 +336,12 @@ def test_odd_rows_and_token_tail_are_prefixes_and_repeatable():
 def test_fused_same_type_gemms_match_separate(T):
     """Row-concatenated registration (gate||up, q||k) on one shared qact: each
     column block of the fused result and the separate GEMM agree with the oracle
-    on sampled elements.  gate||up (22016 rows) and gate, up alone (11008 rows)
-    all have enough tiles for the same tile geometry, so there the per-element
-    summation order is the same and the blocks are bit-identical; q||k (8192
-    rows) and q, k (4096 rows) may differ in geometry at 512 tokens (one or two
-    k-groups), which changes only the f32 summation order."""
+    on sampled elements.  At 3314 tokens gate||up (22016 rows) and gate, up alone
+    (11008 rows) use the same tile geometry and fill the GPU's work-group slots
+    with no ragged last wave, so the per-element summation order is the same and
+    the blocks are bit-identical.  Otherwise the geometry (one or two k-groups)
+    or a K-split of a ragged last wave may differ between the two launches,
+    which changes only the f32 summation order."""
     say(f"fused gate||up and q||k, T={T}")
     rng = np.random.default_rng(21)
     id_ = 4096
@@ -361,7 +362,7 @@ def test_fused_same_type_gemms_match_separate(T):
             ref, A = oracle.mmq_at(synth.Q4_K, raw, od, id_, q, dh, s, ts, js)
             check_close(blk[ts, js], ref, A, f"fused od={2 * od} half {half}")
             check_close(sep[ts, js], ref, A, f"separate od={od} half {half}")
-            if od == 11008:
+            if od == 11008 and T == 3314:
                 assert np.array_equal(blk, sep)
         for w in (wa, wb, wf):
             w.release()
