@@ -18,7 +18,8 @@
 //    MFMA gives the code dot D, and J = sc*D is one 24-bit integer multiply
 //    whose scale byte the instruction selects itself (SDWA);
 //  * planes are stored in MFMA fragment order, so every lane's operand is one
-//    contiguous 16-byte load and a wave's load is one contiguous 1 KiB;
+//    contiguous 16-byte (q4_K codes: 8-byte) load and a wave's load is one
+//    contiguous 1 KiB (512 bytes);
 //  * the q4_K min term sum_c dmin*min_c*s_c is a true small matrix product over
 //    chunks; it runs on the f32 MFMA (32x32x2) instead of the vector ALU.
 #include "qmm_internal.h"
@@ -43,10 +44,9 @@ namespace qmm {
 // q4_K the -dmin*min plane and the scale bytes) -- are copied once per
 // work-group into LDS with direct global->LDS loads (global_load_lds_dwordx4
 // puts lane l's 16 bytes at the LDS base + 16*l, so one wave instruction moves
-// one 1 KiB fragment), and read from
-// there by every wave that shares them.  Two LDS stages alternate: the loads of
-// stage g+1 are issued during stage g, a few per chunk step; one barrier per
-// stage.
+// 1 KiB), and read from there by every wave that shares them.  Two LDS stages
+// alternate: the loads of stage g+1 are issued during stage g, a few per chunk
+// step; one barrier per stage.
 // A small tile and a small LDS footprint let several work-groups share a CU, so
 // one group's barrier wait is covered by the others' work.
 // MFMA orientation: A = weights (rows j), B = activations (columns t), so each
@@ -142,7 +142,7 @@ struct WeightOps<QMM_Q4_K> {
 // round-robin over the 8 XCDs (each with its own 4 MiB L2), so first every XCD
 // gets a contiguous run of positions; positions then walk the tiles in groups of
 // kGroupRows row tiles, row tile fastest, so the work-groups resident on one XCD
-// at a time (about 96) form a block of ~8 row tiles x ~12 token tiles that
+// at a time (32 or 128) form a block of 8 row tiles x 4 to 16 token tiles that
 // share both their weight rows and their activations in that L2.
 constexpr int kGroupRows = 8;
 
@@ -187,18 +187,19 @@ __device__ __forceinline__ void store_block(float* __restrict__ out, const v16f&
                lane, q, od, n_tok, vec_store);
 }
 
-// Ragged last wave ("tail").  When the tiles fill the CUs k times and a few
-// more, the first k waves' worth of row tiles run whole (data-parallel) and
-// each of the remaining tail tiles is split along K into S slices of
-// super-blocks, so the tail runs S times wider.  A slice writes its partial
+// Ragged second wave ("tail").  When the tiles fill the resident work-group
+// slots once and a few more, the first wave's worth of row tiles run whole
+// (data-parallel) and each of the remaining tail tiles is split along K into
+// S slices of super-blocks, so the tail runs S times wider.  A slice writes its partial
 // tile, in the work-group's register order, to a scratch buffer; the fixup
 // kernel adds a tile's S partials in slice order and stores the tile.  The
 // tail is whole row tiles at the end, so the rows before it keep exactly the
 // summation order they have without a tail.
 template <int TYPE, int WR, int WT, int KC, int KS>
-__global__ void __launch_bounds__(64 * WR * WT * KS, (WR * WT * KS == 4) ? 3 : 1)
+__global__ void __launch_bounds__(64 * WR * WT * KS, (WR * WT * KS == 4) ? 4 : 1)
 mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
-           const float* __restrict__ wm, const uint8_t* __restrict__ wsc, const uint8_t* __restrict__ qq,
+           const float* __restrict__ wm, const uint8_t* __restrict__ wsc,
+           const uint8_t* __restrict__ qq,
            const uint8_t* __restrict__ qs, int nchunk, int nsb, int od, int n_tok,
            int tok_tiles, int dp_row_tiles, int split, int vec_store, float* __restrict__ out,
            float* __restrict__ part) {
@@ -259,8 +260,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   const bool has_a = kJobsA >= kWaves || wave < kJobsA;
   const bool has_b = kJobsB >= kWaves || wave < kJobsB;
   const int ka0 = wave * kRunA, kb0 = wave * kRunB;
-  // wave-uniform sources: the copies address them as a scalar base plus the
-  // lane's 16-byte offset, with no per-copy vector arithmetic
+  // wave-uniform sources (see copy_uniform below)
   const int8_t* srcA = wq + (size_t)(rb0 + ka0 / kPerRbA) * nchunk * kFrag + (ka0 % kPerRbA) * 1024 +
                       (size_t)gbeg * KC * kFrag;
   const uint8_t* srcB = qq + (size_t)(tb0 + kb0 / KC) * nchunk * 1024 + (kb0 % KC) * 1024 +
@@ -353,100 +353,100 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   // compile time.
   for (int sbi = 0; sbi < niter / kStagesPerSb; ++sbi) {
 #pragma unroll
-  for (int h = 0; h < kStagesPerSb; ++h) {
-    const int g = sbi * kStagesPerSb + h;
-    if (g < nstages) {  // uniform per k-group
-      St& st = stage[g & 1];
-      const bool starts_sb = h == 0;
-      // Software pipeline over the KC chunks: step cc issues the MFMA(s) of
-      // chunk cc+1 (operands read one step earlier), then the LDS reads of chunk
-      // cc+2 and of chunk cc+1's activation scale (and q4_K scale bytes), then
-      // the scale epilogue of chunk cc on the vector ALU while the matrix core
-      // works.  Every LDS value is consumed one step after its read, so a wait
-      // for it never waits for the reads just issued.
-      const int sc_off = 16 * (lane >> 5);
-      uint32_t dhr = st.s[wt][0][lane & 31];
-      v4i scv = {};
-      if constexpr (TYPE == QMM_Q4_K) scv = *(const v4i*)(&st.sc[wr][0][sc_off]);
-      typename W::A a0 = W::load(st.a[wr][0], lane);
-      v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
-      typename W::A a1 = W::load(st.a[wr][1], lane);
-      v4i bq1 = *(const v4i*)(st.b[wt][1] + lane * 16);
-      typename W::D dj = W::mma(a0, bq0);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int cc = 0; cc < KC; ++cc) {
-        typename W::D dj_next;
-        if (cc + 1 < KC) {
-          dj_next = W::mma(a1, bq1);
-          W::keep(dj_next);
-        }
-        // stage (g+1)&1 was last read in iteration g-1, which every wave finished
-        // before the barrier that ended it
-        if (g + 1 < nstages) {
-          constexpr int per = (kWaveJobs + KC - 1) / KC;
-#pragma unroll
-          for (int q = 0; q < per; ++q)
-            if (cc * per + q < kWaveJobs) issue_job(g + 1, stage[(g + 1) & 1], cc * per + q);
-        }
-        typename W::A a2;
-        v4i bq2;
-        if (cc + 2 < KC) {
-          a2 = W::load(st.a[wr][cc + 2], lane);
-          bq2 = *(const v4i*)(st.b[wt][cc + 2] + lane * 16);
-        }
-        uint32_t dhr_next = 0;
-        v4i scv_next = {};
-        if (cc + 1 < KC) {
-          dhr_next = st.s[wt][cc + 1][lane & 31];
-          if constexpr (TYPE == QMM_Q4_K) scv_next = *(const v4i*)(&st.sc[wr][cc + 1][sc_off]);
-        }
-        if (TYPE == QMM_Q4_K && (cc & 1)) {
-          const int ck = cc - 1 + (lane >> 5);
-          const float mv = st.m[wr][ck][lane & 31];
-          const float sv = f16_bits_to_float(st.s[wt][ck][lane & 31] >> 16);
-          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(mv, sv, acc, 0, 0, 0);
-        }
-        const float dh = f16_bits_to_float(dhr & 0xFFFF);
-        if (cc == 0 && starts_sb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) inner[i] = (float)W::dot(dj, scv, i) * dh;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)W::dot(dj, scv, i), dh, inner[i]);
-        }
-        pin(inner);
-        if (cc + 1 < KC) {
-          dj = dj_next;
-          a1 = a2;
-          bq1 = bq2;
-          dhr = dhr_next;
-          scv = scv_next;
-        }
-        // order inside the step: MFMAs, stage copies, LDS reads, the vector epilogue
-        __builtin_amdgcn_sched_group_barrier(0x008, W::kMfma, 0);  // MFMA (next chunk)
-        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);         // VMEM (stage copies)
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);         // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA (q4_K min term)
-        __builtin_amdgcn_sched_group_barrier(0x002, 72, 0);        // VALU
+    for (int h = 0; h < kStagesPerSb; ++h) {
+      const int g = sbi * kStagesPerSb + h;
+      if (g < nstages) {  // uniform per k-group
+        St& st = stage[g & 1];
+        const bool starts_sb = h == 0;
+        // Software pipeline over the KC chunks: step cc issues the MFMA(s) of
+        // chunk cc+1 (operands read one step earlier), then the LDS reads of chunk
+        // cc+2 and of chunk cc+1's activation scale (and q4_K scale bytes), then
+        // the scale epilogue of chunk cc on the vector ALU while the matrix core
+        // works.  Every LDS value is consumed one step after its read, so a wait
+        // for it never waits for the reads just issued.
+        const int sc_off = 16 * (lane >> 5);
+        uint32_t dhr = st.s[wt][0][lane & 31];
+        v4i scv = {};
+        if constexpr (TYPE == QMM_Q4_K) scv = *(const v4i*)(&st.sc[wr][0][sc_off]);
+        typename W::A a0 = W::load(st.a[wr][0], lane);
+        v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
+        typename W::A a1 = W::load(st.a[wr][1], lane);
+        v4i bq1 = *(const v4i*)(st.b[wt][1] + lane * 16);
+        typename W::D dj = W::mma(a0, bq0);
         __builtin_amdgcn_sched_barrier(0);
-      }
-      if (h == kStagesPerSb - 1) {  // end of a super-block: apply its d
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 d4 = *(const float4*)(&st.d[wr][8 * q + 4 * (lane >> 5)]);
-          acc[4 * q + 0] = fmaf(inner[4 * q + 0], d4.x, acc[4 * q + 0]);
-          acc[4 * q + 1] = fmaf(inner[4 * q + 1], d4.y, acc[4 * q + 1]);
-          acc[4 * q + 2] = fmaf(inner[4 * q + 2], d4.z, acc[4 * q + 2]);
-          acc[4 * q + 3] = fmaf(inner[4 * q + 3], d4.w, acc[4 * q + 3]);
+        for (int cc = 0; cc < KC; ++cc) {
+          typename W::D dj_next;
+          if (cc + 1 < KC) {
+            dj_next = W::mma(a1, bq1);
+            W::keep(dj_next);
+          }
+          // stage (g+1)&1 was last read in iteration g-1, which every wave finished
+          // before the barrier that ended it
+          if (g + 1 < nstages) {
+            constexpr int per = (kWaveJobs + KC - 1) / KC;
+#pragma unroll
+            for (int q = 0; q < per; ++q)
+              if (cc * per + q < kWaveJobs) issue_job(g + 1, stage[(g + 1) & 1], cc * per + q);
+          }
+          typename W::A a2;
+          v4i bq2;
+          if (cc + 2 < KC) {
+            a2 = W::load(st.a[wr][cc + 2], lane);
+            bq2 = *(const v4i*)(st.b[wt][cc + 2] + lane * 16);
+          }
+          uint32_t dhr_next = 0;
+          v4i scv_next = {};
+          if (cc + 1 < KC) {
+            dhr_next = st.s[wt][cc + 1][lane & 31];
+            if constexpr (TYPE == QMM_Q4_K) scv_next = *(const v4i*)(&st.sc[wr][cc + 1][sc_off]);
+          }
+          if (TYPE == QMM_Q4_K && (cc & 1)) {
+            const int ck = cc - 1 + (lane >> 5);
+            const float mv = st.m[wr][ck][lane & 31];
+            const float sv = f16_bits_to_float(st.s[wt][ck][lane & 31] >> 16);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(mv, sv, acc, 0, 0, 0);
+          }
+          const float dh = f16_bits_to_float(dhr & 0xFFFF);
+          if (cc == 0 && starts_sb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) inner[i] = (float)W::dot(dj, scv, i) * dh;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)W::dot(dj, scv, i), dh, inner[i]);
+          }
+          pin(inner);
+          if (cc + 1 < KC) {
+            dj = dj_next;
+            a1 = a2;
+            bq1 = bq2;
+            dhr = dhr_next;
+            scv = scv_next;
+          }
+          // order inside the step: MFMAs, stage copies, LDS reads, the vector epilogue
+          __builtin_amdgcn_sched_group_barrier(0x008, W::kMfma, 0);  // MFMA (next chunk)
+          __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);         // VMEM (stage copies)
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);         // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA (q4_K min term)
+          __builtin_amdgcn_sched_group_barrier(0x002, 72, 0);        // VALU
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (h == kStagesPerSb - 1) {  // end of a super-block: apply its d
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 d4 = *(const float4*)(&st.d[wr][8 * q + 4 * (lane >> 5)]);
+            acc[4 * q + 0] = fmaf(inner[4 * q + 0], d4.x, acc[4 * q + 0]);
+            acc[4 * q + 1] = fmaf(inner[4 * q + 1], d4.y, acc[4 * q + 1]);
+            acc[4 * q + 2] = fmaf(inner[4 * q + 2], d4.z, acc[4 * q + 2]);
+            acc[4 * q + 3] = fmaf(inner[4 * q + 3], d4.w, acc[4 * q + 3]);
+          }
         }
       }
+      if (g + 1 < niter) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads for g+1 landed
+        __syncthreads();                                   // everyone's landed; stage g is free
+      }
     }
-    if (g + 1 < niter) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads for g+1 landed
-      __syncthreads();                                   // everyone's landed; stage g is free
-    }
-  }
   }
   if (KS > 1) {  // add k-group 1's partial sums to k-group 0's, in that order
     __syncthreads();  // every wave is done with the stage buffers
