@@ -550,7 +550,9 @@ MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
     // it form the tail
     const int dp_rows = (int)((tiles / slots) * slots / plan.tok_tiles);
     const int n_tail = (plan.row_tiles - dp_rows) * plan.tok_tiles;
-    const int split = (int)std::min<int64_t>(slots / n_tail, p.nsb);
+    // at least one super-block per k-group in every slice (two k-groups in
+    // the few-tile geometry): a k-group without one would only wait
+    const int split = (int)std::min<int64_t>(slots / n_tail, p.nsb / (plan.many ? 1 : 2));
     if (split >= 2) {
       plan.dp_row_tiles = dp_rows;
       plan.n_tail = n_tail;
