@@ -274,6 +274,34 @@ def test_small_all_elements(case):
     check_close(got, ref, A, name)
 
 
+def _random_shapes(n, seed=11):
+    """Seeded random shapes: both types, odd row counts, 1..8 super-blocks; every
+    other case with 2000..4200 tokens so that it takes the many-tile geometry.
+    Small enough for the oracle on every element."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        type_ = synth.Q6_K if (i // 2) % 2 else synth.Q4_K
+        if i % 2:
+            id_ = 256 * int(rng.integers(1, 3))
+            od = int(rng.integers(900, 1500))
+            T = int(rng.integers(2000, 4201))
+        else:
+            id_ = 256 * int(rng.integers(1, 9))
+            od = int(rng.integers(1, 3000))
+            T = int(rng.integers(1, 701))
+        out.append((f"random {synth.TYPE_NAMES[type_]} {od}x{id_} T={T}", type_, od, id_, T, bool(i % 3 == 0)))
+    return out
+
+
+RANDOM = _random_shapes(8)
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_shapes_all_elements(case):
+    test_small_all_elements(case)
+
+
 def _sample_pairs(rng, T, od, n=3000):
     ts = list(rng.integers(0, T, n))
     js = list(rng.integers(0, od, n))
