@@ -57,6 +57,10 @@ WORKLOADS = {
     "ffn_gate_up": _single(synth.C3_GU),
     "head": _single(synth.C4),
     "c1": _single(synth.C1),
+    # one GPU's share of ffn_down under 8-way tensor parallelism: a column slice
+    # (512 of the 4096 rows) and a row slice (6 of the 43 super-blocks of id)
+    "ffn_down_tp8_col": _single(("q6_K ffn_down column shard 512x11008 T=512", synth.Q6_K, 512, 11008, 512, False)),
+    "ffn_down_tp8_row": _single(("q6_K ffn_down row shard 4096x1536 T=512", synth.Q6_K, 4096, 1536, 512, False)),
     "layer": ("LLaMA-7B q4_K_M-style layer, 3314 tokens (q,k,o,gate,up q4_K; v,down q6_K)",
               synth.C5_TOKENS,
               {"attn_in": 4096, "attn_out": 4096, "ffn_in": 4096, "ffn_mid": 11008},

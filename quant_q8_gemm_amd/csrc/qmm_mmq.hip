@@ -542,10 +542,12 @@ MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
   const int64_t tiles = (int64_t)plan.row_tiles * plan.tok_tiles;
   // work-groups resident at once: one per CU (few tiles), four (many tiles)
   const int64_t slots = (int64_t)num_cus * (plan.many ? 4 : 1);
-  // Only after a single full wave: behind several (e.g. 3328 tiles on 1024
+  // Only after at most one full wave: behind several (e.g. 3328 tiles on 1024
   // slots) the tail's work-groups already overlap the last full wave's end, and
-  // the split measured 0.5-1% slower there instead of 9% faster.
-  if (num_cus > 0 && tiles > slots && tiles < 2 * slots) {
+  // the split measured 0.5-1% slower there instead of 9% faster.  With no full
+  // wave (at most half the slots filled, e.g. one GPU's 512-row share of a
+  // layer), every tile is a tail tile.
+  if (num_cus > 0 && tiles != slots && tiles < 2 * slots) {
     // the full wave stays data-parallel (whole row tiles), the row tiles after
     // it form the tail
     const int dp_rows = (int)((tiles / slots) * slots / plan.tok_tiles);

@@ -256,6 +256,8 @@ SMALL = [("C1 q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          # tail tiles are split along K and added by the fixup kernel
          ("q4_K 4160x1024 T=512", synth.Q4_K, 4160, 1024, 512, False),
          ("q6_K 4200x768 T=500", synth.Q6_K, 4200, 768, 500, True),
+         # far fewer tiles than CUs (24): every tile split along K
+         ("q6_K 512x2816 T=300", synth.Q6_K, 512, 2816, 300, False),
          # enough 64 x 64 tiles (>= 1024) to select the many-tile geometry
          ("q6_K 1000x512 T=4100", synth.Q6_K, 1000, 512, 4100, True),
          ("q4_K 1030x256 T=4000", synth.Q4_K, 1030, 256, 4000, False)]
