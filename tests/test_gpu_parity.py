@@ -320,7 +320,10 @@ def _sample_pairs(rng, T, od, n=3000):
 # the one-layer workload at 3314 tokens: its four distinct GEMM shapes
 LAYER = [(f"layer {synth.TYPE_NAMES[t]} {od}x{id_} T={synth.C5_TOKENS}", t, od, id_, synth.C5_TOKENS, False)
          for t, od, id_ in sorted({(t, od, id_) for _, t, od, id_ in synth.C5_LAYER})]
-FULL = [synth.C2, synth.C2_ODD, synth.C3_QKVO, synth.C3_GU, synth.C4] + LAYER
+# one GPU's share of ffn_down under 8-way tensor parallelism (column and row slices)
+SHARDS = [("q6_K ffn_down column shard 512x11008 T=512", synth.Q6_K, 512, 11008, 512, False),
+          ("q6_K ffn_down row shard 4096x1536 T=512", synth.Q6_K, 4096, 1536, 512, False)]
+FULL = [synth.C2, synth.C2_ODD, synth.C3_QKVO, synth.C3_GU, synth.C4] + LAYER + SHARDS
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=[c[0] for c in FULL])
