@@ -57,9 +57,9 @@ namespace qmm {
 // l's bytes land at the LDS byte address held in M0 plus 16*l).  Written out so
 // that a wave-uniform source is addressed as scalar base + the lane's offset;
 // the builtin form lets the compiler turn the source into a per-lane 64-bit
-// induction variable, a few vector instructions per copy.  M0 is set by each
-// copy itself; a kernel uses either these or the builtin, never both, so no
-// compiler-generated M0 value is live across them.
+// induction variable, a few vector instructions per copy (6-9% of the 512-token
+// ffn_down MMQ).  M0 is set by each copy itself; the kernel issues no other
+// instruction that reads M0.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
@@ -300,51 +300,44 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   // LDS writes interleave with the steps' LDS reads instead of stalling them.
   constexpr int kWaveJobs = kRunA + kRunB + 1;
   // One 1 KiB copy job: a wave-uniform source (weight or code fragments) or a
-  // per-lane source (the small region).  The written-out form measured 4-7%
-  // faster for half- and whole-super-block stages and 1-2% slower for quarter
-  // stages (q6_K, many tiles), which keep the builtin.
-  auto copy_uniform = [&](const void* src, void* dst) __attribute__((always_inline)) {
-    if constexpr (KC >= 4)
-      copy16_uniform(uniform_ptr(src), lane_off, __builtin_amdgcn_readfirstlane(lds_addr(dst)));
-    else
-      __builtin_amdgcn_global_load_lds((const uint8_t*)src + lane_off,
-                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-  };
-  auto copy_lane = [&](const void* src, void* dst) __attribute__((always_inline)) {
-    if constexpr (KC >= 4)
-      copy16_lane(src, __builtin_amdgcn_readfirstlane(lds_addr(dst)));
-    else
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-  };
-  auto issue_job = [&](int g, St& st, int j) __attribute__((always_inline)) {
+  // per-lane source (the small region), into stage buffer buf of this k-group.
+  // Sources and LDS destinations are formed from values made scalar once here,
+  // so a copy costs no vector instruction.
+  const uint8_t* const srcA_u = (const uint8_t*)uniform_ptr(srcA);
+  const uint8_t* const srcB_u = (const uint8_t*)uniform_ptr(srcB);
+  const uint32_t lds_k = __builtin_amdgcn_readfirstlane(lds_addr(stage));
+  auto issue_job = [&](int g, int buf, int j) __attribute__((always_inline)) {
+    const uint32_t lds_buf = lds_k + (uint32_t)buf * (uint32_t)sizeof(St);
     if (j < kRunA) {
       if (has_a)
-        copy_uniform(srcA + (size_t)g * KC * kFrag + j * 1024, &st.a[0][0][0] + (ka0 + j) * 1024);
+        copy16_uniform(srcA_u + (size_t)g * KC * kFrag + j * 1024, lane_off,
+                       lds_buf + (uint32_t)__builtin_offsetof(St, a) + (ka0 + j) * 1024);
     } else if (j < kRunA + kRunB) {
       const int u = j - kRunA;
       if (has_b)
-        copy_uniform(srcB + (size_t)g * KC * 1024 + u * 1024, &st.b[0][0][0] + (kb0 + u) * 1024);
+        copy16_uniform(srcB_u + (size_t)g * KC * 1024 + u * 1024, lane_off,
+                       lds_buf + (uint32_t)__builtin_offsetof(St, b) + (kb0 + u) * 1024);
     } else if (wave < St::kSmallJobs) {
-      uint8_t* ls = (uint8_t*)&st.s[0][0][0] + wave * 1024;
+      const uint32_t ls = lds_buf + (uint32_t)__builtin_offsetof(St, s) + wave * 1024;
       const bool ends_sb = ((g + 1) * KC) % 8 == 0;
       if (small_kind == 1)
-        copy_lane(small_src + (size_t)g * KC * 128, ls);
+        copy16_lane(small_src + (size_t)g * KC * 128, ls);
       else if (small_kind == 3)
-        copy_lane(small_src + (size_t)g * KC * 32, ls);
+        copy16_lane(small_src + (size_t)g * KC * 32, ls);
       else if (small_kind == 2 && ends_sb)
-        copy_lane(small_src + (size_t)((g * KC) / 8) * 128, ls);
+        copy16_lane(small_src + (size_t)((g * KC) / 8) * 128, ls);
     }
   };
-  auto issue_stage = [&](int g, St& st) __attribute__((always_inline)) {  // all at once (prologue)
+  auto issue_stage = [&](int g, int buf) __attribute__((always_inline)) {  // all at once (prologue)
 #pragma unroll
-    for (int j = 0; j < kWaveJobs; ++j) issue_job(g, st, j);
+    for (int j = 0; j < kWaveJobs; ++j) issue_job(g, buf, j);
   };
 
   v16f acc, inner;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 
-  if (nstages > 0) issue_stage(0, stage[0]);
+  if (nstages > 0) issue_stage(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -387,7 +380,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
             constexpr int per = (kWaveJobs + KC - 1) / KC;
 #pragma unroll
             for (int q = 0; q < per; ++q)
-              if (cc * per + q < kWaveJobs) issue_job(g + 1, stage[(g + 1) & 1], cc * per + q);
+              if (cc * per + q < kWaveJobs) issue_job(g + 1, (g + 1) & 1, cc * per + q);
           }
           typename W::A a2;
           v4i bq2;
