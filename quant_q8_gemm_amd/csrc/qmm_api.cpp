@@ -32,7 +32,7 @@ std::atomic<size_t> g_held{0};  // device bytes held by live handles
 std::atomic<size_t> g_cap{0};   // 0 = no cap
 
 // Scratch for the MMQ's tail partials: one buffer per (device, stream), of the
-// largest size any call can need on that device (32 KiB per compute unit).
+// largest size any call can need on that device (64 KiB per compute unit).
 // Calls on one stream run in order, so they share it; it lives until the
 // process ends.
 struct Scratch {
@@ -119,21 +119,31 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   const size_t off_wm = off_wd + round_up(qmm::wd_bytes(p.od_pad, id), 256);
   const size_t off_sc = off_wm + round_up(qmm::wm_bytes(type, p.od_pad, id), 256);
   const size_t plane_bytes = off_sc + round_up(qmm::wsc_bytes(type, p.od_pad, id), 256);
+  // reserve the bytes against the cap before allocating, atomically, so that
+  // registrations on several threads cannot overshoot it together; every
+  // failure below gives them back
   const size_t cap = g_cap.load();
-  if (cap != 0 && g_held.load() + plane_bytes > cap)
-    return fail(QMM_ENOMEM, "registration needs %zu device bytes; cap %zu, held %zu", plane_bytes,
-                cap, g_held.load());
+  size_t held = g_held.load();
+  do {
+    if (cap != 0 && held + plane_bytes > cap)
+      return fail(QMM_ENOMEM, "registration needs %zu device bytes; cap %zu, held %zu", plane_bytes,
+                  cap, held);
+  } while (!g_held.compare_exchange_weak(held, held + plane_bytes));
 
   // ---- first HIP call below this line ----
   hipStream_t s = (hipStream_t)stream;
   int device = 0;
   hipError_t e = hipGetDevice(&device);
-  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (e != hipSuccess) {
+    g_held -= plane_bytes;
+    return fail_hip(e, "hipGetDevice");
+  }
   void* alloc = nullptr;
   void* raw = nullptr;
   e = hipMalloc(&alloc, plane_bytes);
   if (e != hipSuccess) {
     (void)hipGetLastError();
+    g_held -= plane_bytes;
     return e == hipErrorOutOfMemory ? fail(QMM_ENOMEM, "hipMalloc(%zu) failed: out of memory", plane_bytes)
                                     : fail_hip(e, "hipMalloc(planes)");
   }
@@ -141,6 +151,7 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   if (e != hipSuccess) {
     (void)hipGetLastError();
     (void)hipFree(alloc);
+    g_held -= plane_bytes;
     return e == hipErrorOutOfMemory ? fail(QMM_ENOMEM, "hipMalloc(%zu) failed: out of memory", nbytes)
                                     : fail_hip(e, "hipMalloc(raw)");
   }
@@ -158,6 +169,7 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   (void)hipFree(raw);
   if (rc != QMM_OK) {
     (void)hipFree(alloc);
+    g_held -= plane_bytes;
     return rc;
   }
   qmm_weights* w = new qmm_weights;
@@ -169,7 +181,6 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   w->wm_offset = type == QMM_Q4_K ? off_wm : plane_bytes;
   w->sc_offset = type == QMM_Q4_K ? off_sc : plane_bytes;
   w->alloc = alloc;
-  g_held += plane_bytes;
   if (getenv("QMM_LOG") != nullptr)
     fprintf(stderr, "qmm: registered %s od=%lld id=%lld od_pad=%lld raw=%zu planes=%zu device=%d\n",
             type == QMM_Q4_K ? "q4_K" : "q6_K", (long long)od, (long long)id,

@@ -85,6 +85,27 @@ def test_memory_cap_fails_before_allocating():
         qmm.set_memory_cap(0)
 
 
+def test_memory_cap_reservation_is_given_back_on_failure():
+    """With the cap at exactly one registration's bytes, two registrations in a
+    row must both get past the cap: a failed one (no GPU here) returns what it
+    reserved, a successful one is released before the next."""
+    qmm.set_memory_cap(1000)
+    try:
+        rc, _ = _reg(qmm.Q6_K, 4, 256, 4 * 210)
+        assert rc == qmm.ENOMEM
+        need = int(re.search(r"needs (\d+) device bytes", qmm.last_error()).group(1))
+        qmm.set_memory_cap(need)
+        for _ in range(2):
+            rc, h = _reg(qmm.Q6_K, 4, 256, 4 * 210)
+            assert rc != qmm.ENOMEM, qmm.last_error()
+            if rc == qmm.OK:
+                qmm._lib.qmm_release_weights(ctypes.c_void_p(h))
+            else:
+                assert rc == qmm.EHIP and h is None
+    finally:
+        qmm.set_memory_cap(0)
+
+
 def test_quantize_rejects_bad_arguments():
     L = qmm._lib
     good = ctypes.c_void_p(4096)
