@@ -79,15 +79,16 @@ constexpr int kFragA = TYPE == QMM_Q6_K ? 2048 : kQ4CodeFrag;
 
 template <int TYPE, int WR, int WT, int KC>
 struct alignas(16) Stage {
-  int8_t a[WR][KC][kFragA<TYPE>];  // weight fragments: [row block][chunk]
-  int8_t b[WT][KC][1024];          // q8 codes: [token block][chunk][fragment]
-  uint32_t s[WT][KC][32];          // (dh, s) pairs: [token block][chunk][token]
-  float m[WR][KC][32];             // -dmin*min: [row block][chunk][row]; q4_K only
-  uint8_t sc[WR][KC][32];          // scale bytes: [row block][chunk][lane half][16]; q4_K only
-  float d[WR][32];                 // super-block d: [row block][row]
+  static constexpr bool kQ4 = TYPE == QMM_Q4_K;
+  int8_t a[WR][KC][kFragA<TYPE>];    // weight fragments: [row block][chunk]
+  int8_t b[WT][KC][1024];            // q8 codes: [token block][chunk][fragment]
+  uint32_t s[WT][KC][32];            // (dh, s) pairs: [token block][chunk][token]
+  float m[kQ4 ? WR : 0][KC][32];     // -dmin*min: [row block][chunk][row]; q4_K only
+  uint8_t sc[kQ4 ? WR : 0][KC][32];  // scale bytes: [row block][chunk][lane half][16]; q4_K only
+  float d[WR][32];                   // super-block d: [row block][row]
   // s, m, sc and d are contiguous: the "small" region, copied in 16-byte units.
-  static constexpr int kUnitsS = WT * KC * 8, kUnitsM = WR * KC * 8, kUnitsSc = WR * KC * 2,
-                       kUnitsD = WR * 8;
+  static constexpr int kUnitsS = WT * KC * 8, kUnitsM = kQ4 ? WR * KC * 8 : 0,
+                       kUnitsSc = kQ4 ? WR * KC * 2 : 0, kUnitsD = WR * 8;
   static constexpr int kSmallJobs = (kUnitsS + kUnitsM + kUnitsSc + kUnitsD + 63) / 64;
 };
 
@@ -209,6 +210,9 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   constexpr int kJobsA = WR * KC * kFragA<TYPE> / 1024, kJobsB = WT * KC;
   static_assert(KC == 2 || KC == 4 || KC == 8, "a stage is a quarter, half or a whole super-block");
   static_assert(KS == 1 || KS == 2, "one or two k-groups");
+  static_assert(__builtin_offsetof(St, d) ==
+                    __builtin_offsetof(St, s) + 16 * (St::kUnitsS + St::kUnitsM + St::kUnitsSc),
+                "the small region is contiguous");
   // k-group 1's sums pass to k-group 0 through k-group 0's two stages
   static_assert(KS == 1 || 2 * sizeof(St) >= (size_t)kWaves * 16 * 64 * 4, "room to combine k-groups");
   __shared__ St stage_all[KS][2];
@@ -510,13 +514,14 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
 //  * 2 x 2 waves (64 x 64 tile), one k-group, for shapes with many tiles:
 //    several work-groups per CU, so one group's barrier wait is covered by the
 //    others.  Four per CU (16 waves) for both types: q4_K with half-super-block
-//    stages (30 KiB of LDS, 108 VGPRs), q6_K with quarter-super-block stages
-//    (27 KiB, 113 VGPRs; half-super-block stages take 53 KiB, which fits only
+//    stages (29 KiB of LDS, 106 VGPRs), q6_K with quarter-super-block stages
+//    (26 KiB, 108 VGPRs; half-super-block stages take 51 KiB, which fits only
 //    three per CU and ran 7-9% slower);
 //  * 2 x 4 waves (64 rows x 128 tokens) in two k-groups (16 waves), half-super-
-//    block stages, about 140 KiB of LDS, one work-group per CU; for shapes with
-//    too few tiles to fill the CUs several times (e.g. 512 tokens x 4096 rows =
-//    256 work-groups), where the second k-group doubles the waves per CU.
+//    block stages, 137 KiB (q6_K) or 94 KiB (q4_K) of LDS, one work-group per
+//    CU; for shapes with too few tiles to fill the CUs several times (e.g. 512
+//    tokens x 4096 rows = 256 work-groups), where the second k-group doubles
+//    the waves per CU.
 // In both, a ragged second wave (tiles = slots + r with r <= slots / 2, the
 // slots being the work-groups resident at once; e.g. 4097 rows x 512 tokens:
 // 264 tiles on 256 CUs, 11008 rows x 512 tokens: 1376 tiles on 1024 slots) is
