@@ -39,7 +39,7 @@ hipError_t launch_quantize(const float* x, int64_t n_tok, int64_t t_pad, int64_t
 // MMQ launch plan: tile geometry, and for a ragged last wave the K split of the
 // tail tiles and the scratch they need (n_tail tiles x split partials).
 struct MmqPlan {
-  bool many;          // many tiles: 64 x 64 tiles, else 64 x 128 tiles in two k-groups
+  bool many;          // many tiles: the many-tile shapes, else 64 x 128 tiles in two k-groups
   int row_tiles, tok_tiles;
   int dp_row_tiles;   // row tiles computed whole
   int n_tail;         // tiles after them, each split along K

@@ -197,7 +197,7 @@ __device__ __forceinline__ void store_block(float* __restrict__ out, const v16f&
 // tail is whole row tiles at the end, so the rows before it keep exactly the
 // summation order they have without a tail.
 template <int TYPE, int WR, int WT, int KC, int KS>
-__global__ void __launch_bounds__(64 * WR * WT * KS, (WR * WT * KS == 4) ? 4 : 1)
+__global__ void __launch_bounds__(64 * WR * WT * KS, 16 / (WR * WT * KS))
 mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
            const float* __restrict__ wm, const uint8_t* __restrict__ wsc,
            const uint8_t* __restrict__ qq,
@@ -510,36 +510,60 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
   return hipGetLastError();
 }
 
-// Tile geometry per launch.  Two shapes of the same kernel:
-//  * 2 x 2 waves (64 x 64 tile), one k-group, for shapes with many tiles:
-//    several work-groups per CU, so one group's barrier wait is covered by the
-//    others.  Four per CU (16 waves) for both types: q4_K with half-super-block
-//    stages (29 KiB of LDS, 106 VGPRs), q6_K with quarter-super-block stages
-//    (26 KiB, 108 VGPRs; half-super-block stages take 51 KiB, which fits only
-//    three per CU and ran 7-9% slower);
-//  * 2 x 4 waves (64 rows x 128 tokens) in two k-groups (16 waves), half-super-
-//    block stages, 137 KiB (q6_K) or 94 KiB (q4_K) of LDS, one work-group per
-//    CU; for shapes with too few tiles to fill the CUs several times (e.g. 512
-//    tokens x 4096 rows = 256 work-groups), where the second k-group doubles
-//    the waves per CU.
-// In both, a ragged second wave (tiles = slots + r with r <= slots / 2, the
+// Tile geometry per launch (16 waves per CU in every shape):
+//  * many tiles (at least four 64 x 64 tiles per CU, e.g. the 3314-token layer,
+//    the 2048-token head): several work-groups per CU, so one group's barrier
+//    wait is covered by the others.  q4_K: 2 x 2 waves (64 x 64 tiles), four
+//    per CU, half-super-block stages (29 KiB of LDS, 106 VGPRs).  q6_K: 2 x 4
+//    waves (64 rows x 128 tokens), two per CU, half-super-block stages (69 KiB,
+//    124 VGPRs): each weight fragment a work-group copies serves four waves
+//    instead of two, a third fewer copied bytes per output block, which is
+//    what q6_K's 2-byte weights are short of (3-8% faster than 2 x 2 waves with
+//    quarter stages; 4 x 4 and 4 x 2 waves were slower, and the 2 x 4 shape
+//    was 4-9% slower for q4_K, whose copies are a quarter the size);
+//  * few tiles (e.g. 512 tokens x 4096 rows = 256 64 x 128 tiles): 2 x 4 waves
+//    (64 rows x 128 tokens) in two k-groups, half-super-block stages, 137 KiB
+//    (q6_K) or 94 KiB (q4_K) of LDS, one work-group per CU; the second k-group
+//    doubles the waves per CU.
+// In all, a ragged second wave (tiles = slots + r with r <= slots / 2, the
 // slots being the work-groups resident at once; e.g. 4097 rows x 512 tokens:
 // 264 tiles on 256 CUs, 11008 rows x 512 tokens: 1376 tiles on 1024 slots) is
 // split along K.
 // The switch point (about four 64 x 64 tiles per CU) was chosen by timing both
 // on the 512-token shapes, the 3314-token layer shapes and the 2048-token head.
+namespace {
+// One launch shape: WR x WT waves per k-group, KS k-groups, stages of KC chunks,
+// per_cu work-groups resident per CU (16 waves per CU in every shape).
+struct Geometry {
+  int wr, wt, ks, kc, per_cu;
+};
+constexpr Geometry kQ6Many{2, 4, 1, 4, 2};
+constexpr Geometry kQ4Many{2, 2, 1, 4, 4};
+constexpr Geometry kFew{2, 4, 2, 4, 1};
+// a tail slice's partial tile fits the scratch's 64 KiB per CU in every shape
+constexpr bool scratch_fits(const Geometry& g) {
+  return g.per_cu * (32 * g.wr) * (32 * g.wt) * 4 <= 64 * 1024;
+}
+static_assert(scratch_fits(kQ6Many) && scratch_fits(kQ4Many) && scratch_fits(kFew), "scratch per CU");
+constexpr bool sixteen_waves(const Geometry& g) { return g.per_cu * g.wr * g.wt * g.ks == 16; }
+static_assert(sixteen_waves(kQ6Many) && sixteen_waves(kQ4Many) && sixteen_waves(kFew), "16 waves per CU");
+Geometry geometry(int type, bool many) {
+  return !many ? kFew : type == QMM_Q6_K ? kQ6Many : kQ4Many;
+}
+}  // namespace
+
 MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
   MmqPlan plan{};
   const int64_t small_tiles = (p.od_pad / 64) * ((n_tok + 63) / 64);
   plan.many = small_tiles >= 4 * 256;
-  const int wt = plan.many ? 2 : 4;
-  plan.row_tiles = (int)(p.od_pad / 64);
-  plan.tok_tiles = (int)((n_tok + 32 * wt - 1) / (32 * wt));
+  const Geometry g = geometry(p.type, plan.many);
+  plan.row_tiles = (int)(p.od_pad / (32 * g.wr));
+  plan.tok_tiles = (int)((n_tok + 32 * g.wt - 1) / (32 * g.wt));
   plan.dp_row_tiles = plan.row_tiles;
   plan.split = 1;
   const int64_t tiles = (int64_t)plan.row_tiles * plan.tok_tiles;
-  // work-groups resident at once: one per CU (few tiles), four (many tiles)
-  const int64_t slots = (int64_t)num_cus * (plan.many ? 4 : 1);
+  // work-groups resident at once
+  const int64_t slots = (int64_t)num_cus * g.per_cu;
   // Only after at most one full wave: behind several (e.g. 3328 tiles on 1024
   // slots) the tail's work-groups already overlap the last full wave's end, and
   // the split measured 0.5-1% slower there instead of 9% faster.  With no full
@@ -550,30 +574,35 @@ MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
     // it form the tail
     const int dp_rows = (int)((tiles / slots) * slots / plan.tok_tiles);
     const int n_tail = (plan.row_tiles - dp_rows) * plan.tok_tiles;
-    // at least one super-block per k-group in every slice (two k-groups in
-    // the few-tile geometry): a k-group without one would only wait
-    const int split = (int)std::min<int64_t>(slots / n_tail, p.nsb / (plan.many ? 1 : 2));
+    // at least one super-block per k-group in every slice: a k-group without
+    // one would only wait
+    const int split = (int)std::min<int64_t>(slots / n_tail, p.nsb / g.ks);
     if (split >= 2) {
       plan.dp_row_tiles = dp_rows;
       plan.n_tail = n_tail;
       plan.split = split;
-      plan.scratch_bytes = (size_t)n_tail * split * (64 * 32 * wt) * sizeof(float);
+      plan.scratch_bytes = (size_t)n_tail * split * (32 * g.wr) * (32 * g.wt) * sizeof(float);
     }
   }
   return plan;
 }
 
-// n_tail * split work-groups, at most one per slot: num_cus 64 x 128 partial
-// tiles or 4 * num_cus 64 x 64 ones.
-size_t mmq_scratch_max_bytes(int num_cus) { return (size_t)num_cus * (64 * 256) * sizeof(float); }
+// n_tail * split work-groups, at most one per slot, each with one partial tile:
+// at most 64 KiB per CU in every shape (scratch_fits).
+size_t mmq_scratch_max_bytes(int num_cus) { return (size_t)num_cus * 64 * 1024; }
 
 hipError_t launch_mmq(const Planes& p, const MmqPlan& plan, const uint8_t* qact, int64_t n_tok,
                       int64_t t_pad, float* out, float* scratch, hipStream_t s) {
+  constexpr Geometry q6 = kQ6Many, q4 = kQ4Many, f = kFew;
   if (p.type == QMM_Q6_K)
-    return plan.many ? launch_tiled<QMM_Q6_K, 2, 2, 2, 1>(p, plan, qact, n_tok, t_pad, out, scratch, s)
-                     : launch_tiled<QMM_Q6_K, 2, 4, 4, 2>(p, plan, qact, n_tok, t_pad, out, scratch, s);
-  return plan.many ? launch_tiled<QMM_Q4_K, 2, 2, 4, 1>(p, plan, qact, n_tok, t_pad, out, scratch, s)
-                   : launch_tiled<QMM_Q4_K, 2, 4, 4, 2>(p, plan, qact, n_tok, t_pad, out, scratch, s);
+    return plan.many ? launch_tiled<QMM_Q6_K, q6.wr, q6.wt, q6.kc, q6.ks>(p, plan, qact, n_tok, t_pad, out,
+                                                                         scratch, s)
+                     : launch_tiled<QMM_Q6_K, f.wr, f.wt, f.kc, f.ks>(p, plan, qact, n_tok, t_pad, out,
+                                                                     scratch, s);
+  return plan.many ? launch_tiled<QMM_Q4_K, q4.wr, q4.wt, q4.kc, q4.ks>(p, plan, qact, n_tok, t_pad, out,
+                                                                       scratch, s)
+                   : launch_tiled<QMM_Q4_K, f.wr, f.wt, f.kc, f.ks>(p, plan, qact, n_tok, t_pad, out, scratch,
+                                                                   s);
 }
 
 }  // namespace qmm

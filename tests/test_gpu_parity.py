@@ -258,8 +258,11 @@ SMALL = [("C1 q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          ("q6_K 4200x768 T=500", synth.Q6_K, 4200, 768, 500, True),
          # far fewer tiles than CUs (24): every tile split along K
          ("q6_K 512x2816 T=300", synth.Q6_K, 512, 2816, 300, False),
-         # enough 64 x 64 tiles (>= 1024) to select the many-tile geometry
+         # enough 64 x 64 tiles (>= 1024) to select the many-tile geometry;
+         # q6_K there runs 64 x 128 tiles two per CU: 528 tiles on 512 slots
+         # (a split tail), and 1088 tiles (two full waves and a ragged third)
          ("q6_K 1000x512 T=4100", synth.Q6_K, 1000, 512, 4100, True),
+         ("q6_K 2100x256 T=4000", synth.Q6_K, 2100, 256, 4000, False),
          ("q4_K 1030x256 T=4000", synth.Q4_K, 1030, 256, 4000, False)]
 
 
