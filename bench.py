@@ -16,8 +16,9 @@ second pass of K steps (so the timed steps carry nothing but the kernels); each
 kernel's time alone (K back-to-back launches between two events, a third pass);
 the MMQs with the weights cold (a fourth pass rotating over
 copies of the weights whose planes together exceed the 256 MB last-level
-cache), and the CPU oracle timed on the host as a reference (all host threads,
-and one thread).
+cache); the measured roofs (the int8 MFMA rate and the vector-ALU rate of the
+scale epilogue on calibration kernels, with the shader clock); and the CPU
+oracle timed on the host as a reference (all host threads, and one thread).
 """
 from __future__ import annotations
 
@@ -100,6 +101,8 @@ def _parse():
     ap.add_argument("--workload", default="ffn_down", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-weights pass")
+    ap.add_argument("--no-calib", action="store_true",
+                    help="skip the measured MFMA and epilogue roofs (calibration kernels)")
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--cpu-macs", type=float, default=2.4e10,
                     help="multiply-accumulates of the oracle sample (about 20 s of CPU work)")
@@ -122,6 +125,58 @@ def measured_traffic(workload: str):
         return None
     w = rec.get("workloads", {}).get(workload)
     return None if w is None else w.get("bytes_per_step")
+
+
+def calibrate(torch, stream):
+    """Measured roofs on this GPU: the int8 MFMA rate and the vector-ALU rate of
+    the MMQ's scale epilogue (3 instructions per (token, row, 32-block), 64 int8
+    ops each), from the calibration kernels in libqmm_peak.so, with the shader
+    clock (s_memtime against the 100 MHz s_memrealtime) during each run.  Each
+    is the best over a few occupancies, timed with HIP events on `stream`."""
+    import ctypes
+    path = os.path.join(ROOT, "quant_q8_gemm_amd", "libqmm_peak.so")
+    lib = ctypes.CDLL(path)
+    lib.qmm_peak_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    sink = torch.empty(8 * n_cu * 256, dtype=torch.int32, device="cuda")
+    out = {}
+    # kind, name, work-groups per CU tried, SIMD cycles per wave-iteration, int8 ops per wave-iteration
+    for kind, name, per_cu, cyc, ops_it in ((0, "mfma_i8", (1, 2, 3), 128, 4 * 65536),
+                                            (1, "epilogue_valu", (2, 4, 8), 192, 65536)):
+        best = None
+        for g in per_cu:
+            grid = g * n_cu
+            iters = int(8e6 / (g * cyc))  # ~4 ms per launch
+            def launch():
+                rc = lib.qmm_peak_launch(kind, iters, grid, ctypes.c_void_p(clk.data_ptr()),
+                                         ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+                if rc != 0:
+                    raise RuntimeError(f"qmm_peak_launch({kind}) failed: hipError {rc}")
+            launch()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            times = []
+            for _ in range(3):
+                e[0].record(stream)
+                launch()
+                e[1].record(stream)
+                torch.cuda.synchronize()
+                times.append(e[0].elapsed_time(e[1]) / 1e3)
+            t = float(np.median(times))
+            cycles, ticks = (int(v) for v in clk.cpu())
+            tops = grid * 4 * iters * ops_it / t / 1e12
+            rec = {"tops": round(tops, 1), "work_groups_per_cu": g, "ms": round(t * 1e3, 3),
+                   "clock_ghz": round(cycles / (ticks / 100e6) / 1e9, 3) if ticks > 0 else None}
+            if best is None or tops > best["tops"]:
+                best = rec
+        out[name] = best
+    mf = out["mfma_i8"]
+    mf["pct_of_spec"] = round(100 * mf["tops"] / MFMA_INT8_PEAK_TOPS, 1)
+    if mf["clock_ghz"]:
+        # 8192 int8 ops per clock per CU (4 SIMDs x 32x32x32 MAC x 2 / 32 cycles)
+        mf["spec_at_clock_tops"] = round(n_cu * mf["clock_ghz"] * 1e9 * 8192 / 1e12, 1)
+    return out
 
 
 def cpu_baseline(gemms, raws, xs, T, threads, macs_target):
@@ -363,6 +418,14 @@ def main():
         "plane_bytes": sum(w.plane_bytes for w in weights.values()),
         "raw_weight_bytes": sum(w.raw_bytes for w in weights.values()),
     }
+    if not args.no_calib:
+        cal = calibrate(torch, stream)
+        result["calibration"] = cal
+        rl = result["roofline"]
+        rl["measured_peak"] = cal["mfma_i8"]["tops"]
+        rl["frac_of_measured_peak"] = round(mmq_tops / cal["mfma_i8"]["tops"], 4)
+        rl["epilogue_roof"]["measured"] = cal["epilogue_valu"]["tops"]
+        rl["epilogue_roof"]["frac_of_measured"] = round(mmq_tops / cal["epilogue_valu"]["tops"], 4)
     if not args.no_cpu:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         result["cpu_baseline"] = cpu_baseline(gemms, raws, xs, T, threads, args.cpu_macs)

@@ -10,6 +10,9 @@ CSRC = os.path.join(HERE, "csrc")
 KERNELS = ["qmm_repack.hip", "qmm_prepass.hip", "qmm_mmq.hip"]
 SOURCES = [os.path.join(CSRC, "qmm_api.cpp")] + [os.path.join(CSRC, k) for k in KERNELS]
 LIB = os.path.join(HERE, "libqmm.so")
+# calibration kernels for the benchmark's measured rooflines (not part of the ABI)
+PEAK_SRC = os.path.join(CSRC, "qmm_peak.hip")
+PEAK_LIB = os.path.join(HERE, "libqmm_peak.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-FP32 VALU forms are disabled for the device code on purpose (the host
@@ -18,9 +21,9 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def build(verbose: bool = False) -> str:
+def _hipcc(sources, out: str, verbose: bool) -> str:
     cmd = [HIPCC, *DEVICE_FLAGS, "-fPIC", "-shared", "-Wall", "-I", os.path.join(ROOT, "include"),
-           *SOURCES, "-o", LIB + ".tmp"]
+           *sources, "-o", out + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln and ln.strip()]
@@ -28,7 +31,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    _hipcc(SOURCES, LIB, verbose)
+    _hipcc([PEAK_SRC], PEAK_LIB, verbose)
     return LIB
 
 
@@ -36,7 +45,7 @@ def device_asm(out_path: str) -> str:
     """gfx950 assembly of all kernels (for inspection: instruction mix, VGPRs,
     scratch), concatenated into out_path."""
     parts = []
-    for k in KERNELS:
+    for k in KERNELS + ["qmm_peak.hip"]:
         tmp = out_path + "." + k + ".s"
         cmd = [HIPCC, *DEVICE_FLAGS, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"),
                os.path.join(CSRC, k), "-o", tmp]

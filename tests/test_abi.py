@@ -142,3 +142,18 @@ def test_info_struct_matches_header():
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     names = re.findall(r"(\w+)\s*;", body)
     assert names == [f[0] for f in qmm.Info._fields_]
+
+
+def test_calibration_library_loads_and_validates():
+    """The benchmark's calibration kernels (measured MFMA and epilogue roofs)
+    live in their own library; invalid arguments are refused before any HIP
+    call (hipErrorInvalidValue = 1)."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "quant_q8_gemm_amd", "libqmm_peak.so"))
+    f = lib.qmm_peak_launch
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    good = ctypes.c_void_p(4096)
+    assert f(2, 10, 1, good, good, None) == 1
+    assert f(0, 0, 1, good, good, None) == 1
+    assert f(1, 10, 0, good, good, None) == 1
+    assert f(0, 10, 1, None, good, None) == 1
