@@ -76,7 +76,8 @@ typedef struct {
     size_t raw_bytes;    /* od * (id/256) * (144 or 210): the k-quant bytes */
     size_t plane_bytes;  /* device memory the handle holds */
     size_t wd_offset;    /* byte offset of the d plane inside the planes */
-    size_t wm_offset;    /* byte offset of the -dmin*min plane (q4_K; else == plane_bytes) */
+    size_t mn_offset;    /* byte offset of the min plane (q4_K; else == plane_bytes) */
+    size_t dm_offset;    /* byte offset of the dmin plane (q4_K; else == plane_bytes) */
     size_t sc_offset;    /* byte offset of the scale-byte plane (q4_K; else == plane_bytes) */
 } qmm_info;
 
@@ -119,7 +120,10 @@ int qmm_weights_info(const qmm_weights *w, qmm_info *out);
  *                 (j/32*nchunk + k/32)*512 + h*256 + (j%32)*8 + b, the low
  *                 nibble if k%16 < 8, else the high nibble
  *   at wd_offset  f32 [R][nsb][32]: d of (row, super-block)
- *   at wm_offset  f32 [R][nchunk][32]: -(dmin * min) of (row, chunk), q4_K only
+ *   at mn_offset  binary16 [R][nsb][32][8]: the 6-bit min of (row j, chunk c)
+ *                 as an f16 integer, q4_K only, at element
+ *                 ((j/32*nsb + c/8)*32 + j%32)*8 + c%8
+ *   at dm_offset  f32 [R][nsb][32]: dmin of (row, super-block), q4_K only
  *   at sc_offset  uint8 [R][nchunk][32]: the 6-bit scale of (row j, chunk c),
  *                 q4_K only, at byte (j/32*nchunk + c)*32 + 16*((j/4)%2)
  *                 + 4*((j%32)/8) + j%4

@@ -20,7 +20,8 @@ struct qmm_weights {
   size_t raw_bytes;
   size_t plane_bytes;
   size_t wd_offset;
-  size_t wm_offset;
+  size_t mn_offset;
+  size_t dm_offset;
   size_t sc_offset;
   void* alloc;  // one device allocation holding every plane
 };
@@ -116,8 +117,9 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   p.nsb = id / 256;
   p.nchunk = id / 32;
   const size_t off_wd = round_up(qmm::wq_bytes(type, p.od_pad, id), 256);
-  const size_t off_wm = off_wd + round_up(qmm::wd_bytes(p.od_pad, id), 256);
-  const size_t off_sc = off_wm + round_up(qmm::wm_bytes(type, p.od_pad, id), 256);
+  const size_t off_mn = off_wd + round_up(qmm::wd_bytes(p.od_pad, id), 256);
+  const size_t off_dm = off_mn + round_up(qmm::wmn_bytes(type, p.od_pad, id), 256);
+  const size_t off_sc = off_dm + round_up(qmm::wdm_bytes(type, p.od_pad, id), 256);
   const size_t plane_bytes = off_sc + round_up(qmm::wsc_bytes(type, p.od_pad, id), 256);
   // reserve the bytes against the cap before allocating, atomically, so that
   // registrations on several threads cannot overshoot it together; every
@@ -157,7 +159,8 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   }
   p.wq = (int8_t*)alloc;
   p.wd = (float*)((char*)alloc + off_wd);
-  p.wm = type == QMM_Q4_K ? (float*)((char*)alloc + off_wm) : nullptr;
+  p.wmn = type == QMM_Q4_K ? (uint16_t*)((char*)alloc + off_mn) : nullptr;
+  p.wdm = type == QMM_Q4_K ? (float*)((char*)alloc + off_dm) : nullptr;
   p.wsc = type == QMM_Q4_K ? (uint8_t*)alloc + off_sc : nullptr;
   int rc = QMM_OK;
   if ((e = hipMemcpyAsync(raw, host_bytes, nbytes, hipMemcpyHostToDevice, s)) != hipSuccess)
@@ -178,7 +181,8 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   w->raw_bytes = nbytes;
   w->plane_bytes = plane_bytes;
   w->wd_offset = off_wd;
-  w->wm_offset = type == QMM_Q4_K ? off_wm : plane_bytes;
+  w->mn_offset = type == QMM_Q4_K ? off_mn : plane_bytes;
+  w->dm_offset = type == QMM_Q4_K ? off_dm : plane_bytes;
   w->sc_offset = type == QMM_Q4_K ? off_sc : plane_bytes;
   w->alloc = alloc;
   if (getenv("QMM_LOG") != nullptr)
@@ -199,7 +203,8 @@ int qmm_weights_info(const qmm_weights* w, qmm_info* out) {
   out->raw_bytes = w->raw_bytes;
   out->plane_bytes = w->plane_bytes;
   out->wd_offset = w->wd_offset;
-  out->wm_offset = w->wm_offset;
+  out->mn_offset = w->mn_offset;
+  out->dm_offset = w->dm_offset;
   out->sc_offset = w->sc_offset;
   ok();
   return QMM_OK;
@@ -277,10 +282,12 @@ int qmm_mmq(const qmm_weights* w, const void* qact, size_t qact_bytes, int64_t n
       if (sc.device == device && sc.stream == s) scratch = sc.ptr;
     if (scratch == nullptr) {
       e = hipMalloc(&scratch, max_bytes);
-      if (e != hipSuccess)
+      if (e != hipSuccess) {
+        (void)hipGetLastError();  // leave no sticky error for the caller's next HIP call
         return e == hipErrorOutOfMemory
                    ? fail(QMM_ENOMEM, "hipMalloc(%zu) for the tail partials failed", max_bytes)
                    : fail_hip(e, "hipMalloc(tail partials)");
+      }
       g_scratch.push_back({device, s, scratch});
     }
   }

@@ -18,7 +18,8 @@ struct Planes {
   int64_t nchunk;    // id / 32
   int8_t* wq;        // weight fragments in MFMA order: q6_K folded hi/lo, q4_K packed codes
   float* wd;         // d per (row, super-block)
-  float* wm;         // -dmin*min per (row, chunk); q4_K only, else nullptr
+  uint16_t* wmn;     // min per (row, chunk) as f16, super-block-major; q4_K only, else nullptr
+  float* wdm;        // dmin per (row, super-block); q4_K only, else nullptr
   uint8_t* wsc;      // 6-bit scale per (row, chunk) as bytes; q4_K only, else nullptr
 };
 
@@ -29,7 +30,8 @@ constexpr int kQ4CodeFrag = 512; // q4_K code bytes per (32-row block, chunk): t
 // Byte sizes of the planes for a shape (all offsets 256-byte aligned).
 size_t wq_bytes(int type, int64_t od_pad, int64_t id);
 size_t wd_bytes(int64_t od_pad, int64_t id);
-size_t wm_bytes(int type, int64_t od_pad, int64_t id);
+size_t wmn_bytes(int type, int64_t od_pad, int64_t id);
+size_t wdm_bytes(int type, int64_t od_pad, int64_t id);
 size_t wsc_bytes(int type, int64_t od_pad, int64_t id);
 
 // Kernel launchers: return the hipGetLastError() after the launch.

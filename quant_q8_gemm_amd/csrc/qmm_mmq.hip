@@ -20,8 +20,10 @@
 //  * planes are stored in MFMA fragment order, so every lane's operand is one
 //    contiguous 16-byte (q4_K codes: 8-byte) load and a wave's load is one
 //    contiguous 1 KiB (512 bytes);
-//  * the q4_K min term sum_c dmin*min_c*s_c is a true small matrix product over
-//    chunks; it runs on the f32 MFMA (32x32x2) instead of the vector ALU.
+//  * the q4_K min term sum_c dmin*min_c*s_c is a small matrix product over
+//    chunks: per super-block, sum_c min_c*s_c on one f16 MFMA (32x32x8; the
+//    6-bit mins and the f16 scaled sums are exact f16 operands), times dmin
+//    once per super-block, like d.
 #include "qmm_internal.h"
 #include "qmm_common.h"
 
@@ -83,13 +85,16 @@ struct alignas(16) Stage {
   int8_t a[WR][KC][kFragA<TYPE>];    // weight fragments: [row block][chunk]
   int8_t b[WT][KC][1024];            // q8 codes: [token block][chunk][fragment]
   uint32_t s[WT][KC][32];            // (dh, s) pairs: [token block][chunk][token]
-  float m[kQ4 ? WR : 0][KC][32];     // -dmin*min: [row block][chunk][row]; q4_K only
   uint8_t sc[kQ4 ? WR : 0][KC][32];  // scale bytes: [row block][chunk][lane half][16]; q4_K only
   float d[WR][32];                   // super-block d: [row block][row]
-  // s, m, sc and d are contiguous: the "small" region, copied in 16-byte units.
-  static constexpr int kUnitsS = WT * KC * 8, kUnitsM = kQ4 ? WR * KC * 8 : 0,
-                       kUnitsSc = kQ4 ? WR * KC * 2 : 0, kUnitsD = WR * 8;
-  static constexpr int kSmallJobs = (kUnitsS + kUnitsM + kUnitsSc + kUnitsD + 63) / 64;
+  uint16_t mn[kQ4 ? WR : 0][32][8];  // super-block mins as f16: [row block][row][chunk]; q4_K only
+  float dm[kQ4 ? WR : 0][32];        // super-block dmin: [row block][row]; q4_K only
+  // s, sc, d, mn and dm are contiguous: the "small" region, copied in 16-byte
+  // units (s and sc with every stage, d, mn and dm with a super-block's last).
+  static constexpr int kUnitsS = WT * KC * 8, kUnitsSc = kQ4 ? WR * KC * 2 : 0, kUnitsD = WR * 8,
+                       kUnitsMn = kQ4 ? WR * 32 : 0, kUnitsDm = kQ4 ? WR * 8 : 0;
+  static constexpr int kUnits = kUnitsS + kUnitsSc + kUnitsD + kUnitsMn + kUnitsDm;
+  static constexpr int kSmallJobs = (kUnits + 63) / 64;
 };
 
 // The weight side of one chunk: the MFMA operand(s) read from a stage, the
@@ -199,7 +204,7 @@ __device__ __forceinline__ void store_block(float* __restrict__ out, const v16f&
 template <int TYPE, int WR, int WT, int KC, int KS>
 __global__ void __launch_bounds__(64 * WR * WT * KS, 16 / (WR * WT * KS))
 mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
-           const float* __restrict__ wm, const uint8_t* __restrict__ wsc,
+           const uint8_t* __restrict__ wmn, const float* __restrict__ wdm, const uint8_t* __restrict__ wsc,
            const uint8_t* __restrict__ qq,
            const uint8_t* __restrict__ qs, int nchunk, int nsb, int od, int n_tok,
            int tok_tiles, int dp_row_tiles, int split, int vec_store, float* __restrict__ out,
@@ -210,9 +215,11 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   constexpr int kJobsA = WR * KC * kFragA<TYPE> / 1024, kJobsB = WT * KC;
   static_assert(KC == 2 || KC == 4 || KC == 8, "a stage is a quarter, half or a whole super-block");
   static_assert(KS == 1 || KS == 2, "one or two k-groups");
-  static_assert(__builtin_offsetof(St, d) ==
-                    __builtin_offsetof(St, s) + 16 * (St::kUnitsS + St::kUnitsM + St::kUnitsSc),
-                "the small region is contiguous");
+  static_assert(__builtin_offsetof(St, d) == __builtin_offsetof(St, s) + 16 * (St::kUnitsS + St::kUnitsSc) &&
+                    sizeof(St) == __builtin_offsetof(St, s) + 16 * St::kUnits,
+                "the small region is contiguous and ends the stage");
+  // the q4_K min term collects a super-block's 8 chunks over two stages
+  static_assert(TYPE == QMM_Q6_K || KC == 4, "q4_K stages are half super-blocks");
   // k-group 1's sums pass to k-group 0 through k-group 0's two stages
   static_assert(KS == 1 || 2 * sizeof(St) >= (size_t)kWaves * 16 * 64 * 4, "room to combine k-groups");
   __shared__ St stage_all[KS][2];
@@ -271,29 +278,31 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
                         (size_t)gbeg * KC * 1024;
   const uint32_t lane_off = (uint32_t)lane * 16;
   const uint8_t* small_src = nullptr;
-  int small_kind = 0;  // 0 none, 1 pairs/mins (per stage), 2 d (per super-block), 3 scale bytes (per stage)
+  // 0 none; per stage: 1 pairs (128 bytes per chunk), 3 scale bytes (32 per
+  // chunk); per super-block: 2 d or dmin (128 bytes), 4 mins (512 bytes)
+  int small_kind = 0;
   if (wave < St::kSmallJobs) {
     const int u = wave * 64 + lane;
+    const int sb0g = gbeg / kStagesPerSb;
+    constexpr int eSc = St::kUnitsS + St::kUnitsSc, eD = eSc + St::kUnitsD, eMn = eD + St::kUnitsMn;
     if (u < St::kUnitsS) {
       small_src = qs + ((size_t)(tb0 + u / (KC * 8)) * nchunk + gbeg * KC) * 128 + (u % (KC * 8)) * 16;
       small_kind = 1;
-    } else if (u < St::kUnitsS + St::kUnitsM) {
-      if (TYPE == QMM_Q4_K) {
-        const int v = u - St::kUnitsS;
-        small_src = (const uint8_t*)wm + ((size_t)(rb0 + v / (KC * 8)) * nchunk + gbeg * KC) * 128 +
-                    (v % (KC * 8)) * 16;
-        small_kind = 1;
-      }
-    } else if (u < St::kUnitsS + St::kUnitsM + St::kUnitsSc) {
-      if (TYPE == QMM_Q4_K) {
-        const int v = u - St::kUnitsS - St::kUnitsM;
-        small_src = wsc + ((size_t)(rb0 + v / (KC * 2)) * nchunk + gbeg * KC) * 32 + (v % (KC * 2)) * 16;
-        small_kind = 3;
-      }
-    } else if (u < St::kUnitsS + St::kUnitsM + St::kUnitsSc + St::kUnitsD) {
-      const int v = u - St::kUnitsS - St::kUnitsM - St::kUnitsSc;
-      small_src = (const uint8_t*)wd + ((size_t)(rb0 + v / 8) * nsb + gbeg / kStagesPerSb) * 128 +
-                  (v % 8) * 16;
+    } else if (u < eSc) {
+      const int v = u - St::kUnitsS;
+      small_src = wsc + ((size_t)(rb0 + v / (KC * 2)) * nchunk + gbeg * KC) * 32 + (v % (KC * 2)) * 16;
+      small_kind = 3;
+    } else if (u < eD) {
+      const int v = u - eSc;
+      small_src = (const uint8_t*)wd + ((size_t)(rb0 + v / 8) * nsb + sb0g) * 128 + (v % 8) * 16;
+      small_kind = 2;
+    } else if (u < eMn) {
+      const int v = u - eD;
+      small_src = wmn + ((size_t)(rb0 + v / 32) * nsb + sb0g) * 512 + (v % 32) * 16;
+      small_kind = 4;
+    } else if (u < St::kUnits) {
+      const int v = u - eMn;
+      small_src = (const uint8_t*)wdm + ((size_t)(rb0 + v / 8) * nsb + sb0g) * 128 + (v % 8) * 16;
       small_kind = 2;
     }
   }
@@ -330,6 +339,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         copy16_lane(small_src + (size_t)g * KC * 32, ls);
       else if (small_kind == 2 && ends_sb)
         copy16_lane(small_src + (size_t)((g * KC) / 8) * 128, ls);
+      else if (small_kind == 4 && ends_sb)
+        copy16_lane(small_src + (size_t)((g * KC) / 8) * 512, ls);
     }
   };
   auto issue_stage = [&](int g, int buf) __attribute__((always_inline)) {  // all at once (prologue)
@@ -337,9 +348,17 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
     for (int j = 0; j < kWaveJobs; ++j) issue_job(g, buf, j);
   };
 
-  v16f acc, inner;
+  v16f acc, inner, cm;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  // q4_K min term of a super-block, sum over its chunks c of min(row, c) * s(token, c),
+  // on one f16 MFMA (32x32x8) at its end: both operands are exact in f16 (6-bit
+  // integer mins, the f16 scaled sums) and so are their products in f32.  Lane
+  // half hh supplies chunks 4*hh..4*hh+3: the mins from the super-block's mins
+  // region, the scaled sums (bs) collected from the chunks' scale pairs as
+  // they pass, half hh of the lanes during the super-block's stage hh.
+  v2i bs = {};
+  const bool lane_hi = lane >= 32;
 
   if (nstages > 0) issue_stage(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -362,7 +381,10 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         // works.  Every LDS value is consumed one step after its read, so a wait
         // for it never waits for the reads just issued.
         const int sc_off = 16 * (lane >> 5);
-        uint32_t dhr = st.s[wt][0][lane & 31];
+        uint32_t dhr = st.s[wt][0][lane & 31], dhr_even = 0;
+        v2i amin = {};
+        if constexpr (TYPE == QMM_Q4_K)
+          if (h == kStagesPerSb - 1) amin = *(const v2i*)(&st.mn[wr][lane & 31][4 * (lane >> 5)]);
         v4i scv = {};
         if constexpr (TYPE == QMM_Q4_K) scv = *(const v4i*)(&st.sc[wr][0][sc_off]);
         typename W::A a0 = W::load(st.a[wr][0], lane);
@@ -398,11 +420,19 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
             dhr_next = st.s[wt][cc + 1][lane & 31];
             if constexpr (TYPE == QMM_Q4_K) scv_next = *(const v4i*)(&st.sc[wr][cc + 1][sc_off]);
           }
-          if (TYPE == QMM_Q4_K && (cc & 1)) {
-            const int ck = cc - 1 + (lane >> 5);
-            const float mv = st.m[wr][ck][lane & 31];
-            const float sv = f16_bits_to_float(st.s[wt][ck][lane & 31] >> 16);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(mv, sv, acc, 0, 0, 0);
+          if constexpr (TYPE == QMM_Q4_K) {
+            if (cc & 1) {  // the scaled sums of chunks cc-1 and cc as an f16 pair
+              const int sp = (int)__builtin_amdgcn_perm(dhr, dhr_even, 0x07060302u);
+              if (lane_hi == (h == 1)) bs[cc >> 1] = sp;
+            } else {
+              dhr_even = dhr;
+            }
+            if (h == kStagesPerSb - 1 && cc == KC - 1) {
+              typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+              const v16f zero = {};
+              cm = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, amin),
+                                                        __builtin_bit_cast(v4h, bs), zero, 0, 0, 0);
+            }
           }
           const float dh = f16_bits_to_float(dhr & 0xFFFF);
           if (cc == 0 && starts_sb) {
@@ -428,7 +458,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
           __builtin_amdgcn_sched_group_barrier(0x002, 72, 0);        // VALU
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (h == kStagesPerSb - 1) {  // end of a super-block: apply its d
+        if (h == kStagesPerSb - 1) {  // end of a super-block: apply its d (and q4_K's dmin)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float4 d4 = *(const float4*)(&st.d[wr][8 * q + 4 * (lane >> 5)]);
@@ -436,6 +466,13 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
             acc[4 * q + 1] = fmaf(inner[4 * q + 1], d4.y, acc[4 * q + 1]);
             acc[4 * q + 2] = fmaf(inner[4 * q + 2], d4.z, acc[4 * q + 2]);
             acc[4 * q + 3] = fmaf(inner[4 * q + 3], d4.w, acc[4 * q + 3]);
+            if constexpr (TYPE == QMM_Q4_K) {
+              const float4 m4 = *(const float4*)(&st.dm[wr][8 * q + 4 * (lane >> 5)]);
+              acc[4 * q + 0] = fmaf(cm[4 * q + 0], -m4.x, acc[4 * q + 0]);
+              acc[4 * q + 1] = fmaf(cm[4 * q + 1], -m4.y, acc[4 * q + 1]);
+              acc[4 * q + 2] = fmaf(cm[4 * q + 2], -m4.z, acc[4 * q + 2]);
+              acc[4 * q + 3] = fmaf(cm[4 * q + 3], -m4.w, acc[4 * q + 3]);
+            }
           }
         }
       }
@@ -501,7 +538,7 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
   const int vec_store = (p.od % 4 == 0) && ((uintptr_t)out % 16 == 0);
   const int wgs = plan.dp_row_tiles * plan.tok_tiles + plan.n_tail * plan.split;
   mmq_kernel<TYPE, WR, WT, KC, KS><<<dim3((unsigned)wgs), dim3(64 * WR * WT * KS), 0, s>>>(
-      p.wq, p.wd, p.wm, p.wsc, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
+      p.wq, p.wd, (const uint8_t*)p.wmn, p.wdm, p.wsc, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
       plan.dp_row_tiles, plan.split, vec_store, out, scratch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_tail == 0) return e;

@@ -27,7 +27,9 @@ namespace qmm {
 //             k = 16h + 8 + b in its high nibble (so masking and shifting the
 //             two words gives the 16 codes in MFMA order)
 //   wd  f32   [R][nsb][32 rows]      d of (row, super-block)
-//   wm  f32   [R][nchunk][32 rows]   -dmin*min of (row, chunk); q4_K only
+//   wmn f16   [R][nsb][32 rows][8]   the 6-bit min of (row, chunk) as an f16
+//             integer, at ((j/32*nsb + c/8)*32 + j%32)*8 + c%8; q4_K only
+//   wdm f32   [R][nsb][32 rows]      dmin of (row, super-block); q4_K only
 //   wsc uint8 [R][nchunk][32]        6-bit scale of (row, chunk), q4_K only, at
 //             16*((j/4)%2) + 4*((j%32)/8) + j%4: the 16 bytes a lane half of
 //             the MFMA output layout needs, in its register order
@@ -37,8 +39,11 @@ size_t wq_bytes(int type, int64_t od_pad, int64_t id) {
   return type == QMM_Q6_K ? (size_t)od_pad * (size_t)id * 2 : (size_t)od_pad * (size_t)id / 2;
 }
 size_t wd_bytes(int64_t od_pad, int64_t id) { return (size_t)od_pad * (size_t)(id / 256) * 4; }
-size_t wm_bytes(int type, int64_t od_pad, int64_t id) {
-  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) * 4 : 0;
+size_t wmn_bytes(int type, int64_t od_pad, int64_t id) {
+  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) * 2 : 0;
+}
+size_t wdm_bytes(int type, int64_t od_pad, int64_t id) {
+  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 256) * 4 : 0;
 }
 size_t wsc_bytes(int type, int64_t od_pad, int64_t id) {
   return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) : 0;
@@ -48,7 +53,7 @@ size_t wsc_bytes(int type, int64_t od_pad, int64_t id) {
 __global__ void __launch_bounds__(256)
 repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nchunk,
               int64_t total, int8_t* __restrict__ wq, float* __restrict__ wd,
-              float* __restrict__ wm, uint8_t* __restrict__ wsc) {
+              uint16_t* __restrict__ wmn, float* __restrict__ wdm, uint8_t* __restrict__ wsc) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total) return;
   const int h = (int)(gid & 1);
@@ -105,13 +110,19 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
       }
       sc4 = sc;
       if (h == 0) {
-        const float dmin = f16_bits_to_float(B[2] | (B[3] << 8));
-        wm[((int64_t)rb * nchunk + c) * 32 + jr] = -(dmin * (float)mn);
-        if (cl == 0) wd[((int64_t)rb * nsb + b) * 32 + jr] = f16_bits_to_float(B[0] | (B[1] << 8));
+        wmn[(((int64_t)rb * nsb + b) * 32 + jr) * 8 + cl] =
+            __builtin_bit_cast(uint16_t, (_Float16)(float)mn);  // 0..63: exact
+        if (cl == 0) {
+          wd[((int64_t)rb * nsb + b) * 32 + jr] = f16_bits_to_float(B[0] | (B[1] << 8));
+          wdm[((int64_t)rb * nsb + b) * 32 + jr] = f16_bits_to_float(B[2] | (B[3] << 8));
+        }
       }
     }
   } else if (h == 0) {
-    if (type == QMM_Q4_K) wm[((int64_t)rb * nchunk + c) * 32 + jr] = 0.0f;
+    if (type == QMM_Q4_K) {
+      wmn[(((int64_t)rb * nsb + b) * 32 + jr) * 8 + cl] = 0;
+      if (cl == 0) wdm[((int64_t)rb * nsb + b) * 32 + jr] = 0.0f;
+    }
     if (cl == 0) wd[((int64_t)rb * nsb + b) * 32 + jr] = 0.0f;
   }
   if (type == QMM_Q6_K) {
@@ -130,7 +141,7 @@ hipError_t launch_repack(const uint8_t* raw, const Planes& p, hipStream_t s) {
   const int64_t total = p.od_pad * p.nchunk * 2;
   const int64_t blocks = (total + 255) / 256;
   repack_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-      raw, p.type, (int)p.od, (int)p.nsb, (int)p.nchunk, total, p.wq, p.wd, p.wm, p.wsc);
+      raw, p.type, (int)p.od, (int)p.nsb, (int)p.nchunk, total, p.wq, p.wd, p.wmn, p.wdm, p.wsc);
   return hipGetLastError();
 }
 

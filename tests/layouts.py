@@ -22,11 +22,12 @@ def read_qact(buf: np.ndarray, n_tok: int, id_: int):
     return q, sp[:, :, 0].copy(), sp[:, :, 1].copy()
 
 
-def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: int, wm_offset: int,
-                sc_offset: int):
+def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: int, mn_offset: int,
+                dm_offset: int, sc_offset: int):
     """exported planes -> (w [od_pad][id] int32 scale-carrying weights: q6_K the
-    folded 64*hi + lo, q4_K scale * code; d [od_pad][nsb] f32; wm [od_pad][nchunk]
-    f32 or None)."""
+    folded 64*hi + lo, q4_K scale * code; d [od_pad][nsb] f32; for q4_K the mins
+    [od_pad][nchunk] (decoded from their f16 values) and dmin [od_pad][nsb] f32,
+    else None, None)."""
     nchunk, nsb = id_ // 32, id_ // 256
     R = od_pad // 32
     buf = np.asarray(buf, np.uint8)
@@ -50,8 +51,13 @@ def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: i
         w = codes * np.repeat(sc, 32, axis=1)
     d = buf[wd_offset: wd_offset + od_pad * nsb * 4].view("<f4").reshape(R, nsb, 32)
     d = d.transpose(0, 2, 1).reshape(od_pad, nsb)
-    wm = None
+    mn = dm = None
     if type_ == 4:
-        wm = buf[wm_offset: wm_offset + od_pad * nchunk * 4].view("<f4").reshape(R, nchunk, 32)
-        wm = wm.transpose(0, 2, 1).reshape(od_pad, nchunk)
-    return w, d, wm
+        # mins: binary16 [R][nsb][row][chunk of the super-block]
+        m16 = buf[mn_offset: mn_offset + od_pad * nchunk * 2].view("<f2").reshape(R, nsb, 32, 8)
+        mf = m16.astype(np.float64).transpose(0, 2, 1, 3).reshape(od_pad, nchunk)
+        assert np.all(mf == np.round(mf)) and mf.min() >= 0 and mf.max() <= 63
+        mn = mf.astype(np.int32)
+        dm = buf[dm_offset: dm_offset + od_pad * nsb * 4].view("<f4").reshape(R, nsb, 32)
+        dm = dm.transpose(0, 2, 1).reshape(od_pad, nsb)
+    return w, d, mn, dm

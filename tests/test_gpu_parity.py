@@ -137,11 +137,10 @@ def expected_planes(type_, raw, od, id_):
     if type_ == synth.Q6_K:
         w6, sc, d = oracle.decode_q6k(raw, od, id_)
         w = w6.astype(np.int32) * np.repeat(sc.astype(np.int32), 16, axis=1)
-        return w, d, None
+        return w, d, None, None
     w4, sc, mn, d, dm = oracle.decode_q4k(raw, od, id_)
     w = w4.astype(np.int32) * np.repeat(sc.astype(np.int32), 32, axis=1)
-    wm = -(np.repeat(dm, 8, axis=1) * mn.astype(np.float32))
-    return w, d, wm
+    return w, d, mn.astype(np.int32), dm
 
 
 @pytest.mark.parametrize("type_,od,id_,full", [(synth.Q6_K, 5, 512, False), (synth.Q6_K, 130, 768, True),
@@ -152,15 +151,16 @@ def test_planes_byte_exact(type_, od, id_, full):
     raw = _full_range_q6k(rng, od, id_) if full else synth.weights(rng, type_, od, id_)
     w = qmm.register_weights(type_, od, id_, raw)
     assert w.od_pad % 128 == 0 and w.od_pad >= od
-    gw, gd, gwm = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.wm_offset,
-                                      w.sc_offset)
-    ew, ed, ewm = expected_planes(type_, raw, od, id_)
+    gw, gd, gmn, gdm = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.mn_offset,
+                                           w.dm_offset, w.sc_offset)
+    ew, ed, emn, edm = expected_planes(type_, raw, od, id_)
     assert np.array_equal(gw[:od], ew)
-    assert np.array_equal(gd[:od].view(np.uint32), ed.view(np.uint32))
+    assert np.array_equal(gd[:od].view(np.uint32), ed.astype(np.float32).view(np.uint32))
     assert not gw[od:].any() and not gd[od:].any()
     if type_ == synth.Q4_K:
-        assert np.array_equal(gwm[:od].view(np.uint32), ewm.astype(np.float32).view(np.uint32))
-        assert not gwm[od:].any()
+        assert np.array_equal(gmn[:od], emn)
+        assert np.array_equal(gdm[:od].view(np.uint32), edm.astype(np.float32).view(np.uint32))
+        assert not gmn[od:].any() and not gdm[od:].any()
     w.release()
 
 
