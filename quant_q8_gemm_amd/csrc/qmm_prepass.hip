@@ -32,10 +32,14 @@ __device__ __forceinline__ int dpp(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
 }
 
+// Maximum of non-negative finite floats over the 8 lanes, on their bit patterns
+// (ordered like the values), so each step is one integer max.
 __device__ __forceinline__ float max8(float v) {
-  v = fmaxf(v, __builtin_bit_cast(float, dpp<kDppQuadXor1>(__builtin_bit_cast(int, v))));
-  v = fmaxf(v, __builtin_bit_cast(float, dpp<kDppQuadXor2>(__builtin_bit_cast(int, v))));
-  return fmaxf(v, __builtin_bit_cast(float, dpp<kDppHalfMirror>(__builtin_bit_cast(int, v))));
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  u = max(u, (uint32_t)dpp<kDppQuadXor1>((int)u));
+  u = max(u, (uint32_t)dpp<kDppQuadXor2>((int)u));
+  u = max(u, (uint32_t)dpp<kDppHalfMirror>((int)u));
+  return __builtin_bit_cast(float, u);
 }
 
 __device__ __forceinline__ int sum8(int v) {
@@ -72,15 +76,16 @@ __device__ __forceinline__ void quant4(const float4& v, float dhf, float inv, in
 }
 
 __global__ void __launch_bounds__(256)
-quantize_kernel(const float* __restrict__ x, int n_tok, int id, int nchunk,
+quantize_kernel(const float* __restrict__ x, int n_tok, int id, int nchunk, int chunk_major,
                 uint8_t* __restrict__ qq, uint8_t* __restrict__ qs) {
-  const int tb = blockIdx.x;
-  const int c0 = blockIdx.y * kQuantChunks;
+  const int tb = chunk_major ? blockIdx.y : blockIdx.x;
+  const int c0 = (chunk_major ? blockIdx.x : blockIdx.y) * kQuantChunks;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tt = wave * 8 + (lane >> 3);
   const int sub = lane & 7;
   const int64_t t = (int64_t)tb * 32 + tt;
   const bool live = t < n_tok;
+  const bool block_full = (int64_t)(tb + 1) * 32 <= n_tok;  // uniform: no lane past the end
   // Lanes past the last token read the last token's row (and chunks past the
   // end read the last chunk), so that every load is in bounds and issued
   // unconditionally; their values are replaced by zeros below.
@@ -94,7 +99,7 @@ quantize_kernel(const float* __restrict__ x, int n_tok, int id, int nchunk,
   for (int i = 0; i < kQuantChunks; ++i) {
     const int c = c0 + i;
     if (c >= nchunk) break;
-    if (!live) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!block_full && !live) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     const float amax = max8(fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)),
                                   fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
     const float d32 = amax / 127.0f;
@@ -118,8 +123,15 @@ quantize_kernel(const float* __restrict__ x, int n_tok, int id, int nchunk,
 hipError_t launch_quantize(const float* x, int64_t n_tok, int64_t t_pad, int64_t id,
                            uint8_t* qact, hipStream_t s) {
   const int64_t nchunk = id / 32;
-  dim3 grid((unsigned)(t_pad / 32), (unsigned)((nchunk + kQuantChunks - 1) / kQuantChunks));
-  quantize_kernel<<<grid, dim3(256), 0, s>>>(x, (int)n_tok, (int)id, (int)nchunk, qact,
+  const unsigned n_tb = (unsigned)(t_pad / 32), n_cg = (unsigned)((nchunk + kQuantChunks - 1) / kQuantChunks);
+  // Work-group order.  Many tokens: chunk groups fastest, so consecutive
+  // work-groups read consecutive stretches of the same 32 rows (3314 x 4096:
+  // 22% faster; with token blocks fastest the rows' power-of-two stride
+  // concentrates the reads).  Few tokens: token blocks fastest (4-8% faster at
+  // 512 and 2048 tokens).
+  const int chunk_major = n_tb > 96;
+  const dim3 grid = chunk_major ? dim3(n_cg, n_tb) : dim3(n_tb, n_cg);
+  quantize_kernel<<<grid, dim3(256), 0, s>>>(x, (int)n_tok, (int)id, (int)nchunk, chunk_major, qact,
                                              qact + (size_t)t_pad * (size_t)id);
   return hipGetLastError();
 }
