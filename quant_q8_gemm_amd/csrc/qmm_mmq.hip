@@ -43,7 +43,7 @@ namespace qmm {
 // stages of KC chunks of 32 (KC = 2, 4 or 8: a quarter, half or whole 256-wide
 // super-block).  Each stage's operands -- the weight fragments of the WR row
 // blocks, the q8 codes and scale pairs of the WT token blocks, and d (and for
-// q4_K the -dmin*min plane and the scale bytes) -- are copied once per
+// q4_K the scale bytes, the mins and dmin) -- are copied once per
 // work-group into LDS with direct global->LDS loads (global_load_lds_dwordx4
 // puts lane l's 16 bytes at the LDS base + 16*l, so one wave instruction moves
 // 1 KiB), and read from there by every wave that shares them.  Two LDS stages
@@ -551,7 +551,7 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
 //  * many tiles (at least four 64 x 64 tiles per CU, e.g. the 3314-token layer,
 //    the 2048-token head): several work-groups per CU, so one group's barrier
 //    wait is covered by the others.  q4_K: 2 x 2 waves (64 x 64 tiles), four
-//    per CU, half-super-block stages (29 KiB of LDS, 106 VGPRs).  q6_K: 2 x 4
+//    per CU, half-super-block stages (30 KiB of LDS, 110 VGPRs).  q6_K: 2 x 4
 //    waves (64 rows x 128 tokens), two per CU, half-super-block stages (69 KiB,
 //    124 VGPRs): each weight fragment a work-group copies serves four waves
 //    instead of two, a third fewer copied bytes per output block, which is
@@ -560,7 +560,7 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
 //    was 4-9% slower for q4_K, whose copies are a quarter the size);
 //  * few tiles (e.g. 512 tokens x 4096 rows = 256 64 x 128 tiles): 2 x 4 waves
 //    (64 rows x 128 tokens) in two k-groups, half-super-block stages, 137 KiB
-//    (q6_K) or 94 KiB (q4_K) of LDS, one work-group per CU; the second k-group
+//    (q6_K) or 95 KiB (q4_K) of LDS, one work-group per CU; the second k-group
 //    doubles the waves per CU.
 // In all, a ragged second wave (tiles = slots + r with r <= slots / 2, the
 // slots being the work-groups resident at once; e.g. 4097 rows x 512 tokens:
