@@ -198,7 +198,9 @@ int qmm_quantize_activations(const float *x, int64_t n_tok, int64_t id, void *qa
  * that needs it and kept until the process ends; calls on one stream share it
  * in stream order.  Synchronize a stream before destroying it if an MMQ on it
  * may still run.  Results are deterministic: the same call gives the same bits.
- * Errors: QMM_EINVAL, QMM_ESHAPE, QMM_ENOMEM (the scratch), QMM_EHIP.
+ * Errors: QMM_EINVAL (also for a shape whose tiles exceed one launch: n_tok * od
+ * beyond about 6.9e10, i.e. an output of 275 GB), QMM_ESHAPE, QMM_ENOMEM (the
+ * scratch), QMM_EHIP.
  */
 int qmm_mmq(const qmm_weights *w, const void *qact, size_t qact_bytes, int64_t n_tok,
             float *out, void *stream);

@@ -272,6 +272,10 @@ int qmm_mmq(const qmm_weights* w, const void* qact, size_t qact_bytes, int64_t n
   e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(multiprocessor count)");
   const qmm::MmqPlan plan = qmm::plan_mmq(w->p, n_tok, num_cus);
+  // one-dimensional launch: work-groups x threads must stay below 2^32
+  if ((uint64_t)plan.work_groups * (uint64_t)plan.threads >= (1ull << 32))
+    return fail(QMM_EINVAL, "n_tok=%lld x od=%lld needs %lld work-groups, more than one launch holds",
+                (long long)n_tok, (long long)w->p.od, (long long)plan.work_groups);
   const hipStream_t s = (hipStream_t)stream;
   void* scratch = nullptr;
   if (plan.scratch_bytes > 0) {

@@ -47,6 +47,8 @@ struct MmqPlan {
   int n_tail;         // tiles after them, each split along K
   int split;          // K slices per tail tile (1: no tail)
   size_t scratch_bytes;
+  int64_t work_groups;  // of the MMQ launch (one-dimensional grid)
+  int threads;          // per work-group
 };
 MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus);
 // Upper bound of MmqPlan::scratch_bytes on a device with num_cus compute units.

@@ -536,7 +536,7 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
                 "tiles must divide the row and token padding");
   const uint8_t* qs = qact + (size_t)t_pad * (size_t)p.id;
   const int vec_store = (p.od % 4 == 0) && ((uintptr_t)out % 16 == 0);
-  const int wgs = plan.dp_row_tiles * plan.tok_tiles + plan.n_tail * plan.split;
+  const int64_t wgs = plan.work_groups;
   mmq_kernel<TYPE, WR, WT, KC, KS><<<dim3((unsigned)wgs), dim3(64 * WR * WT * KS), 0, s>>>(
       p.wq, p.wd, (const uint8_t*)p.wmn, p.wdm, p.wsc, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
       plan.dp_row_tiles, plan.split, vec_store, out, scratch);
@@ -621,6 +621,8 @@ MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
       plan.scratch_bytes = (size_t)n_tail * split * (32 * g.wr) * (32 * g.wt) * sizeof(float);
     }
   }
+  plan.work_groups = (int64_t)plan.dp_row_tiles * plan.tok_tiles + (int64_t)plan.n_tail * plan.split;
+  plan.threads = 64 * g.wr * g.wt * g.ks;
   return plan;
 }
 

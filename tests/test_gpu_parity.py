@@ -263,6 +263,10 @@ SMALL = [("C1 q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          # (a split tail), and 1088 tiles (two full waves and a ragged third)
          ("q6_K 1000x512 T=4100", synth.Q6_K, 1000, 512, 4100, True),
          ("q6_K 2100x256 T=4000", synth.Q6_K, 2100, 256, 4000, False),
+         # one token against 70000 rows: the many-tile geometry with a single
+         # token tile (1094 row tiles)
+         ("q4_K 70000x256 T=1", synth.Q4_K, 70000, 256, 1, False),
+         ("q6_K 70001x256 T=1", synth.Q6_K, 70001, 256, 1, True),
          ("q4_K 1030x256 T=4000", synth.Q4_K, 1030, 256, 4000, False)]
 
 
