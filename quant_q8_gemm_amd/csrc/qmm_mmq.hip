@@ -434,7 +434,12 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
                                                         __builtin_bit_cast(v4h, bs), zero, 0, 0, 0);
             }
           }
-          const float dh = f16_bits_to_float(dhr & 0xFFFF);
+          // dh converted to f32 once per chunk and kept in a register, so the 16
+          // scale FMAs are plain v_fma_f32, which issue at twice the rate of
+          // the mixed-precision v_fma_mix_f32 the compiler would otherwise fold
+          // the f16 operand into
+          float dh = f16_bits_to_float(dhr & 0xFFFF);
+          pin(dh);
           if (cc == 0 && starts_sb) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) inner[i] = (float)W::dot(dj, scv, i) * dh;
