@@ -5,8 +5,8 @@
 //   kind 1: the vector ALU running the MMQ's per-block scale epilogue, the
 //           same three instructions per (token, row, 32-block) -- combine the
 //           two plane dots (v_lshl_add_u32), convert (v_cvt_f32_i32), scale
-//           and accumulate with the f16 activation scale (v_fma_mix_f32) --
-//           on 16 elements per lane.
+//           and accumulate with the activation scale held as f32 (v_fmac_f32)
+//           -- on 16 elements per lane.
 // Work-group 0's first wave also records the shader clock (s_memtime) and the
 // 100 MHz constant clock (s_memrealtime) across its run, so the caller can
 // state the clock the rates were measured at.  These kernels are measurement
