@@ -599,7 +599,9 @@ MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
   const int64_t small_tiles = (p.od_pad / 64) * ((n_tok + 63) / 64);
   plan.many = small_tiles >= 4 * 256;
   const Geometry g = geometry(p.type, plan.many);
-  plan.row_tiles = (int)(p.od_pad / (32 * g.wr));
+  // row tiles that hold at least one real row: the planes are padded to
+  // kRowPad rows, but a tile of padding only would compute zeros
+  plan.row_tiles = (int)((p.od + 32 * g.wr - 1) / (32 * g.wr));
   plan.tok_tiles = (int)((n_tok + 32 * g.wt - 1) / (32 * g.wt));
   plan.dp_row_tiles = plan.row_tiles;
   plan.split = 1;
