@@ -419,13 +419,19 @@ def main():
         "raw_weight_bytes": sum(w.raw_bytes for w in weights.values()),
     }
     if not args.no_calib:
-        cal = calibrate(torch, stream)
-        result["calibration"] = cal
-        rl = result["roofline"]
-        rl["measured_peak"] = cal["mfma_i8"]["tops"]
-        rl["frac_of_measured_peak"] = round(mmq_tops / cal["mfma_i8"]["tops"], 4)
-        rl["epilogue_roof"]["measured"] = cal["epilogue_valu"]["tops"]
-        rl["epilogue_roof"]["frac_of_measured"] = round(mmq_tops / cal["epilogue_valu"]["tops"], 4)
+        # the measured roofs are context for the MMQ's figures: a failure here
+        # is reported in the line, not allowed to lose the measurement above
+        try:
+            cal = calibrate(torch, stream)
+        except (OSError, RuntimeError) as e:
+            result["calibration"] = {"error": f"{type(e).__name__}: {e}"}
+        else:
+            result["calibration"] = cal
+            rl = result["roofline"]
+            rl["measured_peak"] = cal["mfma_i8"]["tops"]
+            rl["frac_of_measured_peak"] = round(mmq_tops / cal["mfma_i8"]["tops"], 4)
+            rl["epilogue_roof"]["measured"] = cal["epilogue_valu"]["tops"]
+            rl["epilogue_roof"]["frac_of_measured"] = round(mmq_tops / cal["epilogue_valu"]["tops"], 4)
     if not args.no_cpu:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         result["cpu_baseline"] = cpu_baseline(gemms, raws, xs, T, threads, args.cpu_macs)
