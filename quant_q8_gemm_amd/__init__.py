@@ -94,6 +94,12 @@ def _check(rc: int) -> None:
         raise QmmError(rc, last_error())
 
 
+def _check_qact(qact) -> None:
+    import torch
+    if qact.dtype != torch.uint8 or not qact.is_cuda or qact.dim() != 1 or not qact.is_contiguous():
+        raise QmmError(EINVAL, "qact must be a contiguous one-dimensional cuda uint8 tensor")
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -177,6 +183,7 @@ def quantize_activations(x, qact=None, stream=None):
         if nb == 0:
             raise QmmError(EINVAL, f"bad shape n_tok={n_tok} id={id_}")
         qact = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    _check_qact(qact)
     _check(_lib.qmm_quantize_activations(ctypes.c_void_p(x.data_ptr()), n_tok, id_,
                                          ctypes.c_void_p(qact.data_ptr()), qact.numel(),
                                          _stream(stream)))
@@ -186,10 +193,12 @@ def quantize_activations(x, qact=None, stream=None):
 def mmq(w: Weights, qact, n_tok: int, out=None, stream=None):
     """out[t][j] (cuda float32 [n_tok][od]) from a handle and a qact buffer."""
     import torch
+    _check_qact(qact)
     if out is None:
         out = torch.empty((n_tok, w.od), dtype=torch.float32, device=qact.device)
-    elif out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (n_tok, w.od):
-        raise QmmError(EINVAL, "out must be a contiguous float32 [n_tok][od] tensor")
+    elif (out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous()
+          or tuple(out.shape) != (n_tok, w.od)):
+        raise QmmError(EINVAL, "out must be a contiguous cuda float32 [n_tok][od] tensor")
     _check(_lib.qmm_mmq(ctypes.c_void_p(w.handle), ctypes.c_void_p(qact.data_ptr()), qact.numel(),
                         int(n_tok), ctypes.c_void_p(out.data_ptr()), _stream(stream)))
     return out

@@ -157,3 +157,13 @@ def test_calibration_library_loads_and_validates():
     assert f(0, 0, 1, good, good, None) == 1
     assert f(1, 10, 0, good, good, None) == 1
     assert f(0, 10, 1, None, good, None) == 1
+
+
+def test_binding_rejects_wrong_qact_tensors():
+    """The binding passes byte counts from the tensor: a qact that is not a flat
+    uint8 device tensor is refused before any library call."""
+    import torch
+    with pytest.raises(qmm.QmmError):
+        qmm._check_qact(torch.zeros(16, dtype=torch.float32))
+    with pytest.raises(qmm.QmmError):
+        qmm._check_qact(torch.zeros(16, dtype=torch.uint8))  # host memory
