@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libqmm.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it first (python -m quant_q8_gemm_amd._build or "
+        f"{LIB_PATH} is missing: build it first (python quant_q8_gemm_amd/_build.py or "
         "__graft_entry__.build()); there is no fallback implementation")
 
 # One HIP runtime per process: PyTorch ships its own libamdhip64 under the same

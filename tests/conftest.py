@@ -7,8 +7,8 @@ if ROOT not in sys.path:
 
 # Build the C-ABI library and the oracle only if nothing is built yet.
 if not os.path.exists(os.path.join(ROOT, "quant_q8_gemm_amd", "libqmm.so")):
-    from quant_q8_gemm_amd import _build
-    _build.build()
+    import __graft_entry__
+    __graft_entry__._load_build_module().build()
 if not os.path.exists(os.path.join(ROOT, "oracle", "liboracle.so")):
     import oracle
     oracle.build()
