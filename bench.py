@@ -52,18 +52,18 @@ def _single(cfg, inp="x"):
 
 
 WORKLOADS = {
-    "ffn_down": _single(synth.C2),            # q6_K 4096 x 11008, 512 tokens
-    "ffn_down_odd": _single(synth.C2_ODD),
-    "attn": _single(synth.C3_QKVO),
-    "ffn_gate_up": _single(synth.C3_GU),
-    "head": _single(synth.C4),
-    "c1": _single(synth.C1),
+    "ffn_down": _single(synth.FFN_DOWN),            # q6_K 4096 x 11008, 512 tokens
+    "ffn_down_odd": _single(synth.FFN_DOWN_ODD),
+    "attn": _single(synth.ATTN),
+    "ffn_gate_up": _single(synth.GATE_UP),
+    "head": _single(synth.HEAD),
+    "small": _single(synth.SMALL_Q6K),
     # one GPU's share of ffn_down under 8-way tensor parallelism: a column slice
     # (512 of the 4096 rows) and a row slice (6 of the 43 super-blocks of id)
     "ffn_down_tp8_col": _single(("q6_K ffn_down column shard 512x11008 T=512", synth.Q6_K, 512, 11008, 512, False)),
     "ffn_down_tp8_row": _single(("q6_K ffn_down row shard 4096x1536 T=512", synth.Q6_K, 4096, 1536, 512, False)),
     "layer": ("LLaMA-7B q4_K_M-style layer, 3314 tokens (q,k,o,gate,up q4_K; v,down q6_K)",
-              synth.C5_TOKENS,
+              synth.LAYER_TOKENS,
               {"attn_in": 4096, "attn_out": 4096, "ffn_in": 4096, "ffn_mid": 11008},
               [("attn_q", synth.Q4_K, 4096, 4096, "attn_in"),
                ("attn_k", synth.Q4_K, 4096, 4096, "attn_in"),
@@ -76,7 +76,7 @@ WORKLOADS = {
     # the same layer with same-type GEMMs that share an input fused by row
     # concatenation at registration: q||k (od 8192) and gate||up (od 22016)
     "layer_fused": ("LLaMA-7B q4_K_M-style layer, 3314 tokens, q||k and gate||up fused",
-                    synth.C5_TOKENS,
+                    synth.LAYER_TOKENS,
                     {"attn_in": 4096, "attn_out": 4096, "ffn_in": 4096, "ffn_mid": 11008},
                     [("attn_qk", synth.Q4_K, 8192, 4096, "attn_in"),
                      ("attn_v", synth.Q6_K, 4096, 4096, "attn_in"),
@@ -240,7 +240,7 @@ def cpu_single_thread(gemms, raws, xs, T, macs_target):
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path "
+        print("bench.py measures one MI355X: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 

@@ -90,16 +90,16 @@ def case(type_: int, od: int, id_: int, n_tok: int, seed: int = 0,
 
 
 # The five workloads: (name, type, od, id, n_tok, outliers).
-C1 = ("q6_K 256x512 T=64", Q6_K, 256, 512, 64, False)
-C2 = ("q6_K ffn_down 4096x11008 T=512", Q6_K, 4096, 11008, 512, False)
-C2_ODD = ("q6_K ffn_down od=4097 T=509", Q6_K, 4097, 11008, 509, False)
-C3_QKVO = ("q4_K attn 4096x4096 T=512", Q4_K, 4096, 4096, 512, False)
-C3_GU = ("q4_K ffn gate/up 11008x4096 T=512", Q4_K, 11008, 4096, 512, False)
-C4 = ("q6_K head 32000x4096 T=2048", Q6_K, 32000, 4096, 2048, True)
+SMALL_Q6K = ("q6_K 256x512 T=64", Q6_K, 256, 512, 64, False)
+FFN_DOWN = ("q6_K ffn_down 4096x11008 T=512", Q6_K, 4096, 11008, 512, False)
+FFN_DOWN_ODD = ("q6_K ffn_down od=4097 T=509", Q6_K, 4097, 11008, 509, False)
+ATTN = ("q4_K attn 4096x4096 T=512", Q4_K, 4096, 4096, 512, False)
+GATE_UP = ("q4_K ffn gate/up 11008x4096 T=512", Q4_K, 11008, 4096, 512, False)
+HEAD = ("q6_K head 32000x4096 T=2048", Q6_K, 32000, 4096, 2048, True)
 
 # One LLaMA-7B q4_K_M-style layer at a 3314-token prefill: (name, type, od, id).
-C5_TOKENS = 3314
-C5_LAYER = (
+LAYER_TOKENS = 3314
+LAYER_GEMMS = (
     ("attn_q", Q4_K, 4096, 4096),
     ("attn_k", Q4_K, 4096, 4096),
     ("attn_v", Q6_K, 4096, 4096),

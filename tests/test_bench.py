@@ -23,7 +23,7 @@ def test_bench_refuses_more_than_one_gpu():
 
 @pytest.mark.gpu
 def test_bench_json_line_contract():
-    r = _bench("--steps", "5", "--warmup", "2", "--no-cold", "--workload", "c1")
+    r = _bench("--steps", "5", "--warmup", "2", "--no-cold", "--workload", "small")
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
     assert len(lines) == 1

@@ -244,7 +244,7 @@ def test_int_dots_exact_full_range_one_chunk(type_):
 # f32 results
 # --------------------------------------------------------------------------
 
-SMALL = [("C1 q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
+SMALL = [("q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          ("q4_K 300x768 T=77", synth.Q4_K, 300, 768, 77, True),
          ("q6_K 129x1280 T=200", synth.Q6_K, 129, 1280, 200, True),
          ("q4_K 1x256 T=1", synth.Q4_K, 1, 256, 1, False),
@@ -325,12 +325,12 @@ def _sample_pairs(rng, T, od, n=3000):
 
 
 # the one-layer workload at 3314 tokens: its four distinct GEMM shapes
-LAYER = [(f"layer {synth.TYPE_NAMES[t]} {od}x{id_} T={synth.C5_TOKENS}", t, od, id_, synth.C5_TOKENS, False)
-         for t, od, id_ in sorted({(t, od, id_) for _, t, od, id_ in synth.C5_LAYER})]
+LAYER = [(f"layer {synth.TYPE_NAMES[t]} {od}x{id_} T={synth.LAYER_TOKENS}", t, od, id_, synth.LAYER_TOKENS, False)
+         for t, od, id_ in sorted({(t, od, id_) for _, t, od, id_ in synth.LAYER_GEMMS})]
 # one GPU's share of ffn_down under 8-way tensor parallelism (column and row slices)
 SHARDS = [("q6_K ffn_down column shard 512x11008 T=512", synth.Q6_K, 512, 11008, 512, False),
           ("q6_K ffn_down row shard 4096x1536 T=512", synth.Q6_K, 4096, 1536, 512, False)]
-FULL = [synth.C2, synth.C2_ODD, synth.C3_QKVO, synth.C3_GU, synth.C4] + LAYER + SHARDS
+FULL = [synth.FFN_DOWN, synth.FFN_DOWN_ODD, synth.ATTN, synth.GATE_UP, synth.HEAD] + LAYER + SHARDS
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=[c[0] for c in FULL])
@@ -356,7 +356,7 @@ def test_full_size_sampled(cfg):
 # --------------------------------------------------------------------------
 
 def test_odd_rows_and_token_tail_are_prefixes_and_repeatable():
-    name, type_, od, id_, T, _ = synth.C2
+    name, type_, od, id_, T, _ = synth.FFN_DOWN
     say("prefix properties at the ffn_down shape")
     raw, x = synth.case(type_, od + 1, id_, T, seed=3)
     w_odd = qmm.register_weights(type_, od + 1, id_, raw)
