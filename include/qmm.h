@@ -58,7 +58,9 @@ extern "C" {
 #define QMM_EHIP (-4)   /* a HIP runtime call or kernel launch failed */
 
 /* Size limits (validated): 1 <= od <= QMM_MAX_OD, 256 <= id <= QMM_MAX_ID with
- * id % 256 == 0, 1 <= n_tok <= QMM_MAX_TOKENS. */
+ * id % 256 == 0, 0 <= n_tok <= QMM_MAX_TOKENS.  n_tok == 0 is an empty batch:
+ * qmm_qact_bytes gives 0, and qmm_quantize_activations and qmm_mmq (with
+ * qact_bytes 0) return QMM_OK without touching any pointer or the device. */
 #define QMM_MAX_OD (1 << 21)
 #define QMM_MAX_ID (1 << 20)
 #define QMM_MAX_TOKENS (1 << 20)
@@ -146,7 +148,8 @@ void qmm_set_memory_cap(size_t bytes);
 /*
  * qmm_qact_bytes -- size of the quantized-activation buffer for n_tok tokens of
  * id activations: T_pad * id * 9 / 8 with T_pad = n_tok rounded up to
- * QMM_TOKEN_PAD.  Returns 0 if n_tok or id is out of range.
+ * QMM_TOKEN_PAD.  Returns 0 for n_tok == 0 (an empty batch) and if n_tok or
+ * id is out of range.
  */
 size_t qmm_qact_bytes(int64_t n_tok, int64_t id);
 

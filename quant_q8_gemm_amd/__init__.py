@@ -180,7 +180,7 @@ def quantize_activations(x, qact=None, stream=None):
     n_tok, id_ = x.shape
     nb = qact_bytes(n_tok, id_)
     if qact is None:
-        if nb == 0:
+        if nb == 0 and n_tok != 0:
             raise QmmError(EINVAL, f"bad shape n_tok={n_tok} id={id_}")
         qact = torch.empty(nb, dtype=torch.uint8, device=x.device)
     _check_qact(qact)

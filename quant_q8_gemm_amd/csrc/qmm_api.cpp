@@ -73,9 +73,10 @@ int check_id(int64_t id) {
   return QMM_OK;
 }
 
+// n_tok == 0 is an empty batch: valid, and the call does nothing
 int check_tokens(int64_t n_tok) {
-  if (n_tok < 1 || n_tok > QMM_MAX_TOKENS)
-    return fail(QMM_EINVAL, "n_tok must be in [1, %d], got %lld", QMM_MAX_TOKENS, (long long)n_tok);
+  if (n_tok < 0 || n_tok > QMM_MAX_TOKENS)
+    return fail(QMM_EINVAL, "n_tok must be in [0, %d], got %lld", QMM_MAX_TOKENS, (long long)n_tok);
   return QMM_OK;
 }
 
@@ -90,7 +91,7 @@ const char* qmm_last_error(void) { return g_last_error.c_str(); }
 void qmm_set_memory_cap(size_t bytes) { g_cap.store(bytes); }
 
 size_t qmm_qact_bytes(int64_t n_tok, int64_t id) {
-  if (n_tok < 1 || n_tok > QMM_MAX_TOKENS || id < 256 || id > QMM_MAX_ID || id % 256 != 0) return 0;
+  if (n_tok < 0 || n_tok > QMM_MAX_TOKENS || id < 256 || id > QMM_MAX_ID || id % 256 != 0) return 0;
   return (size_t)token_pad(n_tok) * (size_t)id / 8 * 9;
 }
 
@@ -239,6 +240,11 @@ int qmm_quantize_activations(const float* x, int64_t n_tok, int64_t id, void* qa
                              size_t qact_bytes, void* stream) {
   if (int rc = check_tokens(n_tok)) return rc;
   if (int rc = check_id(id)) return rc;
+  if (n_tok == 0) {  // empty batch: no bytes to write, pointers are not used
+    if (qact_bytes != 0) return fail(QMM_EINVAL, "qact_bytes %zu != 0 for n_tok = 0", qact_bytes);
+    ok();
+    return QMM_OK;
+  }
   if (x == nullptr || qact == nullptr) return fail(QMM_EINVAL, "x or qact is NULL");
   if (!aligned(x, 16) || !aligned(qact, 16)) return fail(QMM_EINVAL, "x and qact must be 16-byte aligned");
   const size_t need = qmm_qact_bytes(n_tok, id);
@@ -256,6 +262,11 @@ int qmm_mmq(const qmm_weights* w, const void* qact, size_t qact_bytes, int64_t n
             void* stream) {
   if (w == nullptr) return fail(QMM_EINVAL, "NULL weights handle");
   if (int rc = check_tokens(n_tok)) return rc;
+  if (n_tok == 0) {  // empty batch: an empty output, nothing launched
+    if (qact_bytes != 0) return fail(QMM_ESHAPE, "qact_bytes %zu != 0 for n_tok = 0", qact_bytes);
+    ok();
+    return QMM_OK;
+  }
   if (qact == nullptr || out == nullptr) return fail(QMM_EINVAL, "qact or out is NULL");
   if (!aligned(qact, 16)) return fail(QMM_EINVAL, "qact must be 16-byte aligned");
   if (!aligned(out, 4)) return fail(QMM_EINVAL, "out must be 4-byte aligned");

@@ -136,13 +136,31 @@ struct WeightOps<QMM_Q4_K> {
     return {__builtin_amdgcn_mfma_i32_32x32x32_i8(a.c, bq, zero, 0, 0, 0)};
   }
   __device__ static void keep(D& d) { pin(d.c); }
-  // |D| <= 32*15*127 fits 24 bits; the scale is byte i of the lane's 16 bytes
-  __device__ static int dot(const D& d, v4i sc, int i) {
-    const int dc = (d.c[i] << 8) >> 8;
-    const int s = (int)(((uint32_t)sc[i >> 2] >> (8 * (i & 3))) & 0xFF);
-    return dc * s;
-  }
+  // the code dot D of output element i; the 6-bit scale is not in it but in the
+  // scale product that multiplies it (scale_outer below)
+  __device__ static int dot(const D& d, v4i, int i) { return d.c[i]; }
 };
+
+// q4_K: the scale of output element (row j, token t) of chunk c is sc(j, c) * dh(t, c),
+// an outer product of a row vector and a token vector, each an exact f16 value (a
+// 6-bit integer, the f16 activation scale).  One f16 MFMA (32x32x8, only k = 0
+// non-zero) forms all 32 x 32 products at once, exactly in f32 (11 x 6 significant
+// bits), in the same output layout as the int8 MFMA's block dots, so the epilogue
+// is one conversion and one FMA per element instead of an integer multiply, a
+// conversion and an FMA.  The FMA still sees the exact product sc * D * dh.
+//   sc_byte   the lane's row (lane & 31) scale byte of the chunk
+//   dh_bits   the chunk's (dh, s) pair of the lane's token (lane & 31)
+//   b_mask    0xFFFF on lanes 0..31, else 0: only k = 0 of B is non-zero, so the
+//             other lanes' A values (k = 4) meet zeros
+__device__ __forceinline__ v16f scale_outer(uint32_t sc_byte, uint32_t dh_bits, uint32_t b_mask) {
+  typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+  const _Float16 sch = (_Float16)(uint16_t)sc_byte;
+  const v2i a = {(int)(uint32_t)__builtin_bit_cast(uint16_t, sch), 0};
+  const v2i b = {(int)(dh_bits & b_mask), 0};
+  const v16f zero = {};
+  return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, a), __builtin_bit_cast(v4h, b), zero,
+                                              0, 0, 0);
+}
 
 // Work-group index -> (row tile, token tile).  Work-groups are dispatched
 // round-robin over the 8 XCDs (each with its own 4 MiB L2), so first every XCD
@@ -359,6 +377,11 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   // they pass, half hh of the lanes during the super-block's stage hh.
   v2i bs = {};
   const bool lane_hi = lane >= 32;
+  // q4_K scale bytes: row (lane & 31) of a chunk's 32 sits at this byte (the plane
+  // orders them as a lane half of the block-dot output needs them)
+  const int jr = lane & 31;
+  const int sc_row = 16 * ((jr >> 2) & 1) + 4 * (jr >> 3) + (jr & 3);
+  const uint32_t b_mask = lane_hi ? 0u : 0xFFFFu;
 
   if (nstages > 0) issue_stage(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -380,13 +403,12 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         // the scale epilogue of chunk cc on the vector ALU while the matrix core
         // works.  Every LDS value is consumed one step after its read, so a wait
         // for it never waits for the reads just issued.
-        const int sc_off = 16 * (lane >> 5);
         uint32_t dhr = st.s[wt][0][lane & 31], dhr_even = 0;
         v2i amin = {};
         if constexpr (TYPE == QMM_Q4_K)
           if (h == kStagesPerSb - 1) amin = *(const v2i*)(&st.mn[wr][lane & 31][4 * (lane >> 5)]);
-        v4i scv = {};
-        if constexpr (TYPE == QMM_Q4_K) scv = *(const v4i*)(&st.sc[wr][0][sc_off]);
+        uint32_t scb = 0;
+        if constexpr (TYPE == QMM_Q4_K) scb = st.sc[wr][0][sc_row];
         typename W::A a0 = W::load(st.a[wr][0], lane);
         v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
         typename W::A a1 = W::load(st.a[wr][1], lane);
@@ -395,6 +417,13 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int cc = 0; cc < KC; ++cc) {
+          // q4_K: the scale products of chunk cc, first, so they are ready for
+          // this step's epilogue
+          v16f sd;
+          if constexpr (TYPE == QMM_Q4_K) {
+            sd = scale_outer(scb, dhr, b_mask);
+            pin(sd);
+          }
           typename W::D dj_next;
           if (cc + 1 < KC) {
             dj_next = W::mma(a1, bq1);
@@ -414,11 +443,10 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
             a2 = W::load(st.a[wr][cc + 2], lane);
             bq2 = *(const v4i*)(st.b[wt][cc + 2] + lane * 16);
           }
-          uint32_t dhr_next = 0;
-          v4i scv_next = {};
+          uint32_t dhr_next = 0, scb_next = 0;
           if (cc + 1 < KC) {
             dhr_next = st.s[wt][cc + 1][lane & 31];
-            if constexpr (TYPE == QMM_Q4_K) scv_next = *(const v4i*)(&st.sc[wr][cc + 1][sc_off]);
+            if constexpr (TYPE == QMM_Q4_K) scb_next = st.sc[wr][cc + 1][sc_row];
           }
           if constexpr (TYPE == QMM_Q4_K) {
             if (cc & 1) {  // the scaled sums of chunks cc-1 and cc as an f16 pair
@@ -434,18 +462,28 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
                                                         __builtin_bit_cast(v4h, bs), zero, 0, 0, 0);
             }
           }
-          // dh converted to f32 once per chunk and kept in a register, so the 16
-          // scale FMAs are plain v_fma_f32, which issue at twice the rate of
-          // the mixed-precision v_fma_mix_f32 the compiler would otherwise fold
-          // the f16 operand into
-          float dh = f16_bits_to_float(dhr & 0xFFFF);
-          pin(dh);
-          if (cc == 0 && starts_sb) {
+          if constexpr (TYPE == QMM_Q4_K) {
+            if (cc == 0 && starts_sb) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) inner[i] = (float)W::dot(dj, scv, i) * dh;
+              for (int i = 0; i < 16; ++i) inner[i] = (float)W::dot(dj, {}, i) * sd[i];
+            } else {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)W::dot(dj, {}, i), sd[i], inner[i]);
+            }
           } else {
+            // dh converted to f32 once per chunk and kept in a register, so the 16
+            // scale FMAs are plain v_fma_f32, which issue at twice the rate of
+            // the mixed-precision v_fma_mix_f32 the compiler would otherwise fold
+            // the f16 operand into
+            float dh = f16_bits_to_float(dhr & 0xFFFF);
+            pin(dh);
+            if (cc == 0 && starts_sb) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)W::dot(dj, scv, i), dh, inner[i]);
+              for (int i = 0; i < 16; ++i) inner[i] = (float)W::dot(dj, {}, i) * dh;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)W::dot(dj, {}, i), dh, inner[i]);
+            }
           }
           pin(inner);
           if (cc + 1 < KC) {
@@ -453,10 +491,11 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
             a1 = a2;
             bq1 = bq2;
             dhr = dhr_next;
-            scv = scv_next;
+            scb = scb_next;
           }
           // order inside the step: MFMAs, stage copies, LDS reads, the vector epilogue
-          __builtin_amdgcn_sched_group_barrier(0x008, W::kMfma, 0);  // MFMA (next chunk)
+          // MFMA: q4_K's scale products of this chunk, then the next chunk's block dots
+          __builtin_amdgcn_sched_group_barrier(0x008, W::kMfma + (TYPE == QMM_Q4_K), 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);         // VMEM (stage copies)
           __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);         // DS reads
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA (q4_K min term)

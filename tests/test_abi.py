@@ -118,6 +118,17 @@ def test_quantize_rejects_bad_arguments():
     assert L.qmm_quantize_activations(good, 4, 256, ctypes.c_void_p(4104), n, None) == qmm.EINVAL
     assert L.qmm_quantize_activations(good, 4, 256, good, n - 1, None) == qmm.EINVAL
     assert "qact_bytes" in qmm.last_error()
+    assert L.qmm_quantize_activations(good, -1, 256, good, 0, None) == qmm.EINVAL
+
+
+def test_quantize_empty_batch_is_a_no_op():
+    """n_tok = 0 is valid: nothing to write, no pointer or device is touched (so
+    it succeeds without a GPU); a non-zero qact_bytes or a bad id still fails."""
+    L = qmm._lib
+    assert L.qmm_quantize_activations(None, 0, 256, None, 0, None) == qmm.OK
+    assert qmm.last_error() == ""
+    assert L.qmm_quantize_activations(None, 0, 256, None, 16, None) == qmm.EINVAL
+    assert L.qmm_quantize_activations(None, 0, 300, None, 0, None) == qmm.EINVAL
 
 
 def test_mmq_rejects_bad_arguments():

@@ -466,3 +466,20 @@ def test_shape_mismatch_and_memory_cap():
     w2 = qmm.register_weights(synth.Q6_K, 8, 512, raw)
     w2.release()
     w.release()
+
+
+def test_empty_batch_is_a_no_op():
+    """n_tok = 0 through the binding: an empty qact and an empty output, nothing
+    launched; the handle still serves a normal call afterwards."""
+    say("empty batch")
+    raw, x = synth.case(synth.Q4_K, 40, 512, 3, seed=2)
+    w = qmm.register_weights(synth.Q4_K, 40, 512, raw)
+    qa0 = qmm.quantize_activations(torch.empty((0, 512), dtype=torch.float32, device="cuda"))
+    assert qa0.numel() == 0
+    out0 = qmm.mmq(w, qa0, 0)
+    assert tuple(out0.shape) == (0, 40)
+    qact = gpu_quantize(x)
+    q, dh, s = check_prepass(x, qact)
+    ref, A = oracle.mmq(synth.Q4_K, raw, 40, 512, q, dh, s)
+    check_close(run_mmq(w, qact, 3), ref, A, "after an empty batch")
+    w.release()
