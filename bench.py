@@ -39,8 +39,22 @@ import synth  # noqa: E402
 
 MFMA_INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
 # The vector-ALU roof of the scale epilogue: each (token, row, 32-block) takes 64
-# int8 MFMA ops and 3 VALU instructions, 256 CUs x 64 lanes x 2.4 GHz lane-ops/s.
-VALU_EPILOGUE_PEAK_TOPS = 256 * 64 * 2.4e9 * 64 / 3 / 1e12
+# int8 MFMA ops and, on the vector ALU, 3 instructions for q6_K (join the two
+# plane dots, convert, FMA) or 2 for q4_K (convert, FMA: its scale product comes
+# from the matrix core), at 256 CUs x 64 lanes x 2.4 GHz lane-instructions/s.
+EPILOGUE_INSTRS = {synth.Q6_K: 3, synth.Q4_K: 2}
+VALU_LANE_OPS = 256 * 64 * 2.4e9
+
+
+def epilogue_roof(gemms, T, tops_of_type):
+    """The roof of a step whose GEMMs have different epilogue roofs: its total
+    ops over the sum of each GEMM's time at its own type's roof."""
+    ops = [2.0 * T * od * id_ for _, _, od, id_, _ in gemms]
+    return sum(ops) / sum(o / tops_of_type(t) for o, (_, t, _, _, _) in zip(ops, gemms))
+
+
+def nominal_epilogue_tops(type_):
+    return VALU_LANE_OPS * 64 / EPILOGUE_INSTRS[type_] / 1e12
 HBM_PEAK_GBS = 8000.0
 COLD_BYTES = 512 << 20         # weight planes cycled per cold pass: twice the 256 MB cache
 
@@ -128,9 +142,9 @@ def measured_traffic(workload: str):
 
 
 def calibrate(torch, stream):
-    """Measured roofs on this GPU: the int8 MFMA rate and the vector-ALU rate of
-    the MMQ's scale epilogue (3 instructions per (token, row, 32-block), 64 int8
-    ops each), from the calibration kernels in libqmm_peak.so, with the shader
+    """Measured roofs on this GPU: the int8 MFMA rate and the vector-ALU rates of
+    the MMQ's scale epilogues (q6_K 3 and q4_K 2 instructions per (token, row,
+    32-block), 64 int8 ops each), from the calibration kernels in libqmm_peak.so, with the shader
     clock (s_memtime against the 100 MHz s_memrealtime) during each run.  Each
     is the best over a few occupancies, timed with HIP events on `stream`."""
     import ctypes
@@ -144,7 +158,8 @@ def calibrate(torch, stream):
     out = {}
     # kind, name, work-groups per CU tried, SIMD cycles per wave-iteration, int8 ops per wave-iteration
     for kind, name, per_cu, cyc, ops_it in ((0, "mfma_i8", (1, 2, 3), 128, 4 * 65536),
-                                            (1, "epilogue_valu", (2, 4, 8), 192, 65536)):
+                                            (1, "epilogue_valu", (2, 4, 8), 192, 65536),
+                                            (2, "epilogue_valu_q4k", (2, 4, 8), 128, 65536)):
         best = None
         for g in per_cu:
             grid = g * n_cu
@@ -357,6 +372,7 @@ def main():
     ops = sum(2.0 * T * od * id_ for _, _, od, id_, _ in gemms)
     mmq_avg_s = mmq_ms / 1e3
     mmq_tops = ops / mmq_avg_s / 1e12
+    epi_nominal = epilogue_roof(gemms, T, nominal_epilogue_tops)
     pre_bytes = sum(T * id_ * 4 + qmm.qact_bytes(T, id_) for id_ in inputs.values())
     alg_bytes = sum(weights[g].plane_bytes + T * id_ * 9 // 8 + T * od * 4
                     for g, _, od, id_, _ in gemms)
@@ -411,9 +427,9 @@ def main():
             "algorithmic_bytes_per_step": alg_bytes,
             "kernel_sha256_16": kernel_hash(),
             # the roof that binds by design: the per-32-block scale epilogue
-            "epilogue_roof": {"bound": "alu", "peak": round(VALU_EPILOGUE_PEAK_TOPS, 1),
+            "epilogue_roof": {"bound": "alu", "peak": round(epi_nominal, 1),
                               "unit": "TOP/s (int8-equivalent)",
-                              "frac": round(mmq_tops / VALU_EPILOGUE_PEAK_TOPS, 4)},
+                              "frac": round(mmq_tops / epi_nominal, 4)},
         },
         "plane_bytes": sum(w.plane_bytes for w in weights.values()),
         "raw_weight_bytes": sum(w.raw_bytes for w in weights.values()),
@@ -430,8 +446,10 @@ def main():
             rl = result["roofline"]
             rl["measured_peak"] = cal["mfma_i8"]["tops"]
             rl["frac_of_measured_peak"] = round(mmq_tops / cal["mfma_i8"]["tops"], 4)
-            rl["epilogue_roof"]["measured"] = cal["epilogue_valu"]["tops"]
-            rl["epilogue_roof"]["frac_of_measured"] = round(mmq_tops / cal["epilogue_valu"]["tops"], 4)
+            measured = {synth.Q6_K: cal["epilogue_valu"]["tops"], synth.Q4_K: cal["epilogue_valu_q4k"]["tops"]}
+            epi_measured = epilogue_roof(gemms, T, measured.get)
+            rl["epilogue_roof"]["measured"] = round(epi_measured, 1)
+            rl["epilogue_roof"]["frac_of_measured"] = round(mmq_tops / epi_measured, 4)
     if not args.no_cpu:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         result["cpu_baseline"] = cpu_baseline(gemms, raws, xs, T, threads, args.cpu_macs)

@@ -2,11 +2,14 @@
 // reports next to the MMQ: the rate this GPU reaches on
 //   kind 0: the int8 matrix core, back-to-back v_mfma_i32_32x32x32_i8 with
 //           four independent accumulators per wave (no memory traffic);
-//   kind 1: the vector ALU running the MMQ's per-block scale epilogue, the
-//           same three instructions per (token, row, 32-block) -- combine the
-//           two plane dots (v_lshl_add_u32), convert (v_cvt_f32_i32), scale
+//   kind 1: the vector ALU running the q6_K MMQ's per-block scale epilogue,
+//           the same three instructions per (token, row, 32-block) -- combine
+//           the two plane dots (v_lshl_add_u32), convert (v_cvt_f32_i32), scale
 //           and accumulate with the activation scale held as f32 (v_fmac_f32)
-//           -- on 16 elements per lane.
+//           -- on 16 elements per lane;
+//   kind 2: the q4_K MMQ's epilogue, two instructions per element -- convert
+//           the block dot (v_cvt_f32_i32), multiply by the element's own f32
+//           scale and accumulate (v_fmac_f32) -- on 16 elements per lane.
 // Work-group 0's first wave also records the shader clock (s_memtime) and the
 // 100 MHz constant clock (s_memrealtime) across its run, so the caller can
 // state the clock the rates were measured at.  These kernels are measurement
@@ -81,20 +84,45 @@ __global__ void __launch_bounds__(256) peak_epilogue(int iters, unsigned long lo
   sink[blockIdx.x * blockDim.x + threadIdx.x] = __builtin_bit_cast(int, s);
 }
 
+__global__ void __launch_bounds__(256) peak_epilogue_q4(int iters, unsigned long long* clk, int* sink) {
+  const int lane = threadIdx.x & 63;
+  float acc[16], sc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    acc[i] = (float)(lane + i);
+    sc[i] = 0x1p-40f * (float)(lane + i + 1);  // in registers, as in the MMQ; keeps acc finite
+  }
+  uint64_t t = 0, r = 0;
+  clock_start(t, r);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)  // the converted integer is acc's bit pattern: it changes every step
+      acc[i] = fmaf((float)__builtin_bit_cast(int, acc[i]), sc[i], acc[i]);
+  }
+  clock_end(t, r, clk);
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += acc[i];
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = __builtin_bit_cast(int, s);
+}
+
 }  // namespace
 
 // Launches `grid` work-groups of 256 threads of calibration kernel `kind`
-// (0: int8 MFMA, 1: scale epilogue) for `iters` iterations on `stream`.
+// (0: int8 MFMA, 1: q6_K scale epilogue, 2: q4_K scale epilogue) for `iters`
+// iterations on `stream`.
 // clk: device uint64[2] (shader clocks, 100 MHz ticks of work-group 0's first
 // wave); sink: device int32[grid * 256].  Each iteration is, per wave, 4 MFMAs
-// of 32x32x32 (kind 0) or 16 epilogue elements per lane (kind 1): 262144 or
-// 65536 int8-equivalent operations.  Returns 0 or the hipError_t of the launch.
+// of 32x32x32 (kind 0) or 16 epilogue elements per lane (kinds 1, 2): 262144
+// or 65536 int8-equivalent operations.  Returns 0 or the hipError_t of the launch.
 extern "C" int qmm_peak_launch(int kind, int iters, int grid, void* clk, void* sink, void* stream) {
-  if (kind < 0 || kind > 1 || iters < 1 || grid < 1 || !clk || !sink) return (int)hipErrorInvalidValue;
+  if (kind < 0 || kind > 2 || iters < 1 || grid < 1 || !clk || !sink) return (int)hipErrorInvalidValue;
   hipStream_t s = (hipStream_t)stream;
   if (kind == 0)
     peak_mfma_i8<<<dim3((unsigned)grid), dim3(256), 0, s>>>(iters, (unsigned long long*)clk, (int*)sink);
-  else
+  else if (kind == 1)
     peak_epilogue<<<dim3((unsigned)grid), dim3(256), 0, s>>>(iters, (unsigned long long*)clk, (int*)sink);
+  else
+    peak_epilogue_q4<<<dim3((unsigned)grid), dim3(256), 0, s>>>(iters, (unsigned long long*)clk, (int*)sink);
   return (int)hipGetLastError();
 }

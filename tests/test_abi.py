@@ -164,7 +164,8 @@ def test_calibration_library_loads_and_validates():
     f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_void_p]
     good = ctypes.c_void_p(4096)
-    assert f(2, 10, 1, good, good, None) == 1
+    assert f(3, 10, 1, good, good, None) == 1
+    assert f(-1, 10, 1, good, good, None) == 1
     assert f(0, 0, 1, good, good, None) == 1
     assert f(1, 10, 0, good, good, None) == 1
     assert f(0, 10, 1, None, good, None) == 1

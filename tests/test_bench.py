@@ -45,3 +45,4 @@ def test_bench_json_line_contract():
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
     cal = d["calibration"]
     assert cal["mfma_i8"]["tops"] > 0 and cal["epilogue_valu"]["tops"] > 0
+    assert cal["epilogue_valu_q4k"]["tops"] > 0 and rl["epilogue_roof"]["measured"] > 0
