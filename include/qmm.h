@@ -80,7 +80,7 @@ typedef struct {
     size_t wd_offset;    /* byte offset of the d plane inside the planes */
     size_t mn_offset;    /* byte offset of the min plane (q4_K; else == plane_bytes) */
     size_t dm_offset;    /* byte offset of the dmin plane (q4_K; else == plane_bytes) */
-    size_t sc_offset;    /* byte offset of the scale-byte plane (q4_K; else == plane_bytes) */
+    size_t sc_offset;    /* byte offset of the f16 scale plane (q4_K; else == plane_bytes) */
 } qmm_info;
 
 /*
@@ -126,9 +126,9 @@ int qmm_weights_info(const qmm_weights *w, qmm_info *out);
  *                 as an f16 integer, q4_K only, at element
  *                 ((j/32*nsb + c/8)*32 + j%32)*8 + c%8
  *   at dm_offset  f32 [R][nsb][32]: dmin of (row, super-block), q4_K only
- *   at sc_offset  uint8 [R][nchunk][32]: the 6-bit scale of (row j, chunk c),
- *                 q4_K only, at byte (j/32*nchunk + c)*32 + 16*((j/4)%2)
- *                 + 4*((j%32)/8) + j%4
+ *   at sc_offset  binary16 [R][nsb][32][8]: the 6-bit scale of (row j, chunk
+ *                 c) as an f16 integer, q4_K only, at element
+ *                 ((j/32*nsb + c/8)*32 + j%32)*8 + c%8 (the layout of the mins)
  * Errors: QMM_EINVAL (null pointers, bytes mismatch), QMM_EHIP.
  */
 int qmm_weights_export(const qmm_weights *w, void *host, size_t bytes);

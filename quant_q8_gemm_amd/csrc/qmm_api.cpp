@@ -162,7 +162,7 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   p.wd = (float*)((char*)alloc + off_wd);
   p.wmn = type == QMM_Q4_K ? (uint16_t*)((char*)alloc + off_mn) : nullptr;
   p.wdm = type == QMM_Q4_K ? (float*)((char*)alloc + off_dm) : nullptr;
-  p.wsc = type == QMM_Q4_K ? (uint8_t*)alloc + off_sc : nullptr;
+  p.wsc = type == QMM_Q4_K ? (uint16_t*)((uint8_t*)alloc + off_sc) : nullptr;
   int rc = QMM_OK;
   if ((e = hipMemcpyAsync(raw, host_bytes, nbytes, hipMemcpyHostToDevice, s)) != hipSuccess)
     rc = fail_hip(e, "hipMemcpyAsync(weights)");

@@ -20,7 +20,7 @@ struct Planes {
   float* wd;         // d per (row, super-block)
   uint16_t* wmn;     // min per (row, chunk) as f16, super-block-major; q4_K only, else nullptr
   float* wdm;        // dmin per (row, super-block); q4_K only, else nullptr
-  uint8_t* wsc;      // 6-bit scale per (row, chunk) as bytes; q4_K only, else nullptr
+  uint16_t* wsc;     // 6-bit scale per (row, chunk) as f16, super-block-major; q4_K only, else nullptr
 };
 
 constexpr int kRowPad = 128;     // weight rows are padded to a multiple of this

@@ -15,8 +15,9 @@
 //    folded weight split into two int8 planes (hi = w >> 6, lo = w & 63), so one
 //    K=32 int8 MFMA per plane gives J = 64*J_hi + J_lo.  q4_K (one 6-bit scale
 //    per 32-block): the 4-bit codes stay codes (packed two per byte), one K=32
-//    MFMA gives the code dot D, and J = sc*D is one 24-bit integer multiply
-//    whose scale byte the instruction selects itself (SDWA);
+//    MFMA gives the code dot D, and the products sc(row)*dh(token) of the
+//    block's scale and the activation scale come from one small f16 MFMA (an
+//    outer product), so each element costs a conversion and an FMA;
 //  * planes are stored in MFMA fragment order, so every lane's operand is one
 //    contiguous 16-byte (q4_K codes: 8-byte) load and a wave's load is one
 //    contiguous 1 KiB (512 bytes);
@@ -43,7 +44,7 @@ namespace qmm {
 // stages of KC chunks of 32 (KC = 2, 4 or 8: a quarter, half or whole 256-wide
 // super-block).  Each stage's operands -- the weight fragments of the WR row
 // blocks, the q8 codes and scale pairs of the WT token blocks, and d (and for
-// q4_K the scale bytes, the mins and dmin) -- are copied once per
+// q4_K the scales, the mins and dmin) -- are copied once per
 // work-group into LDS with direct global->LDS loads (global_load_lds_dwordx4
 // puts lane l's 16 bytes at the LDS base + 16*l, so one wave instruction moves
 // 1 KiB), and read from there by every wave that shares them.  Two LDS stages
@@ -85,13 +86,14 @@ struct alignas(16) Stage {
   int8_t a[WR][KC][kFragA<TYPE>];    // weight fragments: [row block][chunk]
   int8_t b[WT][KC][1024];            // q8 codes: [token block][chunk][fragment]
   uint32_t s[WT][KC][32];            // (dh, s) pairs: [token block][chunk][token]
-  uint8_t sc[kQ4 ? WR : 0][KC][32];  // scale bytes: [row block][chunk][lane half][16]; q4_K only
+  uint16_t sc[kQ4 ? WR : 0][32][8];  // super-block scales as f16: [row block][row][chunk]; q4_K only
   float d[WR][32];                   // super-block d: [row block][row]
   uint16_t mn[kQ4 ? WR : 0][32][8];  // super-block mins as f16: [row block][row][chunk]; q4_K only
   float dm[kQ4 ? WR : 0][32];        // super-block dmin: [row block][row]; q4_K only
   // s, sc, d, mn and dm are contiguous: the "small" region, copied in 16-byte
-  // units (s and sc with every stage, d, mn and dm with a super-block's last).
-  static constexpr int kUnitsS = WT * KC * 8, kUnitsSc = kQ4 ? WR * KC * 2 : 0, kUnitsD = WR * 8,
+  // units (s with every stage, sc with a super-block's first, d, mn and dm with
+  // its last).
+  static constexpr int kUnitsS = WT * KC * 8, kUnitsSc = kQ4 ? WR * 32 : 0, kUnitsD = WR * 8,
                        kUnitsMn = kQ4 ? WR * 32 : 0, kUnitsDm = kQ4 ? WR * 8 : 0;
   static constexpr int kUnits = kUnitsS + kUnitsSc + kUnitsD + kUnitsMn + kUnitsDm;
   static constexpr int kSmallJobs = (kUnits + 63) / 64;
@@ -143,22 +145,26 @@ struct WeightOps<QMM_Q4_K> {
 
 // q4_K: the scale of output element (row j, token t) of chunk c is sc(j, c) * dh(t, c),
 // an outer product of a row vector and a token vector, each an exact f16 value (a
-// 6-bit integer, the f16 activation scale).  One f16 MFMA (32x32x8, only k = 0
-// non-zero) forms all 32 x 32 products at once, exactly in f32 (11 x 6 significant
-// bits), in the same output layout as the int8 MFMA's block dots, so the epilogue
-// is one conversion and one FMA per element instead of an integer multiply, a
-// conversion and an FMA.  The FMA still sees the exact product sc * D * dh.
-//   sc_byte   the lane's row (lane & 31) scale byte of the chunk
+// 6-bit integer, the f16 activation scale).  One f16 MFMA (32x32x8) forms all
+// 32 x 32 products at once, exactly in f32 (11 x 6 significant bits), in the same
+// output layout as the int8 MFMA's block dots, so the epilogue is one conversion
+// and one FMA per element instead of an integer multiply, a conversion and an
+// FMA.  The FMA still sees the exact product sc * D * dh.
+// A holds the scales of all 8 chunks of the super-block (k = chunk: the row's
+// 8 f16 scales, lane half h giving chunks 4h..4h+3); B holds the chunk's dh at
+// k = chunk and zeros elsewhere, so the sum over k keeps just that chunk's
+// product.  ci is the chunk's index in the super-block (a constant once the
+// chunk loops are unrolled).
+//   a_sc      the lane's 4 f16 scales (row lane & 31, chunks 4*(lane/32)..+3)
 //   dh_bits   the chunk's (dh, s) pair of the lane's token (lane & 31)
-//   b_mask    0xFFFF on lanes 0..31, else 0: only k = 0 of B is non-zero, so the
-//             other lanes' A values (k = 4) meet zeros
-__device__ __forceinline__ v16f scale_outer(uint32_t sc_byte, uint32_t dh_bits, uint32_t b_mask) {
+//   b_mask    0xFFFF on the lanes of half ci/4, else 0
+__device__ __forceinline__ v16f scale_outer(v2i a_sc, uint32_t dh_bits, uint32_t b_mask, int ci) {
   typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-  const _Float16 sch = (_Float16)(uint16_t)sc_byte;
-  const v2i a = {(int)(uint32_t)__builtin_bit_cast(uint16_t, sch), 0};
-  const v2i b = {(int)(dh_bits & b_mask), 0};
+  const uint32_t x = dh_bits & b_mask;
+  const uint32_t w = ci % 2 == 0 ? x : x << 16;
+  const v2i b = {ci % 4 < 2 ? (int)w : 0, ci % 4 < 2 ? 0 : (int)w};
   const v16f zero = {};
-  return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, a), __builtin_bit_cast(v4h, b), zero,
+  return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, a_sc), __builtin_bit_cast(v4h, b), zero,
                                               0, 0, 0);
 }
 
@@ -296,8 +302,9 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
                         (size_t)gbeg * KC * 1024;
   const uint32_t lane_off = (uint32_t)lane * 16;
   const uint8_t* small_src = nullptr;
-  // 0 none; per stage: 1 pairs (128 bytes per chunk), 3 scale bytes (32 per
-  // chunk); per super-block: 2 d or dmin (128 bytes), 4 mins (512 bytes)
+  // 0 none; per stage: 1 pairs (128 bytes per chunk); per super-block: 3 scales
+  // (512 bytes, at its first stage), 2 d or dmin (128 bytes), 4 mins (512 bytes)
+  // (at its last)
   int small_kind = 0;
   if (wave < St::kSmallJobs) {
     const int u = wave * 64 + lane;
@@ -308,7 +315,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
       small_kind = 1;
     } else if (u < eSc) {
       const int v = u - St::kUnitsS;
-      small_src = wsc + ((size_t)(rb0 + v / (KC * 2)) * nchunk + gbeg * KC) * 32 + (v % (KC * 2)) * 16;
+      small_src = wsc + ((size_t)(rb0 + v / 32) * nsb + sb0g) * 512 + (v % 32) * 16;
       small_kind = 3;
     } else if (u < eD) {
       const int v = u - eSc;
@@ -350,11 +357,11 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
                        lds_buf + (uint32_t)__builtin_offsetof(St, b) + (kb0 + u) * 1024);
     } else if (wave < St::kSmallJobs) {
       const uint32_t ls = lds_buf + (uint32_t)__builtin_offsetof(St, s) + wave * 1024;
-      const bool ends_sb = ((g + 1) * KC) % 8 == 0;
+      const bool ends_sb = ((g + 1) * KC) % 8 == 0, starts_sb = (g * KC) % 8 == 0;
       if (small_kind == 1)
         copy16_lane(small_src + (size_t)g * KC * 128, ls);
-      else if (small_kind == 3)
-        copy16_lane(small_src + (size_t)g * KC * 32, ls);
+      else if (small_kind == 3 && starts_sb)
+        copy16_lane(small_src + (size_t)((g * KC) / 8) * 512, ls);
       else if (small_kind == 2 && ends_sb)
         copy16_lane(small_src + (size_t)((g * KC) / 8) * 128, ls);
       else if (small_kind == 4 && ends_sb)
@@ -377,11 +384,10 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   // they pass, half hh of the lanes during the super-block's stage hh.
   v2i bs = {};
   const bool lane_hi = lane >= 32;
-  // q4_K scale bytes: row (lane & 31) of a chunk's 32 sits at this byte (the plane
-  // orders them as a lane half of the block-dot output needs them)
-  const int jr = lane & 31;
-  const int sc_row = 16 * ((jr >> 2) & 1) + 4 * (jr >> 3) + (jr & 3);
-  const uint32_t b_mask = lane_hi ? 0u : 0xFFFFu;
+  // q4_K scale products: the super-block's scales (A operand) and the dh masks
+  // of the two lane halves
+  v2i a_sc = {};
+  const uint32_t b_mask0 = lane_hi ? 0u : 0xFFFFu, b_mask1 = lane_hi ? 0xFFFFu : 0u;
 
   if (nstages > 0) issue_stage(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -407,8 +413,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         v2i amin = {};
         if constexpr (TYPE == QMM_Q4_K)
           if (h == kStagesPerSb - 1) amin = *(const v2i*)(&st.mn[wr][lane & 31][4 * (lane >> 5)]);
-        uint32_t scb = 0;
-        if constexpr (TYPE == QMM_Q4_K) scb = st.sc[wr][0][sc_row];
+        if constexpr (TYPE == QMM_Q4_K)
+          if (h == 0) a_sc = *(const v2i*)(&st.sc[wr][lane & 31][4 * (lane >> 5)]);
         typename W::A a0 = W::load(st.a[wr][0], lane);
         v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
         typename W::A a1 = W::load(st.a[wr][1], lane);
@@ -421,7 +427,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
           // this step's epilogue
           v16f sd;
           if constexpr (TYPE == QMM_Q4_K) {
-            sd = scale_outer(scb, dhr, b_mask);
+            sd = scale_outer(a_sc, dhr, h == 0 ? b_mask0 : b_mask1, KC * h + cc);
             pin(sd);
           }
           typename W::D dj_next;
@@ -443,11 +449,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
             a2 = W::load(st.a[wr][cc + 2], lane);
             bq2 = *(const v4i*)(st.b[wt][cc + 2] + lane * 16);
           }
-          uint32_t dhr_next = 0, scb_next = 0;
-          if (cc + 1 < KC) {
-            dhr_next = st.s[wt][cc + 1][lane & 31];
-            if constexpr (TYPE == QMM_Q4_K) scb_next = st.sc[wr][cc + 1][sc_row];
-          }
+          uint32_t dhr_next = 0;
+          if (cc + 1 < KC) dhr_next = st.s[wt][cc + 1][lane & 31];
           if constexpr (TYPE == QMM_Q4_K) {
             if (cc & 1) {  // the scaled sums of chunks cc-1 and cc as an f16 pair
               const int sp = (int)__builtin_amdgcn_perm(dhr, dhr_even, 0x07060302u);
@@ -491,7 +494,6 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
             a1 = a2;
             bq1 = bq2;
             dhr = dhr_next;
-            scb = scb_next;
           }
           // order inside the step: MFMAs, stage copies, LDS reads, the vector epilogue
           // MFMA: q4_K's scale products of this chunk, then the next chunk's block dots
@@ -582,7 +584,7 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
   const int vec_store = (p.od % 4 == 0) && ((uintptr_t)out % 16 == 0);
   const int64_t wgs = plan.work_groups;
   mmq_kernel<TYPE, WR, WT, KC, KS><<<dim3((unsigned)wgs), dim3(64 * WR * WT * KS), 0, s>>>(
-      p.wq, p.wd, (const uint8_t*)p.wmn, p.wdm, p.wsc, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
+      p.wq, p.wd, (const uint8_t*)p.wmn, p.wdm, (const uint8_t*)p.wsc, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
       plan.dp_row_tiles, plan.split, vec_store, out, scratch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_tail == 0) return e;

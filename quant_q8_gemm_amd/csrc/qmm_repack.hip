@@ -6,8 +6,9 @@
 // weights is multiplied into the codes (exact) and the folded weight split into
 // two int8 planes (hi = w >> 6, lo = w & 63), so one K=32 int8 MFMA per plane
 // yields the block dot J = 64*J_hi + J_lo; q4_K's 6-bit scale of every 32 weights
-// goes to a byte plane that the GEMM multiplies into the code dot, and its codes
-// stay 4-bit, two per byte.  Only the f16 d of the super-block stays a float.
+// goes to an f16 plane (integers 0..63, exact) from which the GEMM forms the
+// scale product with the activation scale, and its codes stay 4-bit, two per
+// byte.  Only the f16 d of the super-block stays a float.
 #include "qmm_internal.h"
 #include "qmm_common.h"
 
@@ -30,9 +31,9 @@ namespace qmm {
 //   wmn f16   [R][nsb][32 rows][8]   the 6-bit min of (row, chunk) as an f16
 //             integer, at ((j/32*nsb + c/8)*32 + j%32)*8 + c%8; q4_K only
 //   wdm f32   [R][nsb][32 rows]      dmin of (row, super-block); q4_K only
-//   wsc uint8 [R][nchunk][32]        6-bit scale of (row, chunk), q4_K only, at
-//             16*((j/4)%2) + 4*((j%32)/8) + j%4: the 16 bytes a lane half of
-//             the MFMA output layout needs, in its register order
+//   wsc f16   [R][nsb][32 rows][8]   the 6-bit scale of (row, chunk) as an f16
+//             integer, at ((j/32*nsb + c/8)*32 + j%32)*8 + c%8 (the layout of
+//             wmn); q4_K only
 // Rows od..od_pad-1 are zero in every plane.
 // ---------------------------------------------------------------------------
 size_t wq_bytes(int type, int64_t od_pad, int64_t id) {
@@ -46,14 +47,14 @@ size_t wdm_bytes(int type, int64_t od_pad, int64_t id) {
   return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 256) * 4 : 0;
 }
 size_t wsc_bytes(int type, int64_t od_pad, int64_t id) {
-  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) : 0;
+  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) * 2 : 0;
 }
 
 // One thread per (row j in [0, od_pad), chunk c, k-half h): 16 weights.
 __global__ void __launch_bounds__(256)
 repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nchunk,
               int64_t total, int8_t* __restrict__ wq, float* __restrict__ wd,
-              uint16_t* __restrict__ wmn, float* __restrict__ wdm, uint8_t* __restrict__ wsc) {
+              uint16_t* __restrict__ wmn, float* __restrict__ wdm, uint16_t* __restrict__ wsc) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total) return;
   const int h = (int)(gid & 1);
@@ -64,7 +65,6 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
   const int b = c >> 3, cl = c & 7;
 
   uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};  // q6_K planes; q4_K codes in lo[0..1]
-  int sc4 = 0;                                            // q4_K scale
   if (j < od) {
     if (type == QMM_Q6_K) {
       // 210-byte block: ql[128] | qh[64] | int8 scales[16] | f16 d (r56 section 1)
@@ -108,10 +108,10 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
         const uint32_t packed = ((qs[b8] >> shift) & 15) | (((qs[b8 + 8] >> shift) & 15) << 4);
         lo[b8 >> 2] |= packed << (8 * (b8 & 3));
       }
-      sc4 = sc;
       if (h == 0) {
         wmn[(((int64_t)rb * nsb + b) * 32 + jr) * 8 + cl] =
             __builtin_bit_cast(uint16_t, (_Float16)(float)mn);  // 0..63: exact
+        wsc[(((int64_t)rb * nsb + b) * 32 + jr) * 8 + cl] = __builtin_bit_cast(uint16_t, (_Float16)(float)sc);
         if (cl == 0) {
           wd[((int64_t)rb * nsb + b) * 32 + jr] = f16_bits_to_float(B[0] | (B[1] << 8));
           wdm[((int64_t)rb * nsb + b) * 32 + jr] = f16_bits_to_float(B[2] | (B[3] << 8));
@@ -121,6 +121,7 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
   } else if (h == 0) {
     if (type == QMM_Q4_K) {
       wmn[(((int64_t)rb * nsb + b) * 32 + jr) * 8 + cl] = 0;
+      wsc[(((int64_t)rb * nsb + b) * 32 + jr) * 8 + cl] = 0;
       if (cl == 0) wdm[((int64_t)rb * nsb + b) * 32 + jr] = 0.0f;
     }
     if (cl == 0) wd[((int64_t)rb * nsb + b) * 32 + jr] = 0.0f;
@@ -132,8 +133,6 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
   } else {
     int8_t* dst = wq + ((int64_t)rb * nchunk + c) * kQ4CodeFrag + h * 256 + jr * 8;
     *(uint2*)dst = make_uint2(lo[0], lo[1]);
-    if (h == 0)
-      wsc[((int64_t)rb * nchunk + c) * 32 + 16 * ((jr >> 2) & 1) + 4 * (jr >> 3) + (jr & 3)] = (uint8_t)sc4;
   }
 }
 

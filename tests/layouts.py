@@ -42,12 +42,11 @@ def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: i
         pk = buf[: od_pad * id_ // 2].reshape(R, nchunk, 2, 32, 8)
         codes = np.concatenate([pk & 15, pk >> 4], axis=-1)          # [R][nchunk][h][row][16]
         codes = codes.transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
-        # scale byte of row j at 16*((j/4)%2) + 4*((j%32)/8) + j%4
-        scb = buf[sc_offset: sc_offset + od_pad * nchunk].reshape(R, nchunk, 32)
-        j = np.arange(32)
-        pos = 16 * ((j // 4) % 2) + 4 * (j // 8) + j % 4
-        sc = scb[:, :, pos].transpose(0, 2, 1).reshape(od_pad, nchunk).astype(np.int32)
-        assert sc.max() <= 63
+        # scales: binary16 [R][nsb][row][chunk of the super-block], like the mins
+        s16 = buf[sc_offset: sc_offset + od_pad * nchunk * 2].view("<f2").reshape(R, nsb, 32, 8)
+        sf = s16.astype(np.float64).transpose(0, 2, 1, 3).reshape(od_pad, nchunk)
+        assert np.all(sf == np.round(sf)) and sf.min() >= 0 and sf.max() <= 63
+        sc = sf.astype(np.int32)
         w = codes * np.repeat(sc, 32, axis=1)
     d = buf[wd_offset: wd_offset + od_pad * nsb * 4].view("<f4").reshape(R, nsb, 32)
     d = d.transpose(0, 2, 1).reshape(od_pad, nsb)
