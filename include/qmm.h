@@ -117,10 +117,9 @@ int qmm_weights_info(const qmm_weights *w, qmm_info *out);
  *                 (lo in [0, 63]), hi (plane index p = 0) and lo (p = 1) at byte
  *                 ((j/32*nchunk + k/32)*2 + p)*1024 + ((k%32)/16)*512
  *                 + (j%32)*16 + k%16
- *                 q4_K: uint8 [R][nchunk][2][32][8]: the 4-bit codes, two per
- *                 byte; with h = (k%32)/16 and b = k%8, code (j, k) is in byte
- *                 (j/32*nchunk + k/32)*512 + h*256 + (j%32)*8 + b, the low
- *                 nibble if k%16 < 8, else the high nibble
+ *                 q4_K: int8 [R][nchunk][2][32][16]: the 4-bit code (0..15)
+ *                 of (row j, k) at byte (j/32*nchunk + k/32)*1024
+ *                 + ((k%32)/16)*512 + (j%32)*16 + k%16
  *   at wd_offset  f32 [R][nsb][32]: d of (row, super-block)
  *   at mn_offset  binary16 [R][nsb][32][8]: the 6-bit min of (row j, chunk c)
  *                 as an f16 integer, q4_K only, at element

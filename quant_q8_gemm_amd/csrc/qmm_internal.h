@@ -16,7 +16,7 @@ struct Planes {
   int64_t od_pad;    // rows padded to kRowPad
   int64_t nsb;       // id / 256
   int64_t nchunk;    // id / 32
-  int8_t* wq;        // weight fragments in MFMA order: q6_K folded hi/lo, q4_K packed codes
+  int8_t* wq;        // weight fragments in MFMA order: q6_K folded hi/lo, q4_K codes
   float* wd;         // d per (row, super-block)
   uint16_t* wmn;     // min per (row, chunk) as f16, super-block-major; q4_K only, else nullptr
   float* wdm;        // dmin per (row, super-block); q4_K only, else nullptr
@@ -25,7 +25,7 @@ struct Planes {
 
 constexpr int kRowPad = 128;     // weight rows are padded to a multiple of this
 constexpr int kTokenPad = 128;   // tokens are padded to a multiple of this
-constexpr int kQ4CodeFrag = 512; // q4_K code bytes per (32-row block, chunk): two codes per byte
+constexpr int kQ4CodeFrag = 1024; // q4_K code bytes per (32-row block, chunk): one code per byte
 
 // Byte sizes of the planes for a shape (all offsets 256-byte aligned).
 size_t wq_bytes(int type, int64_t od_pad, int64_t id);

@@ -14,13 +14,12 @@
 //    scales): the scale is multiplied into the codes at registration and the
 //    folded weight split into two int8 planes (hi = w >> 6, lo = w & 63), so one
 //    K=32 int8 MFMA per plane gives J = 64*J_hi + J_lo.  q4_K (one 6-bit scale
-//    per 32-block): the 4-bit codes stay codes (packed two per byte), one K=32
-//    MFMA gives the code dot D, and the products sc(row)*dh(token) of the
+//    per 32-block): the 4-bit codes are int8 bytes, one K=32 MFMA gives the
+//    code dot D, and the products sc(row)*dh(token) of the
 //    block's scale and the activation scale come from one small f16 MFMA (an
 //    outer product), so each element costs a conversion and an FMA;
 //  * planes are stored in MFMA fragment order, so every lane's operand is one
-//    contiguous 16-byte (q4_K codes: 8-byte) load and a wave's load is one
-//    contiguous 1 KiB (512 bytes);
+//    contiguous 16-byte load and a wave's load is one contiguous 1 KiB;
 //  * the q4_K min term sum_c dmin*min_c*s_c is a small matrix product over
 //    chunks: per super-block, sum_c min_c*s_c on one f16 MFMA (32x32x8; the
 //    6-bit mins and the f16 scaled sums are exact f16 operands), times dmin
@@ -76,7 +75,7 @@ __device__ __forceinline__ void copy16_lane(const void* src, uint32_t lds) {
 }
 
 // Weight fragment bytes per (32-row block, chunk): q6_K hi and lo planes of
-// 1 KiB each; q4_K packed codes (8 bytes per lane).
+// 1 KiB each; q4_K codes (16 bytes per lane).
 template <int TYPE>
 constexpr int kFragA = TYPE == QMM_Q6_K ? 2048 : kQ4CodeFrag;
 
@@ -127,12 +126,7 @@ struct WeightOps<QMM_Q4_K> {
   struct A { v4i c; };
   struct D { v16i c; };
   static constexpr int kMfma = 1;
-  __device__ static A load(const int8_t* frag, int lane) {
-    // 8 bytes per lane: byte b holds code k0+b (low nibble) and k0+8+b (high)
-    const v2i p = *(const v2i*)(frag + lane * 8);
-    const int m = 0x0F0F0F0F;
-    return {{p[0] & m, p[1] & m, (p[0] >> 4) & m, (p[1] >> 4) & m}};
-  }
+  __device__ static A load(const int8_t* frag, int lane) { return {*(const v4i*)(frag + lane * 16)}; }
   __device__ static D mma(const A& a, v4i bq) {
     const v16i zero = {};
     return {__builtin_amdgcn_mfma_i32_32x32x32_i8(a.c, bq, zero, 0, 0, 0)};

@@ -7,8 +7,8 @@
 // two int8 planes (hi = w >> 6, lo = w & 63), so one K=32 int8 MFMA per plane
 // yields the block dot J = 64*J_hi + J_lo; q4_K's 6-bit scale of every 32 weights
 // goes to an f16 plane (integers 0..63, exact) from which the GEMM forms the
-// scale product with the activation scale, and its codes stay 4-bit, two per
-// byte.  Only the f16 d of the super-block stays a float.
+// scale product with the activation scale, and its 4-bit codes become int8
+// bytes in MFMA fragment order.  Only the f16 d of the super-block stays a float.
 #include "qmm_internal.h"
 #include "qmm_common.h"
 
@@ -23,10 +23,9 @@ namespace qmm {
 //             ((j/32*nchunk + k/32)*2 + p)*1024 + ((k%32)/16)*512 + (j%32)*16 + k%16
 //             where the folded weight w = sc[k/16] * (code - 32) = hi*64 + lo,
 //             w in [-4064, 4096], lo in [0, 63]
-//       q4_K: uint8 [R][nchunk][2 k-halves][32 rows][8 bytes]: lane (k-half h,
-//             row) gets 8 bytes, byte b holding code k = 16h + b in its low and
-//             k = 16h + 8 + b in its high nibble (so masking and shifting the
-//             two words gives the 16 codes in MFMA order)
+//       q4_K: int8 [R][nchunk][2 k-halves][32 rows][16 bytes]: the code of
+//             (row j, k) in [0, 15] at byte
+//             (j/32*nchunk + k/32)*1024 + ((k%32)/16)*512 + (j%32)*16 + k%16
 //   wd  f32   [R][nsb][32 rows]      d of (row, super-block)
 //   wmn f16   [R][nsb][32 rows][8]   the 6-bit min of (row, chunk) as an f16
 //             integer, at ((j/32*nsb + c/8)*32 + j%32)*8 + c%8; q4_K only
@@ -37,7 +36,7 @@ namespace qmm {
 // Rows od..od_pad-1 are zero in every plane.
 // ---------------------------------------------------------------------------
 size_t wq_bytes(int type, int64_t od_pad, int64_t id) {
-  return type == QMM_Q6_K ? (size_t)od_pad * (size_t)id * 2 : (size_t)od_pad * (size_t)id / 2;
+  return type == QMM_Q6_K ? (size_t)od_pad * (size_t)id * 2 : (size_t)od_pad * (size_t)id;
 }
 size_t wd_bytes(int64_t od_pad, int64_t id) { return (size_t)od_pad * (size_t)(id / 256) * 4; }
 size_t wmn_bytes(int type, int64_t od_pad, int64_t id) {
@@ -64,7 +63,7 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
   const int rb = j >> 5, jr = j & 31;
   const int b = c >> 3, cl = c & 7;
 
-  uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};  // q6_K planes; q4_K codes in lo[0..1]
+  uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};  // q6_K planes; q4_K codes in lo
   if (j < od) {
     if (type == QMM_Q6_K) {
       // 210-byte block: ql[128] | qh[64] | int8 scales[16] | f16 d (r56 section 1)
@@ -104,10 +103,7 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
       const uint8_t* qs = B + 16 + 32 * (cl >> 1) + 16 * h;
       const int shift = (cl & 1) * 4;
 #pragma unroll
-      for (int b8 = 0; b8 < 8; ++b8) {
-        const uint32_t packed = ((qs[b8] >> shift) & 15) | (((qs[b8 + 8] >> shift) & 15) << 4);
-        lo[b8 >> 2] |= packed << (8 * (b8 & 3));
-      }
+      for (int i = 0; i < 16; ++i) lo[i >> 2] |= (uint32_t)((qs[i] >> shift) & 15) << (8 * (i & 3));
       if (h == 0) {
         wmn[(((int64_t)rb * nsb + b) * 32 + jr) * 8 + cl] =
             __builtin_bit_cast(uint16_t, (_Float16)(float)mn);  // 0..63: exact
@@ -131,8 +127,8 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
     *(uint4*)dst = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     *(uint4*)(dst + 1024) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   } else {
-    int8_t* dst = wq + ((int64_t)rb * nchunk + c) * kQ4CodeFrag + h * 256 + jr * 8;
-    *(uint2*)dst = make_uint2(lo[0], lo[1]);
+    int8_t* dst = wq + ((int64_t)rb * nchunk + c) * kQ4CodeFrag + h * 512 + jr * 16;
+    *(uint4*)dst = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
 }
 

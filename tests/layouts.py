@@ -38,10 +38,10 @@ def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: i
         assert lo.min() >= 0 and lo.max() <= 63
         w = hi * 64 + lo
     else:
-        # [R][nchunk][k-half h][row][byte b]: code k = 16h + b (low nibble), 16h + 8 + b (high)
-        pk = buf[: od_pad * id_ // 2].reshape(R, nchunk, 2, 32, 8)
-        codes = np.concatenate([pk & 15, pk >> 4], axis=-1)          # [R][nchunk][h][row][16]
-        codes = codes.transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
+        # [R][nchunk][k-half h][row][16]: code k = 16h + byte
+        pk = buf[: od_pad * id_].view(np.int8).reshape(R, nchunk, 2, 32, 16)
+        codes = pk.transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
+        assert codes.min() >= 0 and codes.max() <= 15
         # scales: binary16 [R][nsb][row][chunk of the super-block], like the mins
         s16 = buf[sc_offset: sc_offset + od_pad * nchunk * 2].view("<f2").reshape(R, nsb, 32, 8)
         sf = s16.astype(np.float64).transpose(0, 2, 1, 3).reshape(od_pad, nchunk)
