@@ -283,6 +283,35 @@ def test_small_all_elements(case):
     check_close(got, ref, A, name)
 
 
+@pytest.mark.parametrize("geometry", ["few", "many"])
+@pytest.mark.parametrize("type_", [synth.Q4_K, synth.Q6_K], ids=["q4_K", "q6_K"])
+def test_subnormal_activation_scales(type_, geometry):
+    """Activation scales that are f16 subnormals (amax below 127 * 2^-14) reach
+    the matrix core (q4_K's scale outer product and min term take dh and s as
+    f16 operands) and the vector ALU (q6_K converts dh): every token's first
+    chunks are tiny, some chunks are zero and the rest normal, and the first
+    tokens are tiny throughout, so a flushed subnormal anywhere fails the
+    relative tolerance.  Both tile geometries."""
+    od, id_ = 200, 512
+    T = 40 if geometry == "few" else 4100
+    say(f"subnormal scales {synth.TYPE_NAMES[type_]} T={T}")
+    raw, x = synth.case(type_, od, id_, T, seed=5)
+    x = x.copy()
+    x[:, :96] *= 1e-5                    # amax ~ 3e-5: dh ~ 2e-7, deep in the subnormals
+    x[:, 96:128] *= 3e-3                 # dh near the smallest normal
+    x[:, 128:160] = 0.0                  # zero blocks
+    x[:8] *= 1e-4                        # tokens that are tiny everywhere
+    qact = gpu_quantize(x)
+    q, dh, s = check_prepass(x, qact)
+    d16 = dh.view(np.float16).astype(np.float64)
+    assert np.any((d16 > 0) & (d16 < 2.0 ** -14)), "no subnormal scale in the input"
+    w = qmm.register_weights(type_, od, id_, raw)
+    got = run_mmq(w, qact, T)
+    ref, A = oracle.mmq(type_, raw, od, id_, q, dh, s)
+    check_close(got, ref, A, f"subnormal scales {geometry}")
+    w.release()
+
+
 def _random_shapes(n, seed=11):
     """Seeded random shapes: both types, odd row counts, 1..8 super-blocks; every
     other case with 2000..4200 tokens so that it takes the many-tile geometry.
