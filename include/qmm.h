@@ -121,13 +121,14 @@ int qmm_weights_info(const qmm_weights *w, qmm_info *out);
  *                 of (row j, k) at byte (j/32*nchunk + k/32)*1024
  *                 + ((k%32)/16)*512 + (j%32)*16 + k%16
  *   at wd_offset  f32 [R][nsb][32]: d of (row, super-block)
- *   at mn_offset  binary16 [R][nsb][32][8]: the 6-bit min of (row j, chunk c)
+ *   at mn_offset  binary16 [R][nsb][2][32][4]: the 6-bit min of (row j, chunk c)
  *                 as an f16 integer, q4_K only, at element
- *                 ((j/32*nsb + c/8)*32 + j%32)*8 + c%8
+ *                 ((j/32*nsb + c/8)*2 + (c%8)/4)*128 + (j%32)*4 + c%4
  *   at dm_offset  f32 [R][nsb][32]: dmin of (row, super-block), q4_K only
- *   at sc_offset  binary16 [R][nsb][32][8]: the 6-bit scale of (row j, chunk
+ *   at sc_offset  binary16 [R][nsb][2][32][4]: the 6-bit scale of (row j, chunk
  *                 c) as an f16 integer, q4_K only, at element
- *                 ((j/32*nsb + c/8)*32 + j%32)*8 + c%8 (the layout of the mins)
+ *                 ((j/32*nsb + c/8)*2 + (c%8)/4)*128 + (j%32)*4 + c%4 (the
+ *                 layout of the mins)
  * Errors: QMM_EINVAL (null pointers, bytes mismatch), QMM_EHIP.
  */
 int qmm_weights_export(const qmm_weights *w, void *host, size_t bytes);

@@ -85,9 +85,9 @@ struct alignas(16) Stage {
   int8_t a[WR][KC][kFragA<TYPE>];    // weight fragments: [row block][chunk]
   int8_t b[WT][KC][1024];            // q8 codes: [token block][chunk][fragment]
   uint32_t s[WT][KC][32];            // (dh, s) pairs: [token block][chunk][token]
-  uint16_t sc[kQ4 ? WR : 0][32][8];  // super-block scales as f16: [row block][row][chunk]; q4_K only
+  uint16_t sc[kQ4 ? WR : 0][2][32][4];  // super-block scales as f16: [row block][chunk/4][row][chunk%4]; q4_K only
   float d[WR][32];                   // super-block d: [row block][row]
-  uint16_t mn[kQ4 ? WR : 0][32][8];  // super-block mins as f16: [row block][row][chunk]; q4_K only
+  uint16_t mn[kQ4 ? WR : 0][2][32][4];  // super-block mins as f16, as sc; q4_K only
   float dm[kQ4 ? WR : 0][32];        // super-block dmin: [row block][row]; q4_K only
   // s, sc, d, mn and dm are contiguous: the "small" region, copied in 16-byte
   // units (s with every stage, sc with a super-block's first, d, mn and dm with
@@ -406,9 +406,9 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         uint32_t dhr = st.s[wt][0][lane & 31], dhr_even = 0;
         v2i amin = {};
         if constexpr (TYPE == QMM_Q4_K)
-          if (h == kStagesPerSb - 1) amin = *(const v2i*)(&st.mn[wr][lane & 31][4 * (lane >> 5)]);
+          if (h == kStagesPerSb - 1) amin = *(const v2i*)(&st.mn[wr][lane >> 5][lane & 31][0]);
         if constexpr (TYPE == QMM_Q4_K)
-          if (h == 0) a_sc = *(const v2i*)(&st.sc[wr][lane & 31][4 * (lane >> 5)]);
+          if (h == 0) a_sc = *(const v2i*)(&st.sc[wr][lane >> 5][lane & 31][0]);
         typename W::A a0 = W::load(st.a[wr][0], lane);
         v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
         typename W::A a1 = W::load(st.a[wr][1], lane);

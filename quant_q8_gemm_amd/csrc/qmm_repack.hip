@@ -27,12 +27,14 @@ namespace qmm {
 //             (row j, k) in [0, 15] at byte
 //             (j/32*nchunk + k/32)*1024 + ((k%32)/16)*512 + (j%32)*16 + k%16
 //   wd  f32   [R][nsb][32 rows]      d of (row, super-block)
-//   wmn f16   [R][nsb][32 rows][8]   the 6-bit min of (row, chunk) as an f16
-//             integer, at ((j/32*nsb + c/8)*32 + j%32)*8 + c%8; q4_K only
+//   wmn f16   [R][nsb][2][32 rows][4]  the 6-bit min of (row, chunk) as an f16
+//             integer, at ((j/32*nsb + c/8)*2 + (c%8)/4)*128 + (j%32)*4 + c%4:
+//             per (row block, super-block) two halves of [32 rows][4 chunks],
+//             so a lane half's 8-byte reads are consecutive; q4_K only
 //   wdm f32   [R][nsb][32 rows]      dmin of (row, super-block); q4_K only
-//   wsc f16   [R][nsb][32 rows][8]   the 6-bit scale of (row, chunk) as an f16
-//             integer, at ((j/32*nsb + c/8)*32 + j%32)*8 + c%8 (the layout of
-//             wmn); q4_K only
+//   wsc f16   [R][nsb][2][32 rows][4]  the 6-bit scale of (row, chunk) as an f16
+//             integer, at ((j/32*nsb + c/8)*2 + (c%8)/4)*128 + (j%32)*4 + c%4
+//             (the layout of wmn); q4_K only
 // Rows od..od_pad-1 are zero in every plane.
 // ---------------------------------------------------------------------------
 size_t wq_bytes(int type, int64_t od_pad, int64_t id) {
@@ -105,9 +107,9 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
 #pragma unroll
       for (int i = 0; i < 16; ++i) lo[i >> 2] |= (uint32_t)((qs[i] >> shift) & 15) << (8 * (i & 3));
       if (h == 0) {
-        wmn[(((int64_t)rb * nsb + b) * 32 + jr) * 8 + cl] =
+        wmn[(((int64_t)rb * nsb + b) * 2 + (cl >> 2)) * 128 + jr * 4 + (cl & 3)] =
             __builtin_bit_cast(uint16_t, (_Float16)(float)mn);  // 0..63: exact
-        wsc[(((int64_t)rb * nsb + b) * 32 + jr) * 8 + cl] = __builtin_bit_cast(uint16_t, (_Float16)(float)sc);
+        wsc[(((int64_t)rb * nsb + b) * 2 + (cl >> 2)) * 128 + jr * 4 + (cl & 3)] = __builtin_bit_cast(uint16_t, (_Float16)(float)sc);
         if (cl == 0) {
           wd[((int64_t)rb * nsb + b) * 32 + jr] = f16_bits_to_float(B[0] | (B[1] << 8));
           wdm[((int64_t)rb * nsb + b) * 32 + jr] = f16_bits_to_float(B[2] | (B[3] << 8));
@@ -116,8 +118,8 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
     }
   } else if (h == 0) {
     if (type == QMM_Q4_K) {
-      wmn[(((int64_t)rb * nsb + b) * 32 + jr) * 8 + cl] = 0;
-      wsc[(((int64_t)rb * nsb + b) * 32 + jr) * 8 + cl] = 0;
+      wmn[(((int64_t)rb * nsb + b) * 2 + (cl >> 2)) * 128 + jr * 4 + (cl & 3)] = 0;
+      wsc[(((int64_t)rb * nsb + b) * 2 + (cl >> 2)) * 128 + jr * 4 + (cl & 3)] = 0;
       if (cl == 0) wdm[((int64_t)rb * nsb + b) * 32 + jr] = 0.0f;
     }
     if (cl == 0) wd[((int64_t)rb * nsb + b) * 32 + jr] = 0.0f;

@@ -42,9 +42,9 @@ def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: i
         pk = buf[: od_pad * id_].view(np.int8).reshape(R, nchunk, 2, 32, 16)
         codes = pk.transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
         assert codes.min() >= 0 and codes.max() <= 15
-        # scales: binary16 [R][nsb][row][chunk of the super-block], like the mins
-        s16 = buf[sc_offset: sc_offset + od_pad * nchunk * 2].view("<f2").reshape(R, nsb, 32, 8)
-        sf = s16.astype(np.float64).transpose(0, 2, 1, 3).reshape(od_pad, nchunk)
+        # scales: binary16 [R][nsb][chunk/4][row][chunk%4], like the mins
+        s16 = buf[sc_offset: sc_offset + od_pad * nchunk * 2].view("<f2").reshape(R, nsb, 2, 32, 4)
+        sf = s16.astype(np.float64).transpose(0, 3, 1, 2, 4).reshape(od_pad, nchunk)
         assert np.all(sf == np.round(sf)) and sf.min() >= 0 and sf.max() <= 63
         sc = sf.astype(np.int32)
         w = codes * np.repeat(sc, 32, axis=1)
@@ -52,9 +52,9 @@ def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: i
     d = d.transpose(0, 2, 1).reshape(od_pad, nsb)
     mn = dm = None
     if type_ == 4:
-        # mins: binary16 [R][nsb][row][chunk of the super-block]
-        m16 = buf[mn_offset: mn_offset + od_pad * nchunk * 2].view("<f2").reshape(R, nsb, 32, 8)
-        mf = m16.astype(np.float64).transpose(0, 2, 1, 3).reshape(od_pad, nchunk)
+        # mins: binary16 [R][nsb][chunk/4][row][chunk%4] (chunk within the super-block)
+        m16 = buf[mn_offset: mn_offset + od_pad * nchunk * 2].view("<f2").reshape(R, nsb, 2, 32, 4)
+        mf = m16.astype(np.float64).transpose(0, 3, 1, 2, 4).reshape(od_pad, nchunk)
         assert np.all(mf == np.round(mf)) and mf.min() >= 0 and mf.max() <= 63
         mn = mf.astype(np.int32)
         dm = buf[dm_offset: dm_offset + od_pad * nsb * 4].view("<f4").reshape(R, nsb, 32)
