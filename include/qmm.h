@@ -77,9 +77,9 @@ typedef struct {
     int64_t od_pad;      /* rows padded with zeros to the row tile */
     size_t raw_bytes;    /* od * (id/256) * (144 or 210): the k-quant bytes */
     size_t plane_bytes;  /* device memory the handle holds */
-    size_t wd_offset;    /* byte offset of the d plane inside the planes */
+    size_t wd_offset;    /* byte offset of the d (q6_K) or row-scale (q4_K) plane */
     size_t mn_offset;    /* byte offset of the min plane (q4_K; else == plane_bytes) */
-    size_t dm_offset;    /* byte offset of the dmin plane (q4_K; else == plane_bytes) */
+    size_t dm_offset;    /* no plane: always == plane_bytes (dmin is folded into the min plane) */
     size_t sc_offset;    /* byte offset of the f16 scale plane (q4_K; else == plane_bytes) */
 } qmm_info;
 
@@ -120,15 +120,19 @@ int qmm_weights_info(const qmm_weights *w, qmm_info *out);
  *                 q4_K: int8 [R][nchunk][2][32][16]: the 4-bit code (0..15)
  *                 of (row j, k) at byte (j/32*nchunk + k/32)*1024
  *                 + ((k%32)/16)*512 + (j%32)*16 + k%16
- *   at wd_offset  f32 [R][nsb][32]: d of (row, super-block)
- *   at mn_offset  binary16 [R][nsb][2][32][4]: the 6-bit min of (row j, chunk c)
- *                 as an f16 integer, q4_K only, at element
- *                 ((j/32*nsb + c/8)*2 + (c%8)/4)*128 + (j%32)*4 + c%4
- *   at dm_offset  f32 [R][nsb][32]: dmin of (row, super-block), q4_K only
- *   at sc_offset  binary16 [R][nsb][2][32][4]: the 6-bit scale of (row j, chunk
- *                 c) as an f16 integer, q4_K only, at element
- *                 ((j/32*nsb + c/8)*2 + (c%8)/4)*128 + (j%32)*4 + c%4 (the
- *                 layout of the mins)
+ *   at wd_offset  q6_K: f32 [R][nsb][32]: d of (row, super-block)
+ *                 q4_K: f32 [R][32]: 2^-e of row j, where e = 13 - floor(log2 M)
+ *                 for M the largest d*scale and dmin*min over the row's blocks
+ *                 (e = 0 if M = 0); the q4_K planes below hold values times 2^e
+ *   q4_K only, each value v (exact in binary32) as two binary16 values
+ *   hi = f16(v), lo = f16(v - hi) (round to nearest even; hi + lo == v):
+ *   at mn_offset  binary16 [R][nsb][2][2][32][4]: v = -dmin*min(j, c)*2^e of
+ *                 (row j, chunk c), part p (0: hi, 1: lo) at element
+ *                 (((j/32*nsb + c/8)*2 + p)*2 + (c%8)/4)*128 + (j%32)*4 + c%4
+ *   at sc_offset  binary16 [R][nsb][2][2][32][2][2]: v = d*scale(j, c)*2^e of
+ *                 (row j, chunk c), part p at element
+ *                 ((((j/32*nsb + c/8)*2 + (c%8)/4)*2 + (c%4)/2)*32 + j%32)*4
+ *                 + (c%2)*2 + p
  * Errors: QMM_EINVAL (null pointers, bytes mismatch), QMM_EHIP.
  */
 int qmm_weights_export(const qmm_weights *w, void *host, size_t bytes);

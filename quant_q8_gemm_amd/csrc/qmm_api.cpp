@@ -118,7 +118,7 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   p.nsb = id / 256;
   p.nchunk = id / 32;
   const size_t off_wd = round_up(qmm::wq_bytes(type, p.od_pad, id), 256);
-  const size_t off_mn = off_wd + round_up(qmm::wd_bytes(p.od_pad, id), 256);
+  const size_t off_mn = off_wd + round_up(qmm::wd_bytes(type, p.od_pad, id), 256);
   const size_t off_dm = off_mn + round_up(qmm::wmn_bytes(type, p.od_pad, id), 256);
   const size_t off_sc = off_dm + round_up(qmm::wdm_bytes(type, p.od_pad, id), 256);
   const size_t plane_bytes = off_sc + round_up(qmm::wsc_bytes(type, p.od_pad, id), 256);
@@ -161,7 +161,6 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   p.wq = (int8_t*)alloc;
   p.wd = (float*)((char*)alloc + off_wd);
   p.wmn = type == QMM_Q4_K ? (uint16_t*)((char*)alloc + off_mn) : nullptr;
-  p.wdm = type == QMM_Q4_K ? (float*)((char*)alloc + off_dm) : nullptr;
   p.wsc = type == QMM_Q4_K ? (uint16_t*)((uint8_t*)alloc + off_sc) : nullptr;
   int rc = QMM_OK;
   if ((e = hipMemcpyAsync(raw, host_bytes, nbytes, hipMemcpyHostToDevice, s)) != hipSuccess)
@@ -183,7 +182,7 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   w->plane_bytes = plane_bytes;
   w->wd_offset = off_wd;
   w->mn_offset = type == QMM_Q4_K ? off_mn : plane_bytes;
-  w->dm_offset = type == QMM_Q4_K ? off_dm : plane_bytes;
+  w->dm_offset = plane_bytes;  // no dmin plane: q4_K's dmin is folded into its min plane
   w->sc_offset = type == QMM_Q4_K ? off_sc : plane_bytes;
   w->alloc = alloc;
   if (getenv("QMM_LOG") != nullptr)

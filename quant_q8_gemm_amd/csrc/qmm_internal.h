@@ -17,10 +17,9 @@ struct Planes {
   int64_t nsb;       // id / 256
   int64_t nchunk;    // id / 32
   int8_t* wq;        // weight fragments in MFMA order: q6_K folded hi/lo, q4_K codes
-  float* wd;         // d per (row, super-block)
-  uint16_t* wmn;     // min per (row, chunk) as f16, super-block-major; q4_K only, else nullptr
-  float* wdm;        // dmin per (row, super-block); q4_K only, else nullptr
-  uint16_t* wsc;     // 6-bit scale per (row, chunk) as f16, super-block-major; q4_K only, else nullptr
+  float* wd;         // q6_K: d per (row, super-block); q4_K: the row's 2^-e
+  uint16_t* wmn;     // q4_K: -dmin*min*2^e per (row, chunk) as f16 hi + lo; else nullptr
+  uint16_t* wsc;     // q4_K: d*sc*2^e per (row, chunk) as f16 hi + lo; else nullptr
 };
 
 constexpr int kRowPad = 128;     // weight rows are padded to a multiple of this
@@ -29,7 +28,7 @@ constexpr int kQ4CodeFrag = 1024; // q4_K code bytes per (32-row block, chunk): 
 
 // Byte sizes of the planes for a shape (all offsets 256-byte aligned).
 size_t wq_bytes(int type, int64_t od_pad, int64_t id);
-size_t wd_bytes(int64_t od_pad, int64_t id);
+size_t wd_bytes(int type, int64_t od_pad, int64_t id);
 size_t wmn_bytes(int type, int64_t od_pad, int64_t id);
 size_t wdm_bytes(int type, int64_t od_pad, int64_t id);
 size_t wsc_bytes(int type, int64_t od_pad, int64_t id);

@@ -15,15 +15,16 @@
 //    folded weight split into two int8 planes (hi = w >> 6, lo = w & 63), so one
 //    K=32 int8 MFMA per plane gives J = 64*J_hi + J_lo.  q4_K (one 6-bit scale
 //    per 32-block): the 4-bit codes are int8 bytes, one K=32 MFMA gives the
-//    code dot D, and the products sc(row)*dh(token) of the
-//    block's scale and the activation scale come from one small f16 MFMA (an
-//    outer product), so each element costs a conversion and an FMA;
+//    code dot D, and the products d*sc(row)*dh(token) of the block's scale
+//    and the activation scale come from one small f16 MFMA (an outer product),
+//    so each element costs a conversion and an FMA, and no super-block d is
+//    left to apply;
 //  * planes are stored in MFMA fragment order, so every lane's operand is one
 //    contiguous 16-byte load and a wave's load is one contiguous 1 KiB;
 //  * the q4_K min term sum_c dmin*min_c*s_c is a small matrix product over
-//    chunks: per super-block, sum_c min_c*s_c on one f16 MFMA (32x32x8; the
-//    6-bit mins and the f16 scaled sums are exact f16 operands), times dmin
-//    once per super-block, like d.
+//    chunks: per super-block, two f16 MFMAs (32x32x8) of the f16 scaled sums
+//    with dmin*min as an exact pair of f16 values, accumulating straight into
+//    the f32 output accumulators.
 #include "qmm_internal.h"
 #include "qmm_common.h"
 
@@ -85,16 +86,16 @@ struct alignas(16) Stage {
   int8_t a[WR][KC][kFragA<TYPE>];    // weight fragments: [row block][chunk]
   int8_t b[WT][KC][1024];            // q8 codes: [token block][chunk][fragment]
   uint32_t s[WT][KC][32];            // (dh, s) pairs: [token block][chunk][token]
-  uint16_t sc[kQ4 ? WR : 0][2][32][4];  // super-block scales as f16: [row block][chunk/4][row][chunk%4]; q4_K only
-  float d[WR][32];                   // super-block d: [row block][row]
-  uint16_t mn[kQ4 ? WR : 0][2][32][4];  // super-block mins as f16, as sc; q4_K only
-  float dm[kQ4 ? WR : 0][32];        // super-block dmin: [row block][row]; q4_K only
-  // s, sc, d, mn and dm are contiguous: the "small" region, copied in 16-byte
-  // units (s with every stage, sc with a super-block's first, d, mn and dm with
-  // its last).
-  static constexpr int kUnitsS = WT * KC * 8, kUnitsSc = kQ4 ? WR * 32 : 0, kUnitsD = WR * 8,
-                       kUnitsMn = kQ4 ? WR * 32 : 0, kUnitsDm = kQ4 ? WR * 8 : 0;
-  static constexpr int kUnits = kUnitsS + kUnitsSc + kUnitsD + kUnitsMn + kUnitsDm;
+  // q4_K: the stage's d*sc*2^e as f16 pairs (hi, lo): [row block][chunk/2][row][chunk%2]
+  uint32_t sc[kQ4 ? WR : 0][2][32][2];
+  float d[kQ4 ? 0 : WR][32];         // q6_K: super-block d: [row block][row]
+  // q4_K: -dmin*min*2^e of the super-block as f16: [row block][hi, lo][chunk/4][row][chunk%4]
+  uint16_t mn[kQ4 ? WR : 0][2][2][32][4];
+  // s, sc, d and mn are contiguous: the "small" region, copied in 16-byte units
+  // (s and sc with every stage, d and mn with a super-block's last).
+  static constexpr int kUnitsS = WT * KC * 8, kUnitsSc = kQ4 ? WR * 32 : 0, kUnitsD = kQ4 ? 0 : WR * 8,
+                       kUnitsMn = kQ4 ? WR * 64 : 0;
+  static constexpr int kUnits = kUnitsS + kUnitsSc + kUnitsD + kUnitsMn;
   static constexpr int kSmallJobs = (kUnits + 63) / 64;
 };
 
@@ -137,26 +138,24 @@ struct WeightOps<QMM_Q4_K> {
   __device__ static int dot(const D& d, v4i, int i) { return d.c[i]; }
 };
 
-// q4_K: the scale of output element (row j, token t) of chunk c is sc(j, c) * dh(t, c),
-// an outer product of a row vector and a token vector, each an exact f16 value (a
-// 6-bit integer, the f16 activation scale).  One f16 MFMA (32x32x8) forms all
-// 32 x 32 products at once, exactly in f32 (11 x 6 significant bits), in the same
-// output layout as the int8 MFMA's block dots, so the epilogue is one conversion
-// and one FMA per element instead of an integer multiply, a conversion and an
-// FMA.  The FMA still sees the exact product sc * D * dh.
-// A holds the scales of all 8 chunks of the super-block (k = chunk: the row's
-// 8 f16 scales, lane half h giving chunks 4h..4h+3); B holds the chunk's dh at
-// k = chunk and zeros elsewhere, so the sum over k keeps just that chunk's
-// product.  ci is the chunk's index in the super-block (a constant once the
-// chunk loops are unrolled).
-//   a_sc      the lane's 4 f16 scales (row lane & 31, chunks 4*(lane/32)..+3)
+// q4_K: the scale of output element (row j, token t) of chunk c is
+// d(j)*sc(j, c) * dh(t, c), an outer product of a row vector and a token vector.
+// d*sc (an f16 times a 6-bit integer) is held, times the row's power of two 2^e,
+// as an exact pair of f16 values hi + lo, and dh is an f16 value, so one f16 MFMA
+// (32x32x8) forms all 32 x 32 products (hi + lo)*dh, each exact before one f32
+// rounding, in the same output layout as the int8 MFMA's block dots: the epilogue
+// is one conversion and one FMA per element, and no super-block d is left to
+// apply.  A holds the pairs of the stage's 4 chunks (lane half h: chunks 2h and
+// 2h+1, k = 4h + 2*(chunk%2) + {hi, lo}); B holds the chunk's dh in both of its
+// slots and zeros elsewhere, so the sum over k keeps just that chunk's product.
+// cc is the chunk's index in the stage (a constant once the loops are unrolled).
+//   a_sc      the lane's 4 f16 values (row lane & 31, chunks 2*(lane/32)..+1)
 //   dh_bits   the chunk's (dh, s) pair of the lane's token (lane & 31)
-//   b_mask    0xFFFF on the lanes of half ci/4, else 0
-__device__ __forceinline__ v16f scale_outer(v2i a_sc, uint32_t dh_bits, uint32_t b_mask, int ci) {
+//   sel       byte selector: dh twice on the lanes of half cc/2, else zero
+__device__ __forceinline__ v16f scale_outer(v2i a_sc, uint32_t dh_bits, uint32_t sel, int cc) {
   typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-  const uint32_t x = dh_bits & b_mask;
-  const uint32_t w = ci % 2 == 0 ? x : x << 16;
-  const v2i b = {ci % 4 < 2 ? (int)w : 0, ci % 4 < 2 ? 0 : (int)w};
+  const uint32_t y = __builtin_amdgcn_perm(0u, dh_bits, sel);
+  const v2i b = {cc % 2 == 0 ? (int)y : 0, cc % 2 == 0 ? 0 : (int)y};
   const v16f zero = {};
   return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, a_sc), __builtin_bit_cast(v4h, b), zero,
                                               0, 0, 0);
@@ -222,7 +221,7 @@ __device__ __forceinline__ void store_block(float* __restrict__ out, const v16f&
 template <int TYPE, int WR, int WT, int KC, int KS>
 __global__ void __launch_bounds__(64 * WR * WT * KS, 16 / (WR * WT * KS))
 mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
-           const uint8_t* __restrict__ wmn, const float* __restrict__ wdm, const uint8_t* __restrict__ wsc,
+           const uint8_t* __restrict__ wmn, const uint8_t* __restrict__ wsc,
            const uint8_t* __restrict__ qq,
            const uint8_t* __restrict__ qs, int nchunk, int nsb, int od, int n_tok,
            int tok_tiles, int dp_row_tiles, int split, int vec_store, float* __restrict__ out,
@@ -296,33 +295,29 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
                         (size_t)gbeg * KC * 1024;
   const uint32_t lane_off = (uint32_t)lane * 16;
   const uint8_t* small_src = nullptr;
-  // 0 none; per stage: 1 pairs (128 bytes per chunk); per super-block: 3 scales
-  // (512 bytes, at its first stage), 2 d or dmin (128 bytes), 4 mins (512 bytes)
-  // (at its last)
+  // 0 none; per stage: 1 pairs (128 bytes per chunk), 3 q4_K scale pairs (512
+  // bytes); per super-block, at its last stage: 2 q6_K d (128 bytes), 4 q4_K
+  // mins (1 KiB)
   int small_kind = 0;
   if (wave < St::kSmallJobs) {
     const int u = wave * 64 + lane;
     const int sb0g = gbeg / kStagesPerSb;
-    constexpr int eSc = St::kUnitsS + St::kUnitsSc, eD = eSc + St::kUnitsD, eMn = eD + St::kUnitsMn;
+    constexpr int eSc = St::kUnitsS + St::kUnitsSc, eD = eSc + St::kUnitsD;
     if (u < St::kUnitsS) {
       small_src = qs + ((size_t)(tb0 + u / (KC * 8)) * nchunk + gbeg * KC) * 128 + (u % (KC * 8)) * 16;
       small_kind = 1;
     } else if (u < eSc) {
       const int v = u - St::kUnitsS;
-      small_src = wsc + ((size_t)(rb0 + v / 32) * nsb + sb0g) * 512 + (v % 32) * 16;
+      small_src = wsc + ((size_t)(rb0 + v / 32) * nsb * 2 + gbeg) * 512 + (v % 32) * 16;
       small_kind = 3;
     } else if (u < eD) {
       const int v = u - eSc;
       small_src = (const uint8_t*)wd + ((size_t)(rb0 + v / 8) * nsb + sb0g) * 128 + (v % 8) * 16;
       small_kind = 2;
-    } else if (u < eMn) {
-      const int v = u - eD;
-      small_src = wmn + ((size_t)(rb0 + v / 32) * nsb + sb0g) * 512 + (v % 32) * 16;
-      small_kind = 4;
     } else if (u < St::kUnits) {
-      const int v = u - eMn;
-      small_src = (const uint8_t*)wdm + ((size_t)(rb0 + v / 8) * nsb + sb0g) * 128 + (v % 8) * 16;
-      small_kind = 2;
+      const int v = u - eD;
+      small_src = wmn + ((size_t)(rb0 + v / 64) * nsb + sb0g) * 1024 + (v % 64) * 16;
+      small_kind = 4;
     }
   }
 
@@ -351,15 +346,15 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
                        lds_buf + (uint32_t)__builtin_offsetof(St, b) + (kb0 + u) * 1024);
     } else if (wave < St::kSmallJobs) {
       const uint32_t ls = lds_buf + (uint32_t)__builtin_offsetof(St, s) + wave * 1024;
-      const bool ends_sb = ((g + 1) * KC) % 8 == 0, starts_sb = (g * KC) % 8 == 0;
+      const bool ends_sb = ((g + 1) * KC) % 8 == 0;
       if (small_kind == 1)
         copy16_lane(small_src + (size_t)g * KC * 128, ls);
-      else if (small_kind == 3 && starts_sb)
-        copy16_lane(small_src + (size_t)((g * KC) / 8) * 512, ls);
+      else if (small_kind == 3)
+        copy16_lane(small_src + (size_t)g * 512, ls);
       else if (small_kind == 2 && ends_sb)
         copy16_lane(small_src + (size_t)((g * KC) / 8) * 128, ls);
       else if (small_kind == 4 && ends_sb)
-        copy16_lane(small_src + (size_t)((g * KC) / 8) * 512, ls);
+        copy16_lane(small_src + (size_t)((g * KC) / 8) * 1024, ls);
     }
   };
   auto issue_stage = [&](int g, int buf) __attribute__((always_inline)) {  // all at once (prologue)
@@ -367,29 +362,31 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
     for (int j = 0; j < kWaveJobs; ++j) issue_job(g, buf, j);
   };
 
-  v16f acc, inner, cm;
+  v16f acc, inner;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-  // q4_K min term of a super-block, sum over its chunks c of min(row, c) * s(token, c),
-  // on one f16 MFMA (32x32x8) at its end: both operands are exact in f16 (6-bit
-  // integer mins, the f16 scaled sums) and so are their products in f32.  Lane
-  // half hh supplies chunks 4*hh..4*hh+3: the mins from the super-block's mins
-  // region, the scaled sums (bs) collected from the chunks' scale pairs as
-  // they pass, half hh of the lanes during the super-block's stage hh.
+  // q4_K min term of a super-block, sum over its chunks c of
+  // -dmin*min(row, c)*2^e * s(token, c), on two f16 MFMAs (32x32x8) at its end that
+  // add into acc: the hi and the lo part of the exact pair, each times the f16
+  // scaled sums, products exact in f32.  Lane half hh supplies chunks
+  // 4*hh..4*hh+3: the pairs from the super-block's mins region, the scaled sums
+  // (bs) collected from the chunks' scale pairs as they pass, half hh of the
+  // lanes during the super-block's stage hh.
   v2i bs = {};
   const bool lane_hi = lane >= 32;
-  // q4_K scale products: the super-block's scales (A operand) and the dh masks
-  // of the two lane halves
+  // q4_K scale products: the stage's scale pairs (A operand), and the byte
+  // selectors that put dh twice into B on the lanes of one half and zeros on the
+  // other's
   v2i a_sc = {};
-  const uint32_t b_mask0 = lane_hi ? 0u : 0xFFFFu, b_mask1 = lane_hi ? 0xFFFFu : 0u;
+  const uint32_t sel0 = lane_hi ? 0x0C0C0C0Cu : 0x01000100u, sel1 = lane_hi ? 0x01000100u : 0x0C0C0C0Cu;
 
   if (nstages > 0) issue_stage(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   // Super-blocks in turn, the stages of one unrolled, so where a super-block
-  // starts and ends (first chunk: inner = J*dh; last: apply d) is known at
-  // compile time.
+  // starts and ends (first chunk: inner = J*dh; last: apply d, or q4_K's min
+  // term) is known at compile time.
   for (int sbi = 0; sbi < niter / kStagesPerSb; ++sbi) {
 #pragma unroll
     for (int h = 0; h < kStagesPerSb; ++h) {
@@ -404,11 +401,14 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         // works.  Every LDS value is consumed one step after its read, so a wait
         // for it never waits for the reads just issued.
         uint32_t dhr = st.s[wt][0][lane & 31], dhr_even = 0;
-        v2i amin = {};
-        if constexpr (TYPE == QMM_Q4_K)
-          if (h == kStagesPerSb - 1) amin = *(const v2i*)(&st.mn[wr][lane >> 5][lane & 31][0]);
-        if constexpr (TYPE == QMM_Q4_K)
-          if (h == 0) a_sc = *(const v2i*)(&st.sc[wr][lane >> 5][lane & 31][0]);
+        v2i amin_hi = {}, amin_lo = {};
+        if constexpr (TYPE == QMM_Q4_K) {
+          if (h == kStagesPerSb - 1) {
+            amin_hi = *(const v2i*)(&st.mn[wr][0][lane >> 5][lane & 31][0]);
+            amin_lo = *(const v2i*)(&st.mn[wr][1][lane >> 5][lane & 31][0]);
+          }
+          a_sc = *(const v2i*)(&st.sc[wr][lane >> 5][lane & 31][0]);
+        }
         typename W::A a0 = W::load(st.a[wr][0], lane);
         v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
         typename W::A a1 = W::load(st.a[wr][1], lane);
@@ -421,7 +421,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
           // this step's epilogue
           v16f sd;
           if constexpr (TYPE == QMM_Q4_K) {
-            sd = scale_outer(a_sc, dhr, h == 0 ? b_mask0 : b_mask1, KC * h + cc);
+            sd = scale_outer(a_sc, dhr, cc < 2 ? sel0 : sel1, cc);
             pin(sd);
           }
           typename W::D dj_next;
@@ -452,21 +452,11 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
             } else {
               dhr_even = dhr;
             }
-            if (h == kStagesPerSb - 1 && cc == KC - 1) {
-              typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-              const v16f zero = {};
-              cm = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, amin),
-                                                        __builtin_bit_cast(v4h, bs), zero, 0, 0, 0);
-            }
           }
-          if constexpr (TYPE == QMM_Q4_K) {
-            if (cc == 0 && starts_sb) {
+          if constexpr (TYPE == QMM_Q4_K) {  // straight into acc: d is in the scale product
 #pragma unroll
-              for (int i = 0; i < 16; ++i) inner[i] = (float)W::dot(dj, {}, i) * sd[i];
-            } else {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)W::dot(dj, {}, i), sd[i], inner[i]);
-            }
+            for (int i = 0; i < 16; ++i) acc[i] = fmaf((float)W::dot(dj, {}, i), sd[i], acc[i]);
+            pin(acc);
           } else {
             // dh converted to f32 once per chunk and kept in a register, so the 16
             // scale FMAs are plain v_fma_f32, which issue at twice the rate of
@@ -481,8 +471,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
 #pragma unroll
               for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)W::dot(dj, {}, i), dh, inner[i]);
             }
+            pin(inner);
           }
-          pin(inner);
           if (cc + 1 < KC) {
             dj = dj_next;
             a1 = a2;
@@ -494,24 +484,24 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
           __builtin_amdgcn_sched_group_barrier(0x008, W::kMfma + (TYPE == QMM_Q4_K), 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);         // VMEM (stage copies)
           __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);         // DS reads
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA (q4_K min term)
           __builtin_amdgcn_sched_group_barrier(0x002, 72, 0);        // VALU
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (h == kStagesPerSb - 1) {  // end of a super-block: apply its d (and q4_K's dmin)
+        if (h == kStagesPerSb - 1) {  // end of a super-block
+          if constexpr (TYPE == QMM_Q4_K) {  // its min term, added into acc
+            typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+            acc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, amin_hi),
+                                                       __builtin_bit_cast(v4h, bs), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, amin_lo),
+                                                       __builtin_bit_cast(v4h, bs), acc, 0, 0, 0);
+          } else {  // q6_K: apply its d
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 d4 = *(const float4*)(&st.d[wr][8 * q + 4 * (lane >> 5)]);
-            acc[4 * q + 0] = fmaf(inner[4 * q + 0], d4.x, acc[4 * q + 0]);
-            acc[4 * q + 1] = fmaf(inner[4 * q + 1], d4.y, acc[4 * q + 1]);
-            acc[4 * q + 2] = fmaf(inner[4 * q + 2], d4.z, acc[4 * q + 2]);
-            acc[4 * q + 3] = fmaf(inner[4 * q + 3], d4.w, acc[4 * q + 3]);
-            if constexpr (TYPE == QMM_Q4_K) {
-              const float4 m4 = *(const float4*)(&st.dm[wr][8 * q + 4 * (lane >> 5)]);
-              acc[4 * q + 0] = fmaf(cm[4 * q + 0], -m4.x, acc[4 * q + 0]);
-              acc[4 * q + 1] = fmaf(cm[4 * q + 1], -m4.y, acc[4 * q + 1]);
-              acc[4 * q + 2] = fmaf(cm[4 * q + 2], -m4.z, acc[4 * q + 2]);
-              acc[4 * q + 3] = fmaf(cm[4 * q + 3], -m4.w, acc[4 * q + 3]);
+            for (int q = 0; q < 4; ++q) {
+              const float4 d4 = *(const float4*)(&st.d[wr][8 * q + 4 * (lane >> 5)]);
+              acc[4 * q + 0] = fmaf(inner[4 * q + 0], d4.x, acc[4 * q + 0]);
+              acc[4 * q + 1] = fmaf(inner[4 * q + 1], d4.y, acc[4 * q + 1]);
+              acc[4 * q + 2] = fmaf(inner[4 * q + 2], d4.z, acc[4 * q + 2]);
+              acc[4 * q + 3] = fmaf(inner[4 * q + 3], d4.w, acc[4 * q + 3]);
             }
           }
         }
@@ -520,6 +510,16 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads for g+1 landed
         __syncthreads();                                   // everyone's landed; stage g is free
       }
+    }
+  }
+  if constexpr (TYPE == QMM_Q4_K) {  // undo the rows' 2^e
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 u = *(const float4*)(wd + (size_t)(rb0 + wr) * 32 + 8 * q + 4 * (lane >> 5));
+      acc[4 * q + 0] *= u.x;
+      acc[4 * q + 1] *= u.y;
+      acc[4 * q + 2] *= u.z;
+      acc[4 * q + 3] *= u.w;
     }
   }
   if (KS > 1) {  // add k-group 1's partial sums to k-group 0's, in that order
@@ -578,7 +578,7 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
   const int vec_store = (p.od % 4 == 0) && ((uintptr_t)out % 16 == 0);
   const int64_t wgs = plan.work_groups;
   mmq_kernel<TYPE, WR, WT, KC, KS><<<dim3((unsigned)wgs), dim3(64 * WR * WT * KS), 0, s>>>(
-      p.wq, p.wd, (const uint8_t*)p.wmn, p.wdm, (const uint8_t*)p.wsc, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
+      p.wq, p.wd, (const uint8_t*)p.wmn, (const uint8_t*)p.wsc, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
       plan.dp_row_tiles, plan.split, vec_store, out, scratch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_tail == 0) return e;

@@ -138,9 +138,24 @@ def expected_planes(type_, raw, od, id_):
         w6, sc, d = oracle.decode_q6k(raw, od, id_)
         w = w6.astype(np.int32) * np.repeat(sc.astype(np.int32), 16, axis=1)
         return w, d, None, None
+    # q4_K: the codes; per row 2^-e with e = 13 - floor(log2 M), M the row's
+    # largest d*scale and dmin*min (exact in binary32); d*scale*2^e and
+    # -dmin*min*2^e per (row, chunk) as hi = f16(v), lo = f16(v - hi)
     w4, sc, mn, d, dm = oracle.decode_q4k(raw, od, id_)
-    w = w4.astype(np.int32) * np.repeat(sc.astype(np.int32), 32, axis=1)
-    return w, d, mn.astype(np.int32), dm
+    dsc = np.repeat(d.astype(np.float64), 8, axis=1) * sc
+    dmn = np.repeat(dm.astype(np.float64), 8, axis=1) * mn
+    M = np.maximum(dsc.max(axis=1), dmn.max(axis=1))
+    e = np.where(M > 0, 13 - (np.frexp(M)[1] - 1), 0)
+    pe = np.ldexp(1.0, e)[:, None]
+
+    def pair(v):
+        assert np.all(v.astype(np.float32) == v), "the scaled value is not exact in binary32"
+        hi = v.astype(np.float16)
+        lo = (v - hi.astype(np.float64)).astype(np.float16)
+        assert np.all(np.abs(v) < 2.0 ** 14)
+        return hi.view(np.uint16), lo.view(np.uint16)
+
+    return (w4.astype(np.int32), np.ldexp(1.0, -e).astype(np.float32), pair(dsc * pe), pair(-dmn * pe + 0.0))
 
 
 @pytest.mark.parametrize("type_,od,id_,full", [(synth.Q6_K, 5, 512, False), (synth.Q6_K, 130, 768, True),
@@ -151,16 +166,19 @@ def test_planes_byte_exact(type_, od, id_, full):
     raw = _full_range_q6k(rng, od, id_) if full else synth.weights(rng, type_, od, id_)
     w = qmm.register_weights(type_, od, id_, raw)
     assert w.od_pad % 128 == 0 and w.od_pad >= od
-    gw, gd, gmn, gdm = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.mn_offset,
+    gw, gd, gsc, gmn = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.mn_offset,
                                            w.dm_offset, w.sc_offset)
-    ew, ed, emn, edm = expected_planes(type_, raw, od, id_)
-    assert np.array_equal(gw[:od], ew)
+    ew, ed, esc, emn = expected_planes(type_, raw, od, id_)
+    assert np.array_equal(gw[:od], ew) and not gw[od:].any()
     assert np.array_equal(gd[:od].view(np.uint32), ed.astype(np.float32).view(np.uint32))
-    assert not gw[od:].any() and not gd[od:].any()
-    if type_ == synth.Q4_K:
-        assert np.array_equal(gmn[:od], emn)
-        assert np.array_equal(gdm[:od].view(np.uint32), edm.astype(np.float32).view(np.uint32))
-        assert not gmn[od:].any() and not gdm[od:].any()
+    if type_ == synth.Q6_K:
+        assert not gd[od:].any()
+    else:
+        assert np.all(gd[od:] == 1.0)  # padding rows: 2^0
+        assert w.dm_offset == w.plane_bytes
+        for got, exp in ((gsc, esc), (gmn, emn)):
+            for g, x in zip(got, exp):
+                assert np.array_equal(g[:od], x) and not g[od:].any()
     w.release()
 
 
