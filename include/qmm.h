@@ -122,10 +122,11 @@ int qmm_weights_info(const qmm_weights *w, qmm_info *out);
  *                 + ((k%32)/16)*512 + (j%32)*16 + k%16
  *   at wd_offset  q6_K: f32 [R][nsb][32]: d of (row, super-block)
  *                 q4_K: f32 [R][32]: 2^-e of row j, where e = 13 - floor(log2 M)
- *                 for M the largest d*scale and dmin*min over the row's blocks
+ *                 for M the largest |d*scale| and |dmin*min| over the row's blocks
  *                 (e = 0 if M = 0); the q4_K planes below hold values times 2^e
  *   q4_K only, each value v (exact in binary32) as two binary16 values
- *   hi = f16(v), lo = f16(v - hi) (round to nearest even; hi + lo == v):
+ *   hi = f16(v), lo = f16(v - hi) (round to nearest even, a zero part stored as
+ *   +0; hi + lo == v):
  *   at mn_offset  binary16 [R][nsb][2][2][32][4]: v = -dmin*min(j, c)*2^e of
  *                 (row j, chunk c), part p (0: hi, 1: lo) at element
  *                 (((j/32*nsb + c/8)*2 + p)*2 + (c%8)/4)*128 + (j%32)*4 + c%4

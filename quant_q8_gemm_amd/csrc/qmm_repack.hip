@@ -31,8 +31,8 @@ namespace qmm {
 //             (j/32*nchunk + k/32)*1024 + ((k%32)/16)*512 + (j%32)*16 + k%16
 //   wd  q6_K: f32 [R][nsb][32 rows]  d of (row, super-block)
 //       q4_K: f32 [R][32 rows]       2^-e of the row: e = 13 - floor(log2 M), M the
-//             largest d*sc and dmin*min of the row (e = 0 if M = 0), so that
-//             every scaled value is below 2^14
+//             largest |d*sc| and |dmin*min| of the row (e = 0 if M = 0), so that
+//             every scaled value is below 2^14 in magnitude
 //   wmn f16   [R][nsb][2][2][32 rows][4]  q4_K only: -dmin*min*2^e of (row j,
 //             chunk c) as hi + lo, hi = f16(v), lo = f16(v - hi), part p = 0 (hi)
 //             or 1 (lo) at element (((j/32*nsb + c/8)*2 + p)*2 + (c%8)/4)*128
@@ -85,7 +85,7 @@ q4k_row_scale_kernel(const uint8_t* __restrict__ raw, int od, int nsb, int od_pa
       for (int cl = 0; cl < 8; ++cl) {
         int sc, mn;
         q4k_scale_min(B, cl, sc, mn);
-        m = fmaxf(m, fmaxf(d * (float)sc, dmin * (float)mn));  // exact products
+        m = fmaxf(m, fmaxf(fabsf(d * (float)sc), fabsf(dmin * (float)mn)));  // exact products
       }
     }
   }
@@ -93,11 +93,13 @@ q4k_row_scale_kernel(const uint8_t* __restrict__ raw, int od, int nsb, int od_pa
   wd[j] = ldexpf(1.0f, -e);
 }
 
-// v (exact in f32, at most 17 significant bits) as hi + lo, two f16 values
+// v (exact in f32, at most 17 significant bits) as hi + lo, two f16 values; a
+// zero part is stored as +0 (the + 0 maps -0 to +0), whatever the signs that
+// formed it
 __device__ __forceinline__ void split_f16(float v, uint16_t& hi, uint16_t& lo) {
-  const _Float16 h = (_Float16)v;
+  const _Float16 h = (_Float16)(v + 0.0f);
   hi = __builtin_bit_cast(uint16_t, h);
-  lo = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)h));
+  lo = __builtin_bit_cast(uint16_t, (_Float16)((v - (float)h) + 0.0f));
 }
 
 // One thread per (row j in [0, od_pad), chunk c, k-half h): 16 weights.
@@ -158,7 +160,7 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
         const int64_t si = ((((int64_t)rb * nsb + b) * 2 + (cl >> 2)) * 2 + ((cl & 3) >> 1)) * 32 + jr;
         wsc[si * 4 + (cl & 1) * 2] = hi;
         wsc[si * 4 + (cl & 1) * 2 + 1] = lo;
-        split_f16(-(dmin * (float)mn) * pe + 0.0f, hi, lo);  // + 0: a zero min stored as +0
+        split_f16(-(dmin * (float)mn) * pe, hi, lo);
         const int64_t mi = (((int64_t)rb * nsb + b) * 2) * 2 + (cl >> 2);
         wmn[mi * 128 + jr * 4 + (cl & 3)] = hi;
         wmn[(mi + 2) * 128 + jr * 4 + (cl & 3)] = lo;

@@ -144,18 +144,18 @@ def expected_planes(type_, raw, od, id_):
     w4, sc, mn, d, dm = oracle.decode_q4k(raw, od, id_)
     dsc = np.repeat(d.astype(np.float64), 8, axis=1) * sc
     dmn = np.repeat(dm.astype(np.float64), 8, axis=1) * mn
-    M = np.maximum(dsc.max(axis=1), dmn.max(axis=1))
+    M = np.maximum(np.abs(dsc).max(axis=1), np.abs(dmn).max(axis=1))
     e = np.where(M > 0, 13 - (np.frexp(M)[1] - 1), 0)
     pe = np.ldexp(1.0, e)[:, None]
 
-    def pair(v):
+    def pair(v):  # zero parts as +0 (the + 0.0)
         assert np.all(v.astype(np.float32) == v), "the scaled value is not exact in binary32"
-        hi = v.astype(np.float16)
-        lo = (v - hi.astype(np.float64)).astype(np.float16)
+        hi = (v + 0.0).astype(np.float16)
+        lo = ((v - hi.astype(np.float64)) + 0.0).astype(np.float16)
         assert np.all(np.abs(v) < 2.0 ** 14)
         return hi.view(np.uint16), lo.view(np.uint16)
 
-    return (w4.astype(np.int32), np.ldexp(1.0, -e).astype(np.float32), pair(dsc * pe), pair(-dmn * pe + 0.0))
+    return (w4.astype(np.int32), np.ldexp(1.0, -e).astype(np.float32), pair(dsc * pe), pair(-dmn * pe))
 
 
 @pytest.mark.parametrize("type_,od,id_,full", [(synth.Q6_K, 5, 512, False), (synth.Q6_K, 130, 768, True),
@@ -179,6 +179,45 @@ def test_planes_byte_exact(type_, od, id_, full):
         for got, exp in ((gsc, esc), (gmn, emn)):
             for g, x in zip(got, exp):
                 assert np.array_equal(g[:od], x) and not g[od:].any()
+    w.release()
+
+
+@pytest.mark.parametrize("type_", [synth.Q4_K, synth.Q6_K], ids=["q4_K", "q6_K"])
+def test_extreme_block_scales(type_):
+    """Super-block scales of either sign, huge (60000) and subnormal (2^-24):
+    the planes stay byte-exact (q4_K's row exponent takes magnitudes) and the
+    MMQ stays within the tolerance.  Blocks are drawn as usual, then their f16
+    d (and q4_K dmin) bits are rewritten."""
+    od, id_, T = 90, 1024, 70
+    say(f"extreme block scales {synth.TYPE_NAMES[type_]}")
+    rng = np.random.default_rng(9)
+    bb = 144 if type_ == synth.Q4_K else 210
+    raw = synth.weights(rng, type_, od, id_).reshape(-1, bb).copy()
+    nb = raw.shape[0]
+    fields = [(0, 2), (2, 4)] if type_ == synth.Q4_K else [(208, 210)]
+    for lo, hi in fields:
+        bits = raw[:, lo:hi].copy().view("<u2").reshape(-1)
+        pick = rng.random(nb)
+        bits = np.where(pick < 0.3, bits | 0x8000, bits)                 # negative
+        bits = np.where((pick >= 0.3) & (pick < 0.35), 0x7B53, bits)     # 60000
+        bits = np.where((pick >= 0.35) & (pick < 0.40), 0x0001, bits)    # 2^-24
+        raw[:, lo:hi] = bits.astype("<u2").view(np.uint8).reshape(nb, 2)
+    raw = raw.reshape(-1)
+    w = qmm.register_weights(type_, od, id_, raw)
+    got = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.mn_offset,
+                              w.dm_offset, w.sc_offset)
+    exp = expected_planes(type_, raw, od, id_)
+    assert np.array_equal(got[0][:od], exp[0])
+    assert np.array_equal(got[1][:od].view(np.uint32), np.asarray(exp[1], np.float32).view(np.uint32))
+    if type_ == synth.Q4_K:
+        for g, x in zip(got[2] + got[3], exp[2] + exp[3]):
+            assert np.array_equal(g[:od], x)
+    x = synth.activations(rng, T, id_, False)
+    qact = gpu_quantize(x)
+    q, dh, s = check_prepass(x, qact)
+    out = run_mmq(w, qact, T)
+    ref, A = oracle.mmq(type_, raw, od, id_, q, dh, s)
+    check_close(out, ref, A, "extreme block scales")
     w.release()
 
 
