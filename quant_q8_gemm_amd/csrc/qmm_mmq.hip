@@ -43,8 +43,8 @@ namespace qmm {
 // with too few tiles to keep the CUs busy.  The inner dimension is walked in
 // stages of KC chunks of 32 (KC = 2, 4 or 8: a quarter, half or whole 256-wide
 // super-block).  Each stage's operands -- the weight fragments of the WR row
-// blocks, the q8 codes and scale pairs of the WT token blocks, and d (and for
-// q4_K the scales, the mins and dmin) -- are copied once per
+// blocks, the q8 codes and scale pairs of the WT token blocks, and q6_K's d or
+// q4_K's scale and min pairs -- are copied once per
 // work-group into LDS with direct global->LDS loads (global_load_lds_dwordx4
 // puts lane l's 16 bytes at the LDS base + 16*l, so one wave instruction moves
 // 1 KiB), and read from there by every wave that shares them.  Two LDS stages
@@ -53,8 +53,9 @@ namespace qmm {
 // A small tile and a small LDS footprint let several work-groups share a CU, so
 // one group's barrier wait is covered by the others' work.
 // MFMA orientation: A = weights (rows j), B = activations (columns t), so each
-// lane's 16 outputs share one token: the activation scale dh is one register
-// per chunk, and the super-block d is applied once per 8 chunks.
+// lane's 16 outputs share one token: q6_K's activation scale dh is one register
+// per chunk and its super-block d is applied once per 8 chunks; q4_K's scale
+// products come as a 32 x 32 block from the matrix core.
 // ---------------------------------------------------------------------------
 // Direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4: lane
 // l's bytes land at the LDS byte address held in M0 plus 16*l).  Written out so
@@ -275,8 +276,9 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   // fragments, then the code fragments, split into equal contiguous runs per
   // wave (a run stays inside one row / token block, so its source is one
   // uniform base plus immediate 1 KiB steps; with fewer weight jobs than waves,
-  // the first waves take one each); then the small region (scale pairs, mins,
-  // scale bytes, d) in 16-byte units per lane, one job each for the first waves.
+  // the first waves take one each); then the small region (activation scale
+  // pairs, q4_K scale and min pairs, q6_K d) in 16-byte units per lane, one job
+  // each for the first waves.
   constexpr int kFrag = kFragA<TYPE>;
   constexpr int kPerRbA = KC * kFrag / 1024;  // weight jobs per row block and stage
   static_assert(kJobsA % kWaves == 0 || kJobsA < kWaves, "equal weight runs per wave");
@@ -396,9 +398,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         const bool starts_sb = h == 0;
         // Software pipeline over the KC chunks: step cc issues the MFMA(s) of
         // chunk cc+1 (operands read one step earlier), then the LDS reads of chunk
-        // cc+2 and of chunk cc+1's activation scale (and q4_K scale bytes), then
-        // the scale epilogue of chunk cc on the vector ALU while the matrix core
-        // works.  Every LDS value is consumed one step after its read, so a wait
+        // cc+2 and of chunk cc+1's activation scale, then the scale epilogue of
+        // chunk cc on the vector ALU while the matrix core works.  Every LDS value is consumed one step after its read, so a wait
         // for it never waits for the reads just issued.
         uint32_t dhr = st.s[wt][0][lane & 31], dhr_even = 0;
         v2i amin_hi = {}, amin_lo = {};
