@@ -315,6 +315,9 @@ SMALL = [("q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          ("q6_K 4200x768 T=500", synth.Q6_K, 4200, 768, 500, True),
          # far fewer tiles than CUs (24): every tile split along K
          ("q6_K 512x2816 T=300", synth.Q6_K, 512, 2816, 300, False),
+         # the same for q4_K: partials of the row-scaled accumulators, unscaled
+         # before the fixup adds them
+         ("q4_K 512x3072 T=300", synth.Q4_K, 512, 3072, 300, True),
          # enough 64 x 64 tiles (>= 1024) to select the many-tile geometry;
          # q6_K there runs 64 x 128 tiles two per CU: 528 tiles on 512 slots
          # (a split tail), and 1088 tiles (two full waves and a ragged third)
@@ -415,7 +418,8 @@ LAYER = [(f"layer {synth.TYPE_NAMES[t]} {od}x{id_} T={synth.LAYER_TOKENS}", t, o
          for t, od, id_ in sorted({(t, od, id_) for _, t, od, id_ in synth.LAYER_GEMMS})]
 # one GPU's share of ffn_down under 8-way tensor parallelism (column and row slices)
 SHARDS = [("q6_K ffn_down column shard 512x11008 T=512", synth.Q6_K, 512, 11008, 512, False),
-          ("q6_K ffn_down row shard 4096x1536 T=512", synth.Q6_K, 4096, 1536, 512, False)]
+          ("q6_K ffn_down row shard 4096x1536 T=512", synth.Q6_K, 4096, 1536, 512, False),
+          ("q4_K ffn_gate column shard 1376x4096 T=512", synth.Q4_K, 1376, 4096, 512, False)]
 FULL = [synth.FFN_DOWN, synth.FFN_DOWN_ODD, synth.ATTN, synth.GATE_UP, synth.HEAD] + LAYER + SHARDS
 
 
