@@ -110,8 +110,11 @@ KERNEL_SRC = os.path.join(ROOT, "quant_q8_gemm_amd", "csrc", "qmm_mmq.hip")
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="before the warm-up steps, run untimed steps for at least this long so the "
+                         "shader clock has left its idle state (0: none)")
     ap.add_argument("--workload", default="ffn_down", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-weights pass")
@@ -290,6 +293,18 @@ def main():
         for g in gemms:
             gemm(g)
 
+    # Clock settling: from idle the step runs up to 35% slower for its first
+    # ~40 ms while the GPU raises its clocks; the timed steps measure the rate a
+    # loaded GPU sustains, whatever --warmup asks for.
+    settle_steps = 0
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(20):
+            step()
+        settle_steps += 20
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -387,6 +402,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle": {"steps": settle_steps, "ms": round(settle_ms, 1)},
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

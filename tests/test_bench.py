@@ -34,6 +34,7 @@ def test_bench_json_line_contract():
                      ("roofline", dict), ("cpu_baseline", dict)):
         assert isinstance(d[key], typ), key
     assert d["n_gpus"] == 1 and d["steps"] == 5 and d["warmup"] == 2
+    assert d["clock_settle"]["steps"] > 0 and d["clock_settle"]["ms"] >= 300.0
     assert d["value"] > 0 and d["higher_is_better"] is True and d["vs_baseline"] is None
     assert d["config"]["workload"]
     rl = d["roofline"]
