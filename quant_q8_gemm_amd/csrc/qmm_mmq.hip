@@ -549,22 +549,42 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
 
 // Adds each tail tile's `split` partials in slice order and stores the tile.
 // One work-group per (tail tile, 32 x 32 block); thread (q, lane) sums the four
-// values acc[4*q .. 4*q+3] of that lane over the slices.
+// values acc[4*q .. 4*q+3] of that lane over the slices.  The loads of up to
+// kFixBatch slices are issued before their adds, so a tile split many ways (21
+// slices for 4097 rows) waits for memory once per batch rather than once per
+// slice; the adds keep slice order.
+constexpr int kFixBatch = 8;
+
 template <int WR, int WT>
 __global__ void __launch_bounds__(256)
 mmq_fixup_kernel(const float* __restrict__ part, int split, int dp_row_tiles, int tok_tiles, int od,
                  int n_tok, int vec_store, float* __restrict__ out) {
   constexpr int kWaves = WR * WT;
+  constexpr size_t kSlice = (size_t)kWaves * 1024;  // floats per slice of one tile
   const int u = blockIdx.x / kWaves, w = blockIdx.x % kWaves;
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const float* src = part + ((size_t)u * split * kWaves + w) * 1024 + (4 * q) * 64 + lane;
-  float4 v = make_float4(src[0], src[64], src[128], src[192]);
-  for (int sl = 1; sl < split; ++sl) {
-    src += (size_t)kWaves * 1024;
-    v.x += src[0];
-    v.y += src[64];
-    v.z += src[128];
-    v.w += src[192];
+  float4 v;
+  for (int sl = 0; sl < split; sl += kFixBatch) {
+    // a short last batch loads and adds only the slices that exist
+    float4 t[kFixBatch];
+#pragma unroll
+    for (int b = 0; b < kFixBatch; ++b) {
+      if (sl + b < split) {
+        const float* p = src + (size_t)(sl + b) * kSlice;
+        t[b] = make_float4(p[0], p[64], p[128], p[192]);
+      }
+    }
+    if (sl == 0) v = t[0];
+#pragma unroll
+    for (int b = 0; b < kFixBatch; ++b) {
+      if ((sl > 0 || b > 0) && sl + b < split) {
+        v.x += t[b].x;
+        v.y += t[b].y;
+        v.z += t[b].z;
+        v.w += t[b].w;
+      }
+    }
   }
   const int rt = dp_row_tiles + u / tok_tiles, tt = u % tok_tiles;
   store_quad(out, v, rt * WR + w / WT, tt * WT + w % WT, lane, q, od, n_tok, vec_store);
