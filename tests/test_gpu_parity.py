@@ -521,6 +521,31 @@ def test_concurrent_streams_share_a_handle():
     w.release()
 
 
+def test_tail_scratch_shared_across_shapes():
+    """Launches with different tail tile counts and splits (264 tiles on 256
+    CUs, 24 tiles all split, a q4_K shape with its own geometry) share one
+    stream's tail scratch in turn: each repeat gives its first result bit for
+    bit, which agrees with the oracle."""
+    say("tail scratch across shapes")
+    cases = [(synth.Q6_K, 4200, 768, 500, 21), (synth.Q6_K, 512, 2816, 300, 22),
+             (synth.Q4_K, 4160, 1024, 512, 23)]
+    runs = []
+    for type_, od, id_, T, seed in cases:
+        raw, x = synth.case(type_, od, id_, T, seed=seed)
+        w = qmm.register_weights(type_, od, id_, raw)
+        qact = gpu_quantize(x)
+        first = run_mmq(w, qact, T)
+        q, dh, sm = oracle.quantize(x)
+        ref, A = oracle.mmq(type_, raw, od, id_, q, dh, sm)
+        check_close(first, ref, A, f"type {type_} od {od} T {T}")
+        runs.append((w, qact, T, od, first))
+    for _ in range(3):
+        for w, qact, T, od, first in runs:
+            assert np.array_equal(run_mmq(w, qact, T), first)
+    for w, *_ in runs:
+        w.release()
+
+
 def test_writes_stay_inside_output():
     type_, od, id_, T = synth.Q4_K, 77, 512, 45
     say("output bounds")
