@@ -203,6 +203,31 @@ __device__ __forceinline__ void store_quad(float* __restrict__ out, float4 v, in
   }
 }
 
+// Store one wave's 32 x 32 block through LDS: the lane's 16 values go to the
+// wave's 32 x 33 float region in [row][token] order (33: the reads below hit 32
+// different banks) and come back with lane l holding row l % 32 of tokens
+// 2k + l / 32, so each store instruction writes two runs of 32 consecutive
+// floats of out, at any od and alignment, where store_block's lanes write
+// 16-byte pieces of 32 different token rows (or 4-byte ones when od % 4 != 0).
+//   lds   the wave's 32 * 33 floats, free for it to use
+__device__ __forceinline__ void store_block_lds(float* __restrict__ out, const v16f& acc, float* lds, int rblock,
+                                                int tblock, int lane, int od, int n_tok) {
+  const int t = lane & 31, rb = 4 * (lane >> 5);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds[(rb + 8 * q + i) * 33 + t] = acc[4 * q + i];
+  const int r = lane & 31, j = rblock * 32 + r;
+  if (j >= od) return;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int tl = 2 * k + (lane >> 5);
+    const int tok = tblock * 32 + tl;
+    const float v = lds[r * 33 + tl];
+    if (tok < n_tok) out[(size_t)tok * od + j] = v;
+  }
+}
+
 __device__ __forceinline__ void store_block(float* __restrict__ out, const v16f& acc, int rblock, int tblock,
                                             int lane, int od, int n_tok, int vec_store) {
 #pragma unroll
@@ -537,6 +562,21 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
     }
   }
 
+  if (tail_idx < 0 && !vec_store) {
+    // Without 16-byte stores (od % 4 != 0), through LDS: after the k-group
+    // combine's region (kWaves x 4 KiB), or with one k-group once every wave
+    // is done with the stage buffers.  od 4097 x 11008 at 509 tokens: 4-5%
+    // faster.  With 16-byte stores it measured within 1% either way, and with
+    // one k-group its barrier cost ~1% (q4_K 11008 x 4096, 3314 tokens), so
+    // those stay direct.
+    constexpr size_t kRed = KS > 1 ? (size_t)kWaves * 1024 : 0;
+    static_assert((kRed + (size_t)kWaves * 32 * 33) * sizeof(float) <= KS * 2 * sizeof(St),
+                  "room for the transposes after the combine's region");
+    if (KS == 1) __syncthreads();
+    if (ks != 0) return;
+    store_block_lds(out, acc, (float*)stage_all + kRed + wave * 32 * 33, rb0 + wr, tb0 + wt, lane, od, n_tok);
+    return;
+  }
   if (ks != 0) return;
   if (tail_idx < 0) {
     store_block(out, acc, rb0 + wr, tb0 + wt, lane, od, n_tok, vec_store);
