@@ -77,9 +77,9 @@ typedef struct {
     int64_t od_pad;      /* rows padded with zeros to the row tile */
     size_t raw_bytes;    /* od * (id/256) * (144 or 210): the k-quant bytes */
     size_t plane_bytes;  /* device memory the handle holds */
-    size_t wd_offset;    /* byte offset of the d (q6_K) or row-scale (q4_K) plane */
+    size_t wd_offset;    /* byte offset of the d plane (q4_K: d and -dmin) */
     size_t mn_offset;    /* byte offset of the min plane (q4_K; else == plane_bytes) */
-    size_t dm_offset;    /* no plane: always == plane_bytes (dmin is folded into the min plane) */
+    size_t dm_offset;    /* no plane: always == plane_bytes (q4_K's dmin is in the d plane) */
     size_t sc_offset;    /* byte offset of the f16 scale plane (q4_K; else == plane_bytes) */
 } qmm_info;
 
@@ -120,20 +120,16 @@ int qmm_weights_info(const qmm_weights *w, qmm_info *out);
  *                 q4_K: int8 [R][nchunk][2][32][16]: the 4-bit code (0..15)
  *                 of (row j, k) at byte (j/32*nchunk + k/32)*1024
  *                 + ((k%32)/16)*512 + (j%32)*16 + k%16
- *   at wd_offset  q6_K: f32 [R][nsb][32]: d of (row, super-block)
- *                 q4_K: f32 [R][32]: 2^-e of row j, where e = 13 - floor(log2 M)
- *                 for M the largest |d*scale| and |dmin*min| over the row's blocks
- *                 (e = 0 if M = 0); the q4_K planes below hold values times 2^e
- *   q4_K only, each value v (exact in binary32) as two binary16 values
- *   hi = f16(v), lo = f16(v - hi) (round to nearest even, a zero part stored as
- *   +0; hi + lo == v):
- *   at mn_offset  binary16 [R][nsb][2][2][32][4]: v = -dmin*min(j, c)*2^e of
- *                 (row j, chunk c), part p (0: hi, 1: lo) at element
- *                 (((j/32*nsb + c/8)*2 + p)*2 + (c%8)/4)*128 + (j%32)*4 + c%4
- *   at sc_offset  binary16 [R][nsb][2][2][32][2][2]: v = d*scale(j, c)*2^e of
- *                 (row j, chunk c), part p at element
- *                 ((((j/32*nsb + c/8)*2 + (c%8)/4)*2 + (c%4)/2)*32 + j%32)*4
- *                 + (c%2)*2 + p
+ *   at wd_offset  q6_K: f32 [R][nsb][32]: d of (row j, super-block b) at
+ *                 element (j/32*nsb + b)*32 + j%32
+ *                 q4_K: f32 [R][nsb][2][32]: d*2^25 (part 0) and -dmin
+ *                 (part 1) of (row j, super-block b) at element
+ *                 ((j/32*nsb + b)*2 + part)*32 + j%32; both exact in binary32,
+ *                 zeros stored as +0
+ *   q4_K only, the 6-bit scale and min of (row j, chunk c) as binary16 integers,
+ *   each at element ((j/32*nsb + c/8)*2 + (c%8)/4)*128 + (j%32)*4 + c%4 of:
+ *   at mn_offset  binary16 [R][nsb][2][32][4]: the mins
+ *   at sc_offset  binary16 [R][nsb][2][32][4]: the scales
  * Errors: QMM_EINVAL (null pointers, bytes mismatch), QMM_EHIP.
  */
 int qmm_weights_export(const qmm_weights *w, void *host, size_t bytes);

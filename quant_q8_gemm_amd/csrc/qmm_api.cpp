@@ -182,7 +182,7 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   w->plane_bytes = plane_bytes;
   w->wd_offset = off_wd;
   w->mn_offset = type == QMM_Q4_K ? off_mn : plane_bytes;
-  w->dm_offset = plane_bytes;  // no dmin plane: q4_K's dmin is folded into its min plane
+  w->dm_offset = plane_bytes;  // no plane of its own: q4_K's dmin sits in the d plane
   w->sc_offset = type == QMM_Q4_K ? off_sc : plane_bytes;
   w->alloc = alloc;
   if (getenv("QMM_LOG") != nullptr)

@@ -8,23 +8,26 @@
 //
 // MI355X design (differs from the pages' GB10 kernels on purpose):
 //  * the d*scale pair plane of r56 section 2.2 becomes integer arithmetic: the
-//    block dot J of a 32-block already carries the small integer group scales,
-//    exactly, and only the f16 d of the 256-weight super-block stays a float,
-//    applied once per super-block.  q6_K (two 16-groups per 32-block, int8
-//    scales): the scale is multiplied into the codes at registration and the
-//    folded weight split into two int8 planes (hi = w >> 6, lo = w & 63), so one
-//    K=32 int8 MFMA per plane gives J = 64*J_hi + J_lo.  q4_K (one 6-bit scale
-//    per 32-block): the 4-bit codes are int8 bytes, one K=32 MFMA gives the
-//    code dot D, and the products d*sc(row)*dh(token) of the block's scale
-//    and the activation scale come from one small f16 MFMA (an outer product),
-//    so each element costs a conversion and an FMA, and no super-block d is
-//    left to apply;
+//    block dot of a 32-block carries the small integer group scales exactly,
+//    and only the f16 d (and q4_K's dmin) of the 256-weight super-block stays a
+//    float, applied once per super-block.  q6_K (two 16-groups per 32-block,
+//    int8 scales): the scale is multiplied into the codes at registration and
+//    the folded weight split into two int8 planes (hi = w >> 6, lo = w & 63), so
+//    one K=32 int8 MFMA per plane gives J = 64*J_hi + J_lo.  q4_K (one 6-bit
+//    scale per 32-block): the 4-bit codes are int8 bytes, one K=32 MFMA gives
+//    the code dot D, and the products sc(row)*dh(token) of the block's scale
+//    and the activation scale come from one small f16 MFMA (an outer product of
+//    exact f16 values, so every product is exact);
+//  * q4_K's block dot leaves the matrix core already as an f32: the MFMA's
+//    accumulator input is the inline constant 1/(2 pi), whose bit pattern
+//    0x3E22F983 plus any |D| < 2^21 is the f32 value c0 + D*2^-26 (one binade,
+//    spacing 2^-26), so D*2^-26 = that value - c0 exactly, one full-rate
+//    subtraction where an integer-to-float conversion issues at half rate;
 //  * planes are stored in MFMA fragment order, so every lane's operand is one
 //    contiguous 16-byte load and a wave's load is one contiguous 1 KiB;
 //  * the q4_K min term sum_c dmin*min_c*s_c is a small matrix product over
-//    chunks: per super-block, two f16 MFMAs (32x32x8) of the f16 scaled sums
-//    with dmin*min as an exact pair of f16 values, accumulating straight into
-//    the f32 output accumulators.
+//    chunks: per super-block, one f16 MFMA (32x32x8) of the 6-bit mins and the
+//    f16 scaled sums, times dmin.
 #include "qmm_internal.h"
 #include "qmm_common.h"
 
@@ -87,16 +90,17 @@ struct alignas(16) Stage {
   int8_t a[WR][KC][kFragA<TYPE>];    // weight fragments: [row block][chunk]
   int8_t b[WT][KC][1024];            // q8 codes: [token block][chunk][fragment]
   uint32_t s[WT][KC][32];            // (dh, s) pairs: [token block][chunk][token]
-  // q4_K: the stage's d*sc*2^e as f16 pairs (hi, lo): [row block][chunk/2][row][chunk%2]
-  uint32_t sc[kQ4 ? WR : 0][2][32][2];
-  float d[kQ4 ? 0 : WR][32];         // q6_K: super-block d: [row block][row]
-  // q4_K: -dmin*min*2^e of the super-block as f16: [row block][hi, lo][chunk/4][row][chunk%4]
-  uint16_t mn[kQ4 ? WR : 0][2][2][32][4];
-  // s, sc, d and mn are contiguous: the "small" region, copied in 16-byte units
-  // (s and sc with every stage, d and mn with a super-block's last).
-  static constexpr int kUnitsS = WT * KC * 8, kUnitsSc = kQ4 ? WR * 32 : 0, kUnitsD = kQ4 ? 0 : WR * 8,
-                       kUnitsMn = kQ4 ? WR * 64 : 0;
-  static constexpr int kUnits = kUnitsS + kUnitsSc + kUnitsD + kUnitsMn;
+  // q4_K: the stage's 4 scales as f16 integers: [row block][row][chunk]
+  uint16_t sc[kQ4 ? WR : 0][32][4];
+  // q4_K: the super-block's 8 mins as f16 integers: [row block][chunk/4][row][chunk%4]
+  uint16_t mn[kQ4 ? WR : 0][2][32][4];
+  // q6_K: super-block d: [row block][row]; q4_K: [row block][d*2^25, -dmin][row]
+  float d[WR][kQ4 ? 2 : 1][32];
+  // s, sc, mn and d are contiguous: the "small" region, copied in 16-byte units
+  // (s and sc with every stage, mn and d with a super-block's last).
+  static constexpr int kUnitsS = WT * KC * 8, kUnitsSc = kQ4 ? WR * 16 : 0, kUnitsMn = kQ4 ? WR * 32 : 0,
+                       kUnitsD = kQ4 ? WR * 16 : WR * 8;
+  static constexpr int kUnits = kUnitsS + kUnitsSc + kUnitsMn + kUnitsD;
   static constexpr int kSmallJobs = (kUnits + 63) / 64;
 };
 
@@ -114,14 +118,29 @@ struct WeightOps<QMM_Q6_K> {
   __device__ static A load(const int8_t* frag, int lane) {
     return {*(const v4i*)(frag + lane * 16), *(const v4i*)(frag + 1024 + lane * 16)};
   }
-  __device__ static D mma(const A& a, v4i bq) {
+  __device__ static D mma(const A& a, v4i bq, int) {
     const v16i zero = {};
     return {__builtin_amdgcn_mfma_i32_32x32x32_i8(a.hi, bq, zero, 0, 0, 0),
             __builtin_amdgcn_mfma_i32_32x32x32_i8(a.lo, bq, zero, 0, 0, 0)};
   }
   __device__ static void keep(D& d) { pin(d.hi); pin(d.lo); }
-  __device__ static int dot(const D& d, v4i, int i) { return (d.hi[i] << 6) + d.lo[i]; }
+  // the scale-folded block dot J of output element i, as an f32 (exact: |J| < 2^24)
+  __device__ static float val(const D& d, int i) { return (float)((d.hi[i] << 6) + d.lo[i]); }
 };
+
+// q4_K block dots come out of the matrix core biased: the accumulator input is
+// the bit pattern of the f32 value kQ4Bias (1/(2 pi), encoded as an inline
+// constant of the instruction, so it costs no register), and since the code dot
+// |D| <= 32*15*127 = 60960 is far inside the 2291075 steps below and 6097533
+// above it that its binade [1/8, 1/4) holds, the f32 value of the result's bits
+// is kQ4Bias + D*2^-26 exactly.  Subtracting kQ4Bias is exact (both within a
+// factor of two), so val() = D*2^-26 with one full-rate subtraction.
+// The compiler encodes the splat as the inline constant only for an MFMA whose
+// accumulator input is used by no other instruction of its basic block; a
+// uniform branch that is always taken (live != 0) gives every such MFMA a block
+// of its own, for two scalar instructions.  Shared, the splat is materialized
+// in 16 registers, which the kernel does not have.
+constexpr uint32_t kQ4BiasBits = 0x3E22F983u;
 
 template <>
 struct WeightOps<QMM_Q4_K> {
@@ -129,34 +148,43 @@ struct WeightOps<QMM_Q4_K> {
   struct D { v16i c; };
   static constexpr int kMfma = 1;
   __device__ static A load(const int8_t* frag, int lane) { return {*(const v4i*)(frag + lane * 16)}; }
-  __device__ static D mma(const A& a, v4i bq) {
-    const v16i zero = {};
-    return {__builtin_amdgcn_mfma_i32_32x32x32_i8(a.c, bq, zero, 0, 0, 0)};
+  //   live  nonzero (the launch's chunk count); the result is undefined otherwise
+  __device__ static D mma(const A& a, v4i bq, int live) {
+    D r;
+    if (live) {
+      const v16i bias = (v16i)(int)kQ4BiasBits;
+      r.c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a.c, bq, bias, 0, 0, 0);
+    }
+    return r;
   }
   __device__ static void keep(D& d) { pin(d.c); }
-  // the code dot D of output element i; the 6-bit scale is not in it but in the
-  // scale product that multiplies it (scale_outer below)
-  __device__ static int dot(const D& d, v4i, int i) { return d.c[i]; }
+  // D*2^-26 of output element i; the 6-bit scale is not in it but in the scale
+  // product that multiplies it (scale_outer below)
+  // (the whole vector is reinterpreted: hipcc's __builtin_bit_cast of one
+  // element of an ext-vector reads element 0 whatever the index)
+  __device__ static float val(const D& d, int i) {
+    const v16f f = __builtin_bit_cast(v16f, d.c);
+    return f[i] - __builtin_bit_cast(float, kQ4BiasBits);
+  }
 };
 
 // q4_K: the scale of output element (row j, token t) of chunk c is
-// d(j)*sc(j, c) * dh(t, c), an outer product of a row vector and a token vector.
-// d*sc (an f16 times a 6-bit integer) is held, times the row's power of two 2^e,
-// as an exact pair of f16 values hi + lo, and dh is an f16 value, so one f16 MFMA
-// (32x32x8) forms all 32 x 32 products (hi + lo)*dh, each exact before one f32
-// rounding, in the same output layout as the int8 MFMA's block dots: the epilogue
-// is one conversion and one FMA per element, and no super-block d is left to
-// apply.  A holds the pairs of the stage's 4 chunks (lane half h: chunks 2h and
-// 2h+1, k = 4h + 2*(chunk%2) + {hi, lo}); B holds the chunk's dh in both of its
-// slots and zeros elsewhere, so the sum over k keeps just that chunk's product.
+// d(j)*sc(j, c) * dh(t, c); d is applied once per super-block, and the outer
+// product sc(j, c)*dh(t, c) of a row vector and a token vector -- both exact f16
+// values, a 6-bit integer and the f16 activation scale -- comes from one f16
+// MFMA (32x32x8) in the same output layout as the int8 MFMA's block dots.  A
+// holds the stage's 4 scales of the lane's row (the same 4 on both lane halves,
+// k = 4*half + chunk), B the chunk's dh in slot cc of both halves and zeros
+// elsewhere, so each product is formed twice and added: 2*sc*dh, exact.  That
+// 2 and the block dot's 2^-26 are undone by the plane's d*2^25.
 // cc is the chunk's index in the stage (a constant once the loops are unrolled).
-//   a_sc      the lane's 4 f16 values (row lane & 31, chunks 2*(lane/32)..+1)
+//   a_sc      the lane's 4 f16 scales (row lane & 31, the stage's chunks)
 //   dh_bits   the chunk's (dh, s) pair of the lane's token (lane & 31)
-//   sel       byte selector: dh twice on the lanes of half cc/2, else zero
-__device__ __forceinline__ v16f scale_outer(v2i a_sc, uint32_t dh_bits, uint32_t sel, int cc) {
+__device__ __forceinline__ v16f scale_outer(v2i a_sc, uint32_t dh_bits, int cc) {
   typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-  const uint32_t y = __builtin_amdgcn_perm(0u, dh_bits, sel);
-  const v2i b = {cc % 2 == 0 ? (int)y : 0, cc % 2 == 0 ? 0 : (int)y};
+  // dh into the low (cc even) or high (cc odd) half of the word, zero elsewhere
+  const uint32_t y = __builtin_amdgcn_perm(0u, dh_bits, cc % 2 == 0 ? 0x0C0C0100u : 0x01000C0Cu);
+  const v2i b = {cc < 2 ? (int)y : 0, cc < 2 ? 0 : (int)y};
   const v16f zero = {};
   return __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, a_sc), __builtin_bit_cast(v4h, b), zero,
                                               0, 0, 0);
@@ -258,7 +286,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   constexpr int kJobsA = WR * KC * kFragA<TYPE> / 1024, kJobsB = WT * KC;
   static_assert(KC == 2 || KC == 4 || KC == 8, "a stage is a quarter, half or a whole super-block");
   static_assert(KS == 1 || KS == 2, "one or two k-groups");
-  static_assert(__builtin_offsetof(St, d) == __builtin_offsetof(St, s) + 16 * (St::kUnitsS + St::kUnitsSc) &&
+  static_assert(__builtin_offsetof(St, d) ==
+                        __builtin_offsetof(St, s) + 16 * (St::kUnitsS + St::kUnitsSc + St::kUnitsMn) &&
                     sizeof(St) == __builtin_offsetof(St, s) + 16 * St::kUnits,
                 "the small region is contiguous and ends the stage");
   // the q4_K min term collects a super-block's 8 chunks over two stages
@@ -322,29 +351,31 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
                         (size_t)gbeg * KC * 1024;
   const uint32_t lane_off = (uint32_t)lane * 16;
   const uint8_t* small_src = nullptr;
-  // 0 none; per stage: 1 pairs (128 bytes per chunk), 3 q4_K scale pairs (512
-  // bytes); per super-block, at its last stage: 2 q6_K d (128 bytes), 4 q4_K
-  // mins (1 KiB)
+  // 0 none; per stage: 1 pairs (128 bytes per chunk), 3 q4_K scales (256 bytes
+  // per row block); per super-block, at its last stage: 4 q4_K mins (512
+  // bytes), 2 q6_K d (128 bytes) or q4_K d and dmin (256 bytes)
   int small_kind = 0;
+  constexpr int kDBytes = TYPE == QMM_Q4_K ? 256 : 128;  // d plane bytes per (row block, super-block)
   if (wave < St::kSmallJobs) {
     const int u = wave * 64 + lane;
     const int sb0g = gbeg / kStagesPerSb;
-    constexpr int eSc = St::kUnitsS + St::kUnitsSc, eD = eSc + St::kUnitsD;
+    constexpr int eSc = St::kUnitsS + St::kUnitsSc, eMn = eSc + St::kUnitsMn;
     if (u < St::kUnitsS) {
       small_src = qs + ((size_t)(tb0 + u / (KC * 8)) * nchunk + gbeg * KC) * 128 + (u % (KC * 8)) * 16;
       small_kind = 1;
     } else if (u < eSc) {
       const int v = u - St::kUnitsS;
-      small_src = wsc + ((size_t)(rb0 + v / 32) * nsb * 2 + gbeg) * 512 + (v % 32) * 16;
+      small_src = wsc + ((size_t)(rb0 + v / 16) * nsb * 2 + gbeg) * 256 + (v % 16) * 16;
       small_kind = 3;
-    } else if (u < eD) {
+    } else if (u < eMn) {
       const int v = u - eSc;
-      small_src = (const uint8_t*)wd + ((size_t)(rb0 + v / 8) * nsb + sb0g) * 128 + (v % 8) * 16;
-      small_kind = 2;
-    } else if (u < St::kUnits) {
-      const int v = u - eD;
-      small_src = wmn + ((size_t)(rb0 + v / 64) * nsb + sb0g) * 1024 + (v % 64) * 16;
+      small_src = wmn + ((size_t)(rb0 + v / 32) * nsb + sb0g) * 512 + (v % 32) * 16;
       small_kind = 4;
+    } else if (u < St::kUnits) {
+      const int v = u - eMn;
+      small_src = (const uint8_t*)wd + ((size_t)(rb0 + v / (kDBytes / 16)) * nsb + sb0g) * kDBytes +
+                  (v % (kDBytes / 16)) * 16;
+      small_kind = 2;
     }
   }
 
@@ -377,11 +408,11 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
       if (small_kind == 1)
         copy16_lane(small_src + (size_t)g * KC * 128, ls);
       else if (small_kind == 3)
-        copy16_lane(small_src + (size_t)g * 512, ls);
+        copy16_lane(small_src + (size_t)g * 256, ls);
       else if (small_kind == 2 && ends_sb)
-        copy16_lane(small_src + (size_t)((g * KC) / 8) * 128, ls);
+        copy16_lane(small_src + (size_t)((g * KC) / 8) * kDBytes, ls);
       else if (small_kind == 4 && ends_sb)
-        copy16_lane(small_src + (size_t)((g * KC) / 8) * 1024, ls);
+        copy16_lane(small_src + (size_t)((g * KC) / 8) * 512, ls);
     }
   };
   auto issue_stage = [&](int g, int buf) __attribute__((always_inline)) {  // all at once (prologue)
@@ -393,27 +424,22 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
   // q4_K min term of a super-block, sum over its chunks c of
-  // -dmin*min(row, c)*2^e * s(token, c), on two f16 MFMAs (32x32x8) at its end that
-  // add into acc: the hi and the lo part of the exact pair, each times the f16
-  // scaled sums, products exact in f32.  Lane half hh supplies chunks
-  // 4*hh..4*hh+3: the pairs from the super-block's mins region, the scaled sums
-  // (bs) collected from the chunks' scale pairs as they pass, half hh of the
-  // lanes during the super-block's stage hh.
+  // min(row, c) * s(token, c), on one f16 MFMA (32x32x8) at its end (products
+  // of a 6-bit integer and an f16 value: exact in f32), then times -dmin into
+  // acc.  Lane half hh supplies chunks 4*hh..4*hh+3: the mins from the
+  // super-block's mins region, the scaled sums (bs) collected from the chunks'
+  // scale pairs as they pass, half hh of the lanes during the super-block's
+  // stage hh.
   v2i bs = {};
   const bool lane_hi = lane >= 32;
-  // q4_K scale products: the stage's scale pairs (A operand), and the byte
-  // selectors that put dh twice into B on the lanes of one half and zeros on the
-  // other's
-  v2i a_sc = {};
-  const uint32_t sel0 = lane_hi ? 0x0C0C0C0Cu : 0x01000100u, sel1 = lane_hi ? 0x01000100u : 0x0C0C0C0Cu;
 
   if (nstages > 0) issue_stage(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   // Super-blocks in turn, the stages of one unrolled, so where a super-block
-  // starts and ends (first chunk: inner = J*dh; last: apply d, or q4_K's min
-  // term) is known at compile time.
+  // starts and ends (first chunk: inner = dot * scale; last: apply d, and
+  // q4_K's min term) is known at compile time.
   for (int sbi = 0; sbi < niter / kStagesPerSb; ++sbi) {
 #pragma unroll
     for (int h = 0; h < kStagesPerSb; ++h) {
@@ -424,35 +450,37 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         // Software pipeline over the KC chunks: step cc issues the MFMA(s) of
         // chunk cc+1 (operands read one step earlier), then the LDS reads of chunk
         // cc+2 and of chunk cc+1's activation scale, then the scale epilogue of
-        // chunk cc on the vector ALU while the matrix core works.  Every LDS value is consumed one step after its read, so a wait
-        // for it never waits for the reads just issued.
+        // chunk cc on the vector ALU while the matrix core works.  Every LDS
+        // value is consumed one step after its read, so a wait for it never
+        // waits for the reads just issued.
         uint32_t dhr = st.s[wt][0][lane & 31], dhr_even = 0;
-        v2i amin_hi = {}, amin_lo = {};
+        v2i a_sc = {}, amin = {};
         if constexpr (TYPE == QMM_Q4_K) {
-          if (h == kStagesPerSb - 1) {
-            amin_hi = *(const v2i*)(&st.mn[wr][0][lane >> 5][lane & 31][0]);
-            amin_lo = *(const v2i*)(&st.mn[wr][1][lane >> 5][lane & 31][0]);
-          }
-          a_sc = *(const v2i*)(&st.sc[wr][lane >> 5][lane & 31][0]);
+          if (h == kStagesPerSb - 1) amin = *(const v2i*)(&st.mn[wr][lane >> 5][lane & 31][0]);
+          a_sc = *(const v2i*)(&st.sc[wr][lane & 31][0]);
         }
         typename W::A a0 = W::load(st.a[wr][0], lane);
         v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
         typename W::A a1 = W::load(st.a[wr][1], lane);
         v4i bq1 = *(const v4i*)(st.b[wt][1] + lane * 16);
-        typename W::D dj = W::mma(a0, bq0);
+        typename W::D dj = W::mma(a0, bq0, nchunk);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int cc = 0; cc < KC; ++cc) {
-          // q4_K: the scale products of chunk cc, first, so they are ready for
-          // this step's epilogue
+          // the per-element scale of chunk cc.  q4_K: the scale products, first,
+          // so they are ready for this step's epilogue; q6_K: dh, converted to
+          // f32 once per chunk and kept in a register, so the 16 scale FMAs are
+          // plain v_fma_f32, which issue at twice the rate of the mixed-precision
+          // v_fma_mix_f32 the compiler would otherwise fold the f16 operand into
           v16f sd;
+          float dh = 0.0f;
           if constexpr (TYPE == QMM_Q4_K) {
-            sd = scale_outer(a_sc, dhr, cc < 2 ? sel0 : sel1, cc);
+            sd = scale_outer(a_sc, dhr, cc);
             pin(sd);
           }
           typename W::D dj_next;
           if (cc + 1 < KC) {
-            dj_next = W::mma(a1, bq1);
+            dj_next = W::mma(a1, bq1, nchunk);
             W::keep(dj_next);
           }
           // stage (g+1)&1 was last read in iteration g-1, which every wave finished
@@ -478,27 +506,23 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
             } else {
               dhr_even = dhr;
             }
-          }
-          if constexpr (TYPE == QMM_Q4_K) {  // straight into acc: d is in the scale product
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] = fmaf((float)W::dot(dj, {}, i), sd[i], acc[i]);
-            pin(acc);
           } else {
-            // dh converted to f32 once per chunk and kept in a register, so the 16
-            // scale FMAs are plain v_fma_f32, which issue at twice the rate of
-            // the mixed-precision v_fma_mix_f32 the compiler would otherwise fold
-            // the f16 operand into
-            float dh = f16_bits_to_float(dhr & 0xFFFF);
+            dh = f16_bits_to_float(dhr & 0xFFFF);
             pin(dh);
-            if (cc == 0 && starts_sb) {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) inner[i] = (float)W::dot(dj, {}, i) * dh;
-            } else {
-#pragma unroll
-              for (int i = 0; i < 16; ++i) inner[i] = fmaf((float)W::dot(dj, {}, i), dh, inner[i]);
-            }
-            pin(inner);
           }
+          // element i's scale: q4_K the outer product's, q6_K the token's dh
+          auto scale = [&](int i) __attribute__((always_inline)) {
+            if constexpr (TYPE == QMM_Q4_K) return sd[i];
+            else return dh;
+          };
+          if (cc == 0 && starts_sb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) inner[i] = W::val(dj, i) * scale(i);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) inner[i] = fmaf(W::val(dj, i), scale(i), inner[i]);
+          }
+          pin(inner);
           if (cc + 1 < KC) {
             dj = dj_next;
             a1 = a2;
@@ -513,21 +537,30 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
           __builtin_amdgcn_sched_group_barrier(0x002, 72, 0);        // VALU
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (h == kStagesPerSb - 1) {  // end of a super-block
-          if constexpr (TYPE == QMM_Q4_K) {  // its min term, added into acc
+        if (h == kStagesPerSb - 1) {  // end of a super-block: apply its d (q4_K: d*2^25)
+          v16f mt;
+          if constexpr (TYPE == QMM_Q4_K) {  // and q4_K's min term, times -dmin
             typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-            acc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, amin_hi),
-                                                       __builtin_bit_cast(v4h, bs), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, amin_lo),
-                                                       __builtin_bit_cast(v4h, bs), acc, 0, 0, 0);
-          } else {  // q6_K: apply its d
+            const v16f zero = {};
+            mt = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, amin), __builtin_bit_cast(v4h, bs),
+                                                      zero, 0, 0, 0);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 d4 = *(const float4*)(&st.d[wr][0][8 * q + 4 * (lane >> 5)]);
+            acc[4 * q + 0] = fmaf(inner[4 * q + 0], d4.x, acc[4 * q + 0]);
+            acc[4 * q + 1] = fmaf(inner[4 * q + 1], d4.y, acc[4 * q + 1]);
+            acc[4 * q + 2] = fmaf(inner[4 * q + 2], d4.z, acc[4 * q + 2]);
+            acc[4 * q + 3] = fmaf(inner[4 * q + 3], d4.w, acc[4 * q + 3]);
+          }
+          if constexpr (TYPE == QMM_Q4_K) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float4 d4 = *(const float4*)(&st.d[wr][8 * q + 4 * (lane >> 5)]);
-              acc[4 * q + 0] = fmaf(inner[4 * q + 0], d4.x, acc[4 * q + 0]);
-              acc[4 * q + 1] = fmaf(inner[4 * q + 1], d4.y, acc[4 * q + 1]);
-              acc[4 * q + 2] = fmaf(inner[4 * q + 2], d4.z, acc[4 * q + 2]);
-              acc[4 * q + 3] = fmaf(inner[4 * q + 3], d4.w, acc[4 * q + 3]);
+              const float4 m4 = *(const float4*)(&st.d[wr][1][8 * q + 4 * (lane >> 5)]);
+              acc[4 * q + 0] = fmaf(mt[4 * q + 0], m4.x, acc[4 * q + 0]);
+              acc[4 * q + 1] = fmaf(mt[4 * q + 1], m4.y, acc[4 * q + 1]);
+              acc[4 * q + 2] = fmaf(mt[4 * q + 2], m4.z, acc[4 * q + 2]);
+              acc[4 * q + 3] = fmaf(mt[4 * q + 3], m4.w, acc[4 * q + 3]);
             }
           }
         }
@@ -536,16 +569,6 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads for g+1 landed
         __syncthreads();                                   // everyone's landed; stage g is free
       }
-    }
-  }
-  if constexpr (TYPE == QMM_Q4_K) {  // undo the rows' 2^e
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 u = *(const float4*)(wd + (size_t)(rb0 + wr) * 32 + 8 * q + 4 * (lane >> 5));
-      acc[4 * q + 0] *= u.x;
-      acc[4 * q + 1] *= u.y;
-      acc[4 * q + 2] *= u.z;
-      acc[4 * q + 3] *= u.w;
     }
   }
   if (KS > 1) {  // add k-group 1's partial sums to k-group 0's, in that order

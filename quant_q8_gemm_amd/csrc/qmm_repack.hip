@@ -7,11 +7,10 @@
 // two int8 planes (hi = w >> 6, lo = w & 63), so one K=32 int8 MFMA per plane
 // yields the block dot J = 64*J_hi + J_lo, and only the f16 d of the super-block
 // stays a float.  q4_K's 4-bit codes become int8 bytes in MFMA fragment order;
-// its block scale d*sc and block min dmin*min (f16 times a 6-bit integer: 17
-// significant bits, exact in f32) are stored, scaled by a power of two 2^e per
-// row, as exact pairs of f16 values hi + lo -- the operands from which the GEMM's
-// f16 matrix-core products form d*sc*dh and the min term; the GEMM multiplies
-// its results by 2^-e once, at the store.
+// its 6-bit scales and mins become f16 integers (exact), the operands from which
+// the GEMM's f16 matrix-core products form scale*dh and the min term; its d and
+// dmin stay per super-block f32 values, applied once per super-block, so every
+// stored value is exact whatever the spread of d and dmin along a row.
 #include "qmm_internal.h"
 #include "qmm_common.h"
 
@@ -30,33 +29,30 @@ namespace qmm {
 //             (row j, k) in [0, 15] at byte
 //             (j/32*nchunk + k/32)*1024 + ((k%32)/16)*512 + (j%32)*16 + k%16
 //   wd  q6_K: f32 [R][nsb][32 rows]  d of (row, super-block)
-//       q4_K: f32 [R][32 rows]       2^-e of the row: e = 13 - floor(log2 M), M the
-//             largest |d*sc| and |dmin*min| of the row (e = 0 if M = 0), so that
-//             every scaled value is below 2^14 in magnitude
-//   wmn f16   [R][nsb][2][2][32 rows][4]  q4_K only: -dmin*min*2^e of (row j,
-//             chunk c) as hi + lo, hi = f16(v), lo = f16(v - hi), part p = 0 (hi)
-//             or 1 (lo) at element (((j/32*nsb + c/8)*2 + p)*2 + (c%8)/4)*128
-//             + (j%32)*4 + c%4: per part two halves of [32 rows][4 chunks], so
-//             a lane half's 8-byte reads are consecutive
-//   wsc f16   [R][nsb][2][2][32 rows][2][2]  q4_K only: d*sc*2^e of (row j,
-//             chunk c) as the pair (hi, lo), at element
-//             ((((j/32*nsb + c/8)*2 + (c%8)/4)*2 + (c%4)/2)*32 + j%32)*4
-//             + (c%2)*2 + p: per stage of 4 chunks, lane half (c%4)/2 of a row
-//             reads its two chunks' pairs as one 8-byte word
+//       q4_K: f32 [R][nsb][2][32 rows]  of (row j, super-block b): part 0 is
+//             d*2^25, part 1 is -dmin, at element ((j/32*nsb + b)*2 + part)*32
+//             + j%32 (both exact in f32; a zero is stored as +0)
+//   wmn f16   [R][nsb][2][32 rows][4]  q4_K only: the 6-bit min of (row j,
+//             chunk c) as an f16 integer at element ((j/32*nsb + c/8)*2
+//             + (c%8)/4)*128 + (j%32)*4 + c%4 (lane half h of the min-term
+//             MFMA reads chunks 4h..4h+3 of its row as one 8-byte word)
+//   wsc f16   [R][nsb][2][32 rows][4]  q4_K only: the 6-bit scale of (row j,
+//             chunk c) as an f16 integer, same element index as wmn (one 8-byte
+//             word per row and 4-chunk stage)
 // Rows od..od_pad-1 are zero in every plane.
 // ---------------------------------------------------------------------------
 size_t wq_bytes(int type, int64_t od_pad, int64_t id) {
   return type == QMM_Q6_K ? (size_t)od_pad * (size_t)id * 2 : (size_t)od_pad * (size_t)id;
 }
 size_t wd_bytes(int type, int64_t od_pad, int64_t id) {
-  return type == QMM_Q4_K ? (size_t)od_pad * 4 : (size_t)od_pad * (size_t)(id / 256) * 4;
+  return (size_t)od_pad * (size_t)(id / 256) * 4 * (type == QMM_Q4_K ? 2 : 1);
 }
 size_t wmn_bytes(int type, int64_t od_pad, int64_t id) {
-  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) * 4 : 0;
+  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) * 2 : 0;
 }
 size_t wdm_bytes(int, int64_t, int64_t) { return 0; }
 size_t wsc_bytes(int type, int64_t od_pad, int64_t id) {
-  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) * 4 : 0;
+  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) * 2 : 0;
 }
 
 // q4_K: the 6-bit scale and min of sub-block cl of a 144-byte block (ggml's
@@ -70,36 +66,6 @@ __device__ __forceinline__ void q4k_scale_min(const uint8_t* B, int cl, int& sc,
     sc = (P[cl + 4] & 15) | ((P[cl - 4] >> 6) << 4);
     mn = (P[cl + 4] >> 4) | ((P[cl] >> 6) << 4);
   }
-}
-
-// q4_K: one thread per row in [0, od_pad): wd[row] = 2^-e (1 for padding rows).
-__global__ void __launch_bounds__(256)
-q4k_row_scale_kernel(const uint8_t* __restrict__ raw, int od, int nsb, int od_pad, float* __restrict__ wd) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= od_pad) return;
-  float m = 0.0f;
-  if (j < od) {
-    for (int b = 0; b < nsb; ++b) {
-      const uint8_t* B = raw + ((int64_t)j * nsb + b) * 144;
-      const float d = f16_bits_to_float(B[0] | (B[1] << 8)), dmin = f16_bits_to_float(B[2] | (B[3] << 8));
-      for (int cl = 0; cl < 8; ++cl) {
-        int sc, mn;
-        q4k_scale_min(B, cl, sc, mn);
-        m = fmaxf(m, fmaxf(fabsf(d * (float)sc), fabsf(dmin * (float)mn)));  // exact products
-      }
-    }
-  }
-  const int e = m > 0.0f ? 13 - ilogbf(m) : 0;
-  wd[j] = ldexpf(1.0f, -e);
-}
-
-// v (exact in f32, at most 17 significant bits) as hi + lo, two f16 values; a
-// zero part is stored as +0 (the + 0 maps -0 to +0), whatever the signs that
-// formed it
-__device__ __forceinline__ void split_f16(float v, uint16_t& hi, uint16_t& lo) {
-  const _Float16 h = (_Float16)(v + 0.0f);
-  hi = __builtin_bit_cast(uint16_t, h);
-  lo = __builtin_bit_cast(uint16_t, (_Float16)((v - (float)h) + 0.0f));
 }
 
 // One thread per (row j in [0, od_pad), chunk c, k-half h): 16 weights.
@@ -151,29 +117,28 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
 #pragma unroll
       for (int i = 0; i < 16; ++i) lo[i >> 2] |= (uint32_t)((qs[i] >> shift) & 15) << (8 * (i & 3));
       if (h == 0) {
-        // 2^e from the row's 2^-e (a power of two: exact); d*sc and dmin*min are
-        // exact in f32, and so are their products with 2^e
-        const float pe = 1.0f / wd[j];
-        const float d = f16_bits_to_float(B[0] | (B[1] << 8)), dmin = f16_bits_to_float(B[2] | (B[3] << 8));
-        uint16_t hi, lo;
-        split_f16(d * (float)sc * pe, hi, lo);
-        const int64_t si = ((((int64_t)rb * nsb + b) * 2 + (cl >> 2)) * 2 + ((cl & 3) >> 1)) * 32 + jr;
-        wsc[si * 4 + (cl & 1) * 2] = hi;
-        wsc[si * 4 + (cl & 1) * 2 + 1] = lo;
-        split_f16(-(dmin * (float)mn) * pe, hi, lo);
-        const int64_t mi = (((int64_t)rb * nsb + b) * 2) * 2 + (cl >> 2);
-        wmn[mi * 128 + jr * 4 + (cl & 3)] = hi;
-        wmn[(mi + 2) * 128 + jr * 4 + (cl & 3)] = lo;
+        // the scale and min as f16 integers (6 bits: exact); d and dmin once per
+        // super-block, d times 2^25 (the GEMM's scale products and block dots
+        // carry 2^-25 between them; a power of two, so the product stays exact)
+        const int64_t si = (((int64_t)rb * nsb + b) * 2 + (cl >> 2)) * 128 + jr * 4 + (cl & 3);
+        wsc[si] = __builtin_bit_cast(uint16_t, (_Float16)sc);
+        wmn[si] = __builtin_bit_cast(uint16_t, (_Float16)mn);
+        if (cl == 0) {
+          const float d = f16_bits_to_float(B[0] | (B[1] << 8)), dmin = f16_bits_to_float(B[2] | (B[3] << 8));
+          wd[(((int64_t)rb * nsb + b) * 2 + 0) * 32 + jr] = ldexpf(d, 25) + 0.0f;
+          wd[(((int64_t)rb * nsb + b) * 2 + 1) * 32 + jr] = -dmin + 0.0f;
+        }
       }
     }
   } else if (h == 0) {
     if (type == QMM_Q4_K) {
-      const int64_t si = ((((int64_t)rb * nsb + b) * 2 + (cl >> 2)) * 2 + ((cl & 3) >> 1)) * 32 + jr;
-      wsc[si * 4 + (cl & 1) * 2] = 0;
-      wsc[si * 4 + (cl & 1) * 2 + 1] = 0;
-      const int64_t mi = (((int64_t)rb * nsb + b) * 2) * 2 + (cl >> 2);
-      wmn[mi * 128 + jr * 4 + (cl & 3)] = 0;
-      wmn[(mi + 2) * 128 + jr * 4 + (cl & 3)] = 0;
+      const int64_t si = (((int64_t)rb * nsb + b) * 2 + (cl >> 2)) * 128 + jr * 4 + (cl & 3);
+      wsc[si] = 0;
+      wmn[si] = 0;
+      if (cl == 0) {
+        wd[(((int64_t)rb * nsb + b) * 2 + 0) * 32 + jr] = 0.0f;
+        wd[(((int64_t)rb * nsb + b) * 2 + 1) * 32 + jr] = 0.0f;
+      }
     } else if (cl == 0) {
       wd[((int64_t)rb * nsb + b) * 32 + jr] = 0.0f;
     }
@@ -189,11 +154,6 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
 }
 
 hipError_t launch_repack(const uint8_t* raw, const Planes& p, hipStream_t s) {
-  if (p.type == QMM_Q4_K) {  // the rows' 2^-e first: the repack reads it
-    q4k_row_scale_kernel<<<dim3((unsigned)((p.od_pad + 255) / 256)), dim3(256), 0, s>>>(
-        raw, (int)p.od, (int)p.nsb, (int)p.od_pad, p.wd);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  }
   const int64_t total = p.od_pad * p.nchunk * 2;
   const int64_t blocks = (total + 255) / 256;
   repack_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(

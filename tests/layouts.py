@@ -23,11 +23,11 @@ def read_qact(buf: np.ndarray, n_tok: int, id_: int):
 
 
 def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: int, mn_offset: int,
-                dm_offset: int, sc_offset: int):
-    """exported planes -> q6_K: (w [od_pad][id] int32 folded weights 64*hi + lo,
-    d [od_pad][nsb] f32, None, None); q4_K: (codes [od_pad][id] int32, the rows'
-    2^-e [od_pad] f32, the scale pairs and the min pairs, each a (hi, lo) tuple
-    of binary16 bit patterns [od_pad][nchunk] (values times 2^e))."""
+                dm_offset: int, sc_offset: int) -> dict:
+    """exported planes -> dict.  q6_K: w [od_pad][id] int32 folded weights
+    64*hi + lo, d [od_pad][nsb] f32.  q4_K: codes [od_pad][id] int32, d25
+    [od_pad][nsb] f32 (d times 2^25), ndmin [od_pad][nsb] f32 (-dmin), sc and mn
+    [od_pad][nchunk] binary16 bit patterns."""
     nchunk, nsb = id_ // 32, id_ // 256
     R = od_pad // 32
     buf = np.asarray(buf, np.uint8)
@@ -38,16 +38,19 @@ def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: i
         assert lo.min() >= 0 and lo.max() <= 63
         w = hi * 64 + lo
         d = buf[wd_offset: wd_offset + od_pad * nsb * 4].view("<f4").reshape(R, nsb, 32)
-        return w, d.transpose(0, 2, 1).reshape(od_pad, nsb), None, None
+        return {"w": w, "d": d.transpose(0, 2, 1).reshape(od_pad, nsb)}
     # [R][nchunk][k-half h][row][16]: code k = 16h + byte
     pk = buf[: od_pad * id_].view(np.int8).reshape(R, nchunk, 2, 32, 16)
     codes = pk.transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
     assert codes.min() >= 0 and codes.max() <= 15
-    unscale = buf[wd_offset: wd_offset + od_pad * 4].view("<f4").copy()
-    # scale pairs: [R][nsb][chunk/4][(chunk%4)/2][row][chunk%2][hi, lo]
-    sp = buf[sc_offset: sc_offset + od_pad * nchunk * 4].view("<u2").reshape(R, nsb, 2, 2, 32, 2, 2)
-    sp = sp.transpose(0, 4, 1, 2, 3, 5, 6).reshape(od_pad, nchunk, 2)
-    # min pairs: [R][nsb][hi, lo][chunk/4][row][chunk%4]
-    mp = buf[mn_offset: mn_offset + od_pad * nchunk * 4].view("<u2").reshape(R, nsb, 2, 2, 32, 4)
-    mp = mp.transpose(0, 4, 1, 3, 5, 2).reshape(od_pad, nchunk, 2)
-    return codes, unscale, (sp[..., 0].copy(), sp[..., 1].copy()), (mp[..., 0].copy(), mp[..., 1].copy())
+    # (d*2^25, -dmin): [R][nsb][part][row]
+    dd = buf[wd_offset: wd_offset + od_pad * nsb * 8].view("<f4").reshape(R, nsb, 2, 32)
+    dd = dd.transpose(0, 3, 1, 2).reshape(od_pad, nsb, 2)
+    # scales and mins: [R][nsb][chunk%8 / 4][row][chunk%4]
+
+    def chunks(off):
+        v = buf[off: off + od_pad * nchunk * 2].view("<u2").reshape(R, nsb, 2, 32, 4)
+        return v.transpose(0, 3, 1, 2, 4).reshape(od_pad, nchunk).copy()
+
+    return {"codes": codes, "d25": dd[..., 0].copy(), "ndmin": dd[..., 1].copy(),
+            "sc": chunks(sc_offset), "mn": chunks(mn_offset)}

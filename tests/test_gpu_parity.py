@@ -134,28 +134,36 @@ def _full_range_q6k(rng, od, id_):
 
 
 def expected_planes(type_, raw, od, id_):
+    """The planes include/qmm.h documents, from the oracle's decode: q6_K the
+    scale-folded weights and d; q4_K the codes, d*2^25 and -dmin (exact in
+    binary32: an f16 value times a power of two), and the 6-bit scales and mins
+    as binary16 integers (exact)."""
     if type_ == synth.Q6_K:
         w6, sc, d = oracle.decode_q6k(raw, od, id_)
         w = w6.astype(np.int32) * np.repeat(sc.astype(np.int32), 16, axis=1)
-        return w, d, None, None
-    # q4_K: the codes; per row 2^-e with e = 13 - floor(log2 M), M the row's
-    # largest d*scale and dmin*min (exact in binary32); d*scale*2^e and
-    # -dmin*min*2^e per (row, chunk) as hi = f16(v), lo = f16(v - hi)
+        return {"w": w, "d": d}
     w4, sc, mn, d, dm = oracle.decode_q4k(raw, od, id_)
-    dsc = np.repeat(d.astype(np.float64), 8, axis=1) * sc
-    dmn = np.repeat(dm.astype(np.float64), 8, axis=1) * mn
-    M = np.maximum(np.abs(dsc).max(axis=1), np.abs(dmn).max(axis=1))
-    e = np.where(M > 0, 13 - (np.frexp(M)[1] - 1), 0)
-    pe = np.ldexp(1.0, e)[:, None]
+    d25 = np.ldexp(d.astype(np.float64), 25)
+    assert np.all(d25.astype(np.float32) == d25)
+    return {"codes": w4.astype(np.int32), "d25": d25.astype(np.float32) + np.float32(0.0),
+            "ndmin": (-dm.astype(np.float32)) + np.float32(0.0),
+            "sc": sc.astype(np.float16).view(np.uint16), "mn": mn.astype(np.float16).view(np.uint16)}
 
-    def pair(v):  # zero parts as +0 (the + 0.0)
-        assert np.all(v.astype(np.float32) == v), "the scaled value is not exact in binary32"
-        hi = (v + 0.0).astype(np.float16)
-        lo = ((v - hi.astype(np.float64)) + 0.0).astype(np.float16)
-        assert np.all(np.abs(v) < 2.0 ** 14)
-        return hi.view(np.uint16), lo.view(np.uint16)
 
-    return (w4.astype(np.int32), np.ldexp(1.0, -e).astype(np.float32), pair(dsc * pe), pair(-dmn * pe))
+def check_planes(w, type_, raw, od, id_):
+    got = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.mn_offset,
+                              w.dm_offset, w.sc_offset)
+    exp = expected_planes(type_, raw, od, id_)
+    assert set(got) == set(exp)
+    for k, e in exp.items():
+        g = got[k]
+        if e.dtype == np.float32:  # compare bit patterns: -0 and +0 differ
+            assert np.array_equal(g[:od].view(np.uint32), e.view(np.uint32)), f"plane {k} differs"
+        else:
+            assert np.array_equal(g[:od], e), f"plane {k} differs"
+        assert not g[od:].view(np.uint8).any(), f"plane {k}: padding rows not zero"
+    if type_ == synth.Q4_K:
+        assert w.dm_offset == w.plane_bytes
 
 
 @pytest.mark.parametrize("type_,od,id_,full", [(synth.Q6_K, 5, 512, False), (synth.Q6_K, 130, 768, True),
@@ -166,58 +174,91 @@ def test_planes_byte_exact(type_, od, id_, full):
     raw = _full_range_q6k(rng, od, id_) if full else synth.weights(rng, type_, od, id_)
     w = qmm.register_weights(type_, od, id_, raw)
     assert w.od_pad % 128 == 0 and w.od_pad >= od
-    gw, gd, gsc, gmn = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.mn_offset,
-                                           w.dm_offset, w.sc_offset)
-    ew, ed, esc, emn = expected_planes(type_, raw, od, id_)
-    assert np.array_equal(gw[:od], ew) and not gw[od:].any()
-    assert np.array_equal(gd[:od].view(np.uint32), ed.astype(np.float32).view(np.uint32))
-    if type_ == synth.Q6_K:
-        assert not gd[od:].any()
-    else:
-        assert np.all(gd[od:] == 1.0)  # padding rows: 2^0
-        assert w.dm_offset == w.plane_bytes
-        for got, exp in ((gsc, esc), (gmn, emn)):
-            for g, x in zip(got, exp):
-                assert np.array_equal(g[:od], x) and not g[od:].any()
+    check_planes(w, type_, raw, od, id_)
     w.release()
+
+
+def _set_f16(raw, lo, bits):
+    """Overwrite the f16 field at byte offset lo of every block with bits."""
+    nb = raw.shape[0]
+    raw[:, lo:lo + 2] = np.asarray(bits, np.uint16).astype("<u2").view(np.uint8).reshape(nb, 2)
 
 
 @pytest.mark.parametrize("type_", [synth.Q4_K, synth.Q6_K], ids=["q4_K", "q6_K"])
 def test_extreme_block_scales(type_):
     """Super-block scales of either sign, huge (60000) and subnormal (2^-24):
-    the planes stay byte-exact (q4_K's row exponent takes magnitudes) and the
-    MMQ stays within the tolerance.  Blocks are drawn as usual, then their f16
-    d (and q4_K dmin) bits are rewritten."""
+    the planes stay byte-exact and the MMQ stays within the tolerance.  Blocks
+    are drawn as usual, then their f16 d (and q4_K dmin) bits are rewritten."""
     od, id_, T = 90, 1024, 70
     say(f"extreme block scales {synth.TYPE_NAMES[type_]}")
     rng = np.random.default_rng(9)
     bb = 144 if type_ == synth.Q4_K else 210
     raw = synth.weights(rng, type_, od, id_).reshape(-1, bb).copy()
     nb = raw.shape[0]
-    fields = [(0, 2), (2, 4)] if type_ == synth.Q4_K else [(208, 210)]
-    for lo, hi in fields:
-        bits = raw[:, lo:hi].copy().view("<u2").reshape(-1)
+    fields = [0, 2] if type_ == synth.Q4_K else [208]
+    for lo in fields:
+        bits = raw[:, lo:lo + 2].copy().view("<u2").reshape(-1)
         pick = rng.random(nb)
         bits = np.where(pick < 0.3, bits | 0x8000, bits)                 # negative
         bits = np.where((pick >= 0.3) & (pick < 0.35), 0x7B53, bits)     # 60000
         bits = np.where((pick >= 0.35) & (pick < 0.40), 0x0001, bits)    # 2^-24
-        raw[:, lo:hi] = bits.astype("<u2").view(np.uint8).reshape(nb, 2)
+        _set_f16(raw, lo, bits)
     raw = raw.reshape(-1)
     w = qmm.register_weights(type_, od, id_, raw)
-    got = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.mn_offset,
-                              w.dm_offset, w.sc_offset)
-    exp = expected_planes(type_, raw, od, id_)
-    assert np.array_equal(got[0][:od], exp[0])
-    assert np.array_equal(got[1][:od].view(np.uint32), np.asarray(exp[1], np.float32).view(np.uint32))
-    if type_ == synth.Q4_K:
-        for g, x in zip(got[2] + got[3], exp[2] + exp[3]):
-            assert np.array_equal(g[:od], x)
+    check_planes(w, type_, raw, od, id_)
     x = synth.activations(rng, T, id_, False)
     qact = gpu_quantize(x)
     q, dh, s = check_prepass(x, qact)
     out = run_mmq(w, qact, T)
     ref, A = oracle.mmq(type_, raw, od, id_, q, dh, s)
     check_close(out, ref, A, "extreme block scales")
+    w.release()
+
+
+# Shapes for the wide-scale-range rows: both tile geometries, a ragged second
+# wave whose tail tiles are split along K, and an under-filled launch where
+# every tile is split.
+WIDE = [("few-tile 96x2048 T=70", 96, 2048, 70), ("many-tile 1030x1024 T=4000", 1030, 1024, 4000),
+        ("ragged tail 4160x1024 T=512", 4160, 1024, 512), ("all split 512x3072 T=300", 512, 3072, 300)]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=[c[0] for c in WIDE])
+def test_q4k_wide_scale_range_rows(case):
+    """q4_K rows whose super-block scales span the whole f16 range: super-block
+    0 of every row has d = 60000 (and dmin = 60000 on a third of the rows), the
+    others d = k * 2^-24 for k in [1, 1023] (subnormal) and dmin either tiny
+    (k * 2^-24), zero or 60000.  Half of the tokens are zero over super-block 0,
+    so their outputs are made of the tiny terms alone; a quarter are non-zero in
+    one small super-block only.  Every element must land within 1e-4 of the sum
+    of its terms' magnitudes -- which a scale stored relative to the row's
+    largest value cannot do."""
+    name, od, id_, T = case
+    say(f"q4_K wide scale range {name}")
+    rng = np.random.default_rng(31)
+    nsb = id_ // 256
+    raw = synth.q4k_weights(rng, od, id_).reshape(od, nsb, 144).copy()
+    d = rng.integers(1, 1024, size=(od, nsb)).astype(np.uint16)           # k * 2^-24
+    kind = rng.integers(0, 3, size=(od, nsb))
+    dmin = np.where(kind == 0, rng.integers(1, 1024, size=(od, nsb)), np.where(kind == 1, 0, 0x7B53))
+    d[:, 0] = 0x7B53
+    dmin[:, 0] = np.where(np.arange(od) % 3 == 0, 0x7B53, dmin[:, 0])
+    raw[:, :, 0:2] = d.astype("<u2").view(np.uint8).reshape(od, nsb, 2)
+    raw[:, :, 2:4] = dmin.astype(np.uint16).astype("<u2").view(np.uint8).reshape(od, nsb, 2)
+    raw = raw.reshape(-1)
+    x = synth.activations(rng, T, id_)
+    x[0::2, :256] = 0.0                                   # zero over the d = 60000 block
+    one = 1 + (np.arange(T) % max(1, nsb - 1))            # one small super-block only
+    for t in range(1, T, 4):
+        keep = x[t, 256 * one[t]: 256 * one[t] + 256].copy()
+        x[t] = 0.0
+        x[t, 256 * one[t]: 256 * one[t] + 256] = keep
+    w = qmm.register_weights(synth.Q4_K, od, id_, raw)
+    check_planes(w, synth.Q4_K, raw, od, id_)
+    qact = gpu_quantize(x)
+    q, dh, s = check_prepass(x, qact)
+    got = run_mmq(w, qact, T)
+    ref, A = oracle.mmq(synth.Q4_K, raw, od, id_, q, dh, s)
+    check_close(got, ref, A, f"wide scale range {name}")
     w.release()
 
 
