@@ -209,6 +209,26 @@ int qmm_quantize_activations(const float *x, int64_t n_tok, int64_t id, void *qa
 int qmm_mmq(const qmm_weights *w, const void *qact, size_t qact_bytes, int64_t n_tok,
             float *out, void *stream);
 
+/*
+ * qmm_mmq_noalloc -- qmm_mmq for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, validation, kernels and results (bit for bit)
+ * as qmm_mmq; it calls no hipMalloc, hipFree or other allocating routine.  The
+ * tail partials (see qmm_mmq) live in a static device array of 16 MiB that
+ * every GPU the library runs on holds until the process ends; its address is
+ * looked up (hipGetSymbolAddress) on the first call on each device.
+ *   - Every call on one GPU shares that GPU's array and leaves the last call's
+ *     partials in it: calls that may overlap on one GPU (different streams
+ *     without ordering between them) race.  Calls on one stream are ordered.
+ *   - Nothing in the array needs clearing: each partial is written whole
+ *     before it is read.
+ *   - A launch that needs more than 16 MiB of partials (only on GPUs with more
+ *     than 256 compute units) fails with QMM_EINVAL before any launch.
+ * Errors: as qmm_mmq, without QMM_ENOMEM.
+ */
+int qmm_mmq_noalloc(const qmm_weights *w, const void *qact, size_t qact_bytes, int64_t n_tok,
+                    float *out, void *stream);
+
 /* qmm_last_error -- message for the calling thread's last failed call ("" if
  * none).  Valid until the thread's next call into the library. */
 const char *qmm_last_error(void);

@@ -45,7 +45,7 @@ BLOCK_BYTES = {Q4_K: 144, Q6_K: 210}
 # The full list of entry points include/qmm.h declares.
 EXPORTS = ("qmm_register_weights", "qmm_weights_info", "qmm_weights_export", "qmm_release_weights",
            "qmm_set_memory_cap", "qmm_qact_bytes", "qmm_quantize_activations", "qmm_mmq",
-           "qmm_last_error")
+           "qmm_mmq_noalloc", "qmm_last_error")
 
 
 class Info(ctypes.Structure):
@@ -75,6 +75,8 @@ _lib.qmm_quantize_activations.argtypes = [_P, _I64, _I64, _P, _SZ, _P]
 _lib.qmm_quantize_activations.restype = ctypes.c_int
 _lib.qmm_mmq.argtypes = [_P, _P, _SZ, _I64, _P, _P]
 _lib.qmm_mmq.restype = ctypes.c_int
+_lib.qmm_mmq_noalloc.argtypes = [_P, _P, _SZ, _I64, _P, _P]
+_lib.qmm_mmq_noalloc.restype = ctypes.c_int
 _lib.qmm_last_error.argtypes = []
 _lib.qmm_last_error.restype = ctypes.c_char_p
 
@@ -190,8 +192,7 @@ def quantize_activations(x, qact=None, stream=None):
     return qact
 
 
-def mmq(w: Weights, qact, n_tok: int, out=None, stream=None):
-    """out[t][j] (cuda float32 [n_tok][od]) from a handle and a qact buffer."""
+def _mmq_args(w: Weights, qact, n_tok: int, out):
     import torch
     _check_qact(qact)
     if out is None:
@@ -199,6 +200,20 @@ def mmq(w: Weights, qact, n_tok: int, out=None, stream=None):
     elif (out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous()
           or tuple(out.shape) != (n_tok, w.od)):
         raise QmmError(EINVAL, "out must be a contiguous cuda float32 [n_tok][od] tensor")
+    return out
+
+
+def mmq(w: Weights, qact, n_tok: int, out=None, stream=None):
+    """out[t][j] (cuda float32 [n_tok][od]) from a handle and a qact buffer."""
+    out = _mmq_args(w, qact, n_tok, out)
     _check(_lib.qmm_mmq(ctypes.c_void_p(w.handle), ctypes.c_void_p(qact.data_ptr()), qact.numel(),
                         int(n_tok), ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+    return out
+
+
+def mmq_noalloc(w: Weights, qact, n_tok: int, out, stream=None):
+    """mmq through the allocation-free entry point (the caller passes out)."""
+    out = _mmq_args(w, qact, n_tok, out)
+    _check(_lib.qmm_mmq_noalloc(ctypes.c_void_p(w.handle), ctypes.c_void_p(qact.data_ptr()), qact.numel(),
+                                int(n_tok), ctypes.c_void_p(out.data_ptr()), _stream(stream)))
     return out

@@ -257,13 +257,19 @@ int qmm_quantize_activations(const float* x, int64_t n_tok, int64_t id, void* qa
   return QMM_OK;
 }
 
-int qmm_mmq(const qmm_weights* w, const void* qact, size_t qact_bytes, int64_t n_tok, float* out,
-            void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch plan shared by qmm_mmq and qmm_mmq_noalloc.  Returns
+// QMM_OK with *launch false for an empty batch (nothing to launch).
+int prepare_mmq(const qmm_weights* w, const void* qact, size_t qact_bytes, int64_t n_tok, const float* out,
+                qmm::MmqPlan* plan, int* device, int* num_cus, bool* launch) {
+  *launch = false;
   if (w == nullptr) return fail(QMM_EINVAL, "NULL weights handle");
   if (int rc = check_tokens(n_tok)) return rc;
   if (n_tok == 0) {  // empty batch: an empty output, nothing launched
     if (qact_bytes != 0) return fail(QMM_ESHAPE, "qact_bytes %zu != 0 for n_tok = 0", qact_bytes);
-    ok();
     return QMM_OK;
   }
   if (qact == nullptr || out == nullptr) return fail(QMM_EINVAL, "qact or out is NULL");
@@ -273,29 +279,46 @@ int qmm_mmq(const qmm_weights* w, const void* qact, size_t qact_bytes, int64_t n
   if (qact_bytes != need)
     return fail(QMM_ESHAPE, "qact_bytes %zu does not match n_tok=%lld and the handle's id=%lld (%zu)",
                 qact_bytes, (long long)n_tok, (long long)w->p.id, need);
-  int device = -1;
-  hipError_t e = hipGetDevice(&device);
+  hipError_t e = hipGetDevice(device);
   if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
-  if (device != w->device)
-    return fail(QMM_EINVAL, "handle belongs to device %d but device %d is current", w->device, device);
-  int num_cus = 0;
-  e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (*device != w->device)
+    return fail(QMM_EINVAL, "handle belongs to device %d but device %d is current", w->device, *device);
+  e = hipDeviceGetAttribute(num_cus, hipDeviceAttributeMultiprocessorCount, *device);
   if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(multiprocessor count)");
-  const qmm::MmqPlan plan = qmm::plan_mmq(w->p, n_tok, num_cus);
+  *plan = qmm::plan_mmq(w->p, n_tok, *num_cus);
   // one-dimensional launch: work-groups x threads must stay below 2^32
-  if ((uint64_t)plan.work_groups * (uint64_t)plan.threads >= (1ull << 32))
+  if ((uint64_t)plan->work_groups * (uint64_t)plan->threads >= (1ull << 32))
     return fail(QMM_EINVAL, "n_tok=%lld x od=%lld needs %lld work-groups, more than one launch holds",
-                (long long)n_tok, (long long)w->p.od, (long long)plan.work_groups);
+                (long long)n_tok, (long long)w->p.od, (long long)plan->work_groups);
+  if (plan->scratch_bytes > qmm::mmq_scratch_max_bytes(*num_cus))
+    return fail(QMM_EINVAL, "internal: tail scratch exceeds its bound");
+  *launch = true;
+  return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmm_mmq(const qmm_weights* w, const void* qact, size_t qact_bytes, int64_t n_tok, float* out,
+            void* stream) {
+  qmm::MmqPlan plan{};
+  int device = -1, num_cus = 0;
+  bool launch = false;
+  if (int rc = prepare_mmq(w, qact, qact_bytes, n_tok, out, &plan, &device, &num_cus, &launch)) return rc;
+  if (!launch) {
+    ok();
+    return QMM_OK;
+  }
   const hipStream_t s = (hipStream_t)stream;
   void* scratch = nullptr;
   if (plan.scratch_bytes > 0) {
     const size_t max_bytes = qmm::mmq_scratch_max_bytes(num_cus);
-    if (plan.scratch_bytes > max_bytes) return fail(QMM_EINVAL, "internal: tail scratch exceeds its bound");
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     for (const Scratch& sc : g_scratch)
       if (sc.device == device && sc.stream == s) scratch = sc.ptr;
     if (scratch == nullptr) {
-      e = hipMalloc(&scratch, max_bytes);
+      hipError_t e = hipMalloc(&scratch, max_bytes);
       if (e != hipSuccess) {
         (void)hipGetLastError();  // leave no sticky error for the caller's next HIP call
         return e == hipErrorOutOfMemory
@@ -305,7 +328,33 @@ int qmm_mmq(const qmm_weights* w, const void* qact, size_t qact_bytes, int64_t n
       g_scratch.push_back({device, s, scratch});
     }
   }
-  e = qmm::launch_mmq(w->p, plan, (const uint8_t*)qact, n_tok, token_pad(n_tok), out, (float*)scratch, s);
+  hipError_t e = qmm::launch_mmq(w->p, plan, (const uint8_t*)qact, n_tok, token_pad(n_tok), out,
+                                 (float*)scratch, s);
+  if (e != hipSuccess) return fail_hip(e, "mmq launch");
+  ok();
+  return QMM_OK;
+}
+
+int qmm_mmq_noalloc(const qmm_weights* w, const void* qact, size_t qact_bytes, int64_t n_tok, float* out,
+                    void* stream) {
+  qmm::MmqPlan plan{};
+  int device = -1, num_cus = 0;
+  bool launch = false;
+  if (int rc = prepare_mmq(w, qact, qact_bytes, n_tok, out, &plan, &device, &num_cus, &launch)) return rc;
+  if (!launch) {
+    ok();
+    return QMM_OK;
+  }
+  if (plan.scratch_bytes > qmm::kStaticScratchBytes)
+    return fail(QMM_EINVAL, "this launch needs %zu bytes of tail scratch; the static scratch holds %zu",
+                plan.scratch_bytes, qmm::kStaticScratchBytes);
+  float* part = nullptr;
+  if (plan.scratch_bytes > 0) {
+    hipError_t e = qmm::static_scratch(device, &part);
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(static tail scratch)");
+  }
+  hipError_t e = qmm::launch_mmq(w->p, plan, (const uint8_t*)qact, n_tok, token_pad(n_tok), out, part,
+                                 (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "mmq launch");
   ok();
   return QMM_OK;

@@ -53,6 +53,12 @@ MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus);
 // Upper bound of MmqPlan::scratch_bytes on a device with num_cus compute units.
 size_t mmq_scratch_max_bytes(int num_cus);
 hipError_t launch_mmq(const Planes& p, const MmqPlan& plan, const uint8_t* qact, int64_t n_tok,
-                      int64_t t_pad, float* out, float* scratch, hipStream_t s);
+                      int64_t t_pad, float* out, float* part, hipStream_t s);
+// The allocation-free entry point's tail scratch: a static device array of
+// this many bytes per GPU (64 KiB per compute unit of a 256-CU MI355X).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+// Its device address on `device`, which must be the current device; looked up
+// on the first call for that device, without allocating.
+hipError_t static_scratch(int device, float** ptr);
 
 }  // namespace qmm

@@ -32,6 +32,7 @@
 #include "qmm_common.h"
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/qmm.h"
 
@@ -655,7 +656,7 @@ mmq_fixup_kernel(const float* __restrict__ part, int split, int dp_row_tiles, in
 
 template <int TYPE, int WR, int WT, int KC, int KS>
 static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8_t* qact, int64_t n_tok,
-                               int64_t t_pad, float* out, float* scratch, hipStream_t s) {
+                               int64_t t_pad, float* out, float* part, hipStream_t s) {
   static_assert(kRowPad % (32 * WR) == 0 && kTokenPad % (32 * WT) == 0,
                 "tiles must divide the row and token padding");
   const uint8_t* qs = qact + (size_t)t_pad * (size_t)p.id;
@@ -663,11 +664,11 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
   const int64_t wgs = plan.work_groups;
   mmq_kernel<TYPE, WR, WT, KC, KS><<<dim3((unsigned)wgs), dim3(64 * WR * WT * KS), 0, s>>>(
       p.wq, p.wd, (const uint8_t*)p.wmn, (const uint8_t*)p.wsc, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
-      plan.dp_row_tiles, plan.split, vec_store, out, scratch);
+      plan.dp_row_tiles, plan.split, vec_store, out, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_tail == 0) return e;
   mmq_fixup_kernel<WR, WT><<<dim3((unsigned)(plan.n_tail * WR * WT)), dim3(256), 0, s>>>(
-      scratch, plan.split, plan.dp_row_tiles, plan.tok_tiles, (int)p.od, (int)n_tok, vec_store, out);
+      part, plan.split, plan.dp_row_tiles, plan.tok_tiles, (int)p.od, (int)n_tok, vec_store, out);
   return hipGetLastError();
 }
 
@@ -757,17 +758,40 @@ MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
 size_t mmq_scratch_max_bytes(int num_cus) { return (size_t)num_cus * 64 * 1024; }
 
 hipError_t launch_mmq(const Planes& p, const MmqPlan& plan, const uint8_t* qact, int64_t n_tok,
-                      int64_t t_pad, float* out, float* scratch, hipStream_t s) {
+                      int64_t t_pad, float* out, float* part, hipStream_t s) {
   constexpr Geometry q6 = kQ6Many, q4 = kQ4Many, f = kFew;
   if (p.type == QMM_Q6_K)
     return plan.many ? launch_tiled<QMM_Q6_K, q6.wr, q6.wt, q6.kc, q6.ks>(p, plan, qact, n_tok, t_pad, out,
-                                                                         scratch, s)
+                                                                         part, s)
                      : launch_tiled<QMM_Q6_K, f.wr, f.wt, f.kc, f.ks>(p, plan, qact, n_tok, t_pad, out,
-                                                                     scratch, s);
+                                                                     part, s);
   return plan.many ? launch_tiled<QMM_Q4_K, q4.wr, q4.wt, q4.kc, q4.ks>(p, plan, qact, n_tok, t_pad, out,
-                                                                       scratch, s)
-                   : launch_tiled<QMM_Q4_K, f.wr, f.wt, f.kc, f.ks>(p, plan, qact, n_tok, t_pad, out, scratch,
+                                                                       part, s)
+                   : launch_tiled<QMM_Q4_K, f.wr, f.wt, f.kc, f.ks>(p, plan, qact, n_tok, t_pad, out, part,
                                                                    s);
+}
+
+// The tail partials of the allocation-free entry point (qmm_mmq_noalloc): one
+// array per GPU, in the code object's zero-initialized device memory, so no
+// call allocates.  Host code never passes the array's name to a kernel (there it
+// is a host-side stand-in); it passes the device address hipGetSymbolAddress
+// gives for the current device, looked up once per device.
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
+hipError_t static_scratch(int device, float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[device] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[device] = (float*)p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
 }
 
 }  // namespace qmm

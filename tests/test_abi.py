@@ -131,10 +131,15 @@ def test_quantize_empty_batch_is_a_no_op():
     assert L.qmm_quantize_activations(None, 0, 300, None, 0, None) == qmm.EINVAL
 
 
-def test_mmq_rejects_bad_arguments():
-    L = qmm._lib
+@pytest.mark.parametrize("entry", ["qmm_mmq", "qmm_mmq_noalloc"])
+def test_mmq_rejects_bad_arguments(entry):
+    """Both MMQ entry points share their validation: a null handle fails before
+    any HIP call, and an empty batch with a null handle still fails."""
+    f = getattr(qmm._lib, entry)
     good = ctypes.c_void_p(4096)
-    assert L.qmm_mmq(None, good, 100, 4, good, None) == qmm.EINVAL
+    assert f(None, good, 100, 4, good, None) == qmm.EINVAL
+    assert "handle" in qmm.last_error()
+    assert f(None, None, 0, 0, None, None) == qmm.EINVAL
 
 
 def test_info_and_export_reject_null():
