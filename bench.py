@@ -40,9 +40,11 @@ import synth  # noqa: E402
 MFMA_INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
 # The vector-ALU roof of the scale epilogue: each (token, row, 32-block) takes 64
 # int8 MFMA ops and, on the vector ALU, 3 instructions for q6_K (join the two
-# plane dots, convert, FMA) or 2 for q4_K (convert, FMA: its scale product comes
-# from the matrix core), at 256 CUs x 64 lanes x 2.4 GHz lane-instructions/s.
-EPILOGUE_INSTRS = {synth.Q6_K: 3, synth.Q4_K: 2}
+# plane dots, convert, FMA) or 2.25 for q4_K (remove the block dot's accumulator
+# bias, FMA with the scale product that comes from the matrix core, and per
+# super-block of 8 chunks two FMAs for d and the min term), at 256 CUs x 64
+# lanes x 2.4 GHz lane-instructions/s.
+EPILOGUE_INSTRS = {synth.Q6_K: 3, synth.Q4_K: 2.25}
 VALU_LANE_OPS = 256 * 64 * 2.4e9
 
 
@@ -115,12 +117,14 @@ def _parse():
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="before the warm-up steps, run untimed steps for at least this long so the "
                          "shader clock has left its idle state (0: none)")
-    ap.add_argument("--workload", default="ffn_down", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="layer", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-weights pass")
     ap.add_argument("--no-calib", action="store_true",
                     help="skip the measured MFMA and epilogue roofs (calibration kernels)")
-    ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads (default: the job's CPU share, OMP_NUM_THREADS where the "
+                         "machine sets it, else every CPU this process may run on)")
     ap.add_argument("--cpu-macs", type=float, default=2.4e10,
                     help="multiply-accumulates of the oracle sample (about 20 s of CPU work)")
     return ap.parse_args()
@@ -146,8 +150,8 @@ def measured_traffic(workload: str):
 
 def calibrate(torch, stream):
     """Measured roofs on this GPU: the int8 MFMA rate and the vector-ALU rates of
-    the MMQ's scale epilogues (q6_K 3 and q4_K 2 instructions per (token, row,
-    32-block), 64 int8 ops each), from the calibration kernels in libqmm_peak.so, with the shader
+    the MMQ's scale epilogues (q6_K 3 and q4_K 2.25 instructions per (token,
+    row, 32-block), 64 int8 ops each), from the calibration kernels in libqmm_peak.so, with the shader
     clock (s_memtime against the 100 MHz s_memrealtime) during each run.  Each
     is the best over a few occupancies, timed with HIP events on `stream`."""
     import ctypes
@@ -162,7 +166,7 @@ def calibrate(torch, stream):
     # kind, name, work-groups per CU tried, SIMD cycles per wave-iteration, int8 ops per wave-iteration
     for kind, name, per_cu, cyc, ops_it in ((0, "mfma_i8", (1, 2, 3), 128, 4 * 65536),
                                             (1, "epilogue_valu", (2, 4, 8), 192, 65536),
-                                            (2, "epilogue_valu_q4k", (2, 4, 8), 128, 65536)):
+                                            (2, "epilogue_valu_q4k", (2, 4, 8), 1152, 8 * 65536)):
         best = None
         for g in per_cu:
             grid = g * n_cu
@@ -195,6 +199,18 @@ def calibrate(torch, stream):
         # 8192 int8 ops per clock per CU (4 SIMDs x 32x32x32 MAC x 2 / 32 cycles)
         mf["spec_at_clock_tops"] = round(n_cu * mf["clock_ghz"] * 1e9 * 8192 / 1e12, 1)
     return out
+
+
+def cpu_threads(requested: int):
+    """Oracle threads: the request, else the CPUs this job may use -- where the
+    machine states the job's CPU share in OMP_NUM_THREADS that share, else every
+    CPU in this process's affinity mask."""
+    if requested > 0:
+        return requested, "--cpu-threads"
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        return int(share), "OMP_NUM_THREADS (the job's CPU share)"
+    return len(os.sched_getaffinity(0)), "all CPUs in the affinity mask"
 
 
 def cpu_baseline(gemms, raws, xs, T, threads, macs_target):
@@ -467,8 +483,11 @@ def main():
             rl["epilogue_roof"]["measured"] = round(epi_measured, 1)
             rl["epilogue_roof"]["frac_of_measured"] = round(mmq_tops / epi_measured, 4)
     if not args.no_cpu:
-        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        threads, rule = cpu_threads(args.cpu_threads)
         result["cpu_baseline"] = cpu_baseline(gemms, raws, xs, T, threads, args.cpu_macs)
+        result["cpu_baseline"]["host"] = {"cpu_count": os.cpu_count(),
+                                          "affinity_cpus": len(os.sched_getaffinity(0)),
+                                          "threads_rule": rule}
         result["cpu_baseline"]["single_thread"] = cpu_single_thread(gemms, raws, xs, T,
                                                                     args.cpu_macs / 4)
     for w in weights.values():

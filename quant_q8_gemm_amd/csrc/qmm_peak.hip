@@ -7,9 +7,12 @@
 //           the two plane dots (v_lshl_add_u32), convert (v_cvt_f32_i32), scale
 //           and accumulate with the activation scale held as f32 (v_fmac_f32)
 //           -- on 16 elements per lane;
-//   kind 2: the q4_K MMQ's epilogue, two instructions per element -- convert
-//           the block dot (v_cvt_f32_i32), multiply by the element's own f32
-//           scale and accumulate (v_fmac_f32) -- on 16 elements per lane.
+//   kind 2: the q4_K MMQ's epilogue over one 256-wide super-block (8 chunks):
+//           per chunk and element, subtract the accumulator bias from the block
+//           dot (v_add_f32 with a literal) and multiply by the element's own f32
+//           scale product and accumulate (v_fmac_f32); per super-block and
+//           element, two more FMAs (apply d, add the min term times -dmin) --
+//           2.25 instructions per (token, row, 32-block), on 16 elements per lane.
 // Work-group 0's first wave also records the shader clock (s_memtime) and the
 // 100 MHz constant clock (s_memrealtime) across its run, so the caller can
 // state the clock the rates were measured at.  These kernels are measurement
@@ -86,23 +89,34 @@ __global__ void __launch_bounds__(256) peak_epilogue(int iters, unsigned long lo
 
 __global__ void __launch_bounds__(256) peak_epilogue_q4(int iters, unsigned long long* clk, int* sink) {
   const int lane = threadIdx.x & 63;
-  float acc[16], sc[16];
+  float acc[16], inner[16], sc[16], d[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    acc[i] = (float)(lane + i);
-    sc[i] = 0x1p-40f * (float)(lane + i + 1);  // in registers, as in the MMQ; keeps acc finite
+    acc[i] = 0.0f;
+    inner[i] = (float)(lane + i);
+    sc[i] = 0x1p-40f * (float)(lane + i + 1);  // in registers, as in the MMQ; keeps the values finite
+    d[i] = 0x1p-20f * (float)(i + 1);
   }
+  const float c0 = 0.15915494f;
   uint64_t t = 0, r = 0;
   clock_start(t, r);
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)  // the converted integer is acc's bit pattern: it changes every step
-      acc[i] = fmaf((float)__builtin_bit_cast(int, acc[i]), sc[i], acc[i]);
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)  // the "block dot" is inner's own value: it changes every step
+        inner[i] = fmaf(inner[i] - c0, sc[i], inner[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      acc[i] = fmaf(inner[i], d[i], acc[i]);
+      acc[i] = fmaf(acc[i], sc[i], acc[i]);
+    }
   }
   clock_end(t, r, clk);
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s += acc[i];
+  for (int i = 0; i < 16; ++i) s += acc[i] + inner[i];
   sink[blockIdx.x * blockDim.x + threadIdx.x] = __builtin_bit_cast(int, s);
 }
 
@@ -113,8 +127,9 @@ __global__ void __launch_bounds__(256) peak_epilogue_q4(int iters, unsigned long
 // iterations on `stream`.
 // clk: device uint64[2] (shader clocks, 100 MHz ticks of work-group 0's first
 // wave); sink: device int32[grid * 256].  Each iteration is, per wave, 4 MFMAs
-// of 32x32x32 (kind 0) or 16 epilogue elements per lane (kinds 1, 2): 262144
-// or 65536 int8-equivalent operations.  Returns 0 or the hipError_t of the launch.
+// of 32x32x32 (kind 0), 16 epilogue elements per lane (kind 1) or 8 chunks of
+// 16 epilogue elements per lane (kind 2): 262144, 65536 or 524288
+// int8-equivalent operations.  Returns 0 or the hipError_t of the launch.
 extern "C" int qmm_peak_launch(int kind, int iters, int grid, void* clk, void* sink, void* stream) {
   if (kind < 0 || kind > 2 || iters < 1 || grid < 1 || !clk || !sink) return (int)hipErrorInvalidValue;
   hipStream_t s = (hipStream_t)stream;
