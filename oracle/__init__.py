@@ -211,6 +211,33 @@ def mmq_rows(type_: int, raw: np.ndarray, od: int, id_: int, q, dh, s, j0: int, 
     return out, A
 
 
+def mmq_parallel(type_: int, raw: np.ndarray, od: int, id_: int, q, dh, s, threads: int = 0):
+    """mmq() with the rows split into blocks that oracle_mmq_rows computes on
+    separate threads (the C call releases the GIL); the arithmetic of every
+    element is mmq()'s.  threads = 0: OMP_NUM_THREADS, else the CPUs in this
+    process's affinity mask."""
+    import concurrent.futures as cf
+    raw = _raw_check(type_, raw, od, id_)
+    q, dh, s, T = _act_check(q, dh, s, id_)
+    if threads <= 0:
+        env = os.environ.get("OMP_NUM_THREADS", "")
+        threads = int(env) if env.isdigit() and int(env) > 0 else len(os.sched_getaffinity(0))
+    out = np.empty((T, od), np.float64)
+    A = np.empty((T, od), np.float64)
+    bounds = np.linspace(0, od, min(od, 4 * threads) + 1).astype(int)
+
+    def work(i):
+        j0, j1 = int(bounds[i]), int(bounds[i + 1])
+        if j1 > j0:
+            o, a = mmq_rows(type_, raw, od, id_, q, dh, s, j0, j1)
+            out[:, j0:j1] = o
+            A[:, j0:j1] = a
+
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(work, range(len(bounds) - 1)))
+    return out, A
+
+
 def mmq_at(type_: int, raw: np.ndarray, od: int, id_: int, q, dh, s, ts, js):
     """Result at the (ts[i], js[i]) pairs: (out [n], A [n]).  Pairs sorted by j
     decode each weight row once."""

@@ -72,6 +72,31 @@ def test_unit_q4k_is_integer_matmul():
     assert np.array_equal(D32, ref32)
 
 
+def test_q6k_scale_folded_dots_at_full_range_scales():
+    """J (the block dot carrying both 16-group scales) at full-range int8 scales
+    against an independent numpy int64 product of the scale-folded weights
+    sc[k/16] * (code - 32): per 32-block, and summed over the row (d = 1 and
+    integer activations with dh = 1 make the result that exact integer matmul)."""
+    rng = np.random.default_rng(12)
+    od, id_, T = 6, 768, 5
+    nb = od * (id_ // 256)
+    blocks = [q6k_block(ql=rng.integers(0, 256, 128, dtype=np.uint8),
+                        qh=rng.integers(0, 256, 64, dtype=np.uint8),
+                        sc=rng.integers(-128, 128, 16).astype(np.int8)) for _ in range(nb)]
+    raw = np.concatenate(blocks)
+    x = _int_acts(rng, T, id_)
+    q, dh, s = oracle.quantize(x)
+    assert np.all(dh == 0x3C00)
+    w, sc, d = oracle.decode_q6k(raw, od, id_)
+    assert np.all(d == 1.0) and sc.min() < -100 and sc.max() > 100
+    folded = w.astype(np.int64) * np.repeat(sc.astype(np.int64), 16, axis=1)     # [od][id]
+    Jref = np.einsum("tck,jck->tjc", x.astype(np.int64).reshape(T, -1, 32), folded.reshape(od, -1, 32))
+    D16, J = oracle.dots_q6k(raw, od, id_, q)
+    assert np.array_equal(J, Jref)
+    out, _ = oracle.mmq(oracle.Q6_K, raw, od, id_, q, dh, s)
+    assert np.array_equal(out, (x.astype(np.int64) @ folded.T).astype(np.float64))
+
+
 def _brute_force(type_, raw, od, id_, q, dh, s):
     """Dequantize both sides in f64 and multiply; returns (ref, extra bound)."""
     T = q.shape[0]
@@ -112,6 +137,8 @@ def test_per_pair_and_row_slices_agree_with_full():
     out, A = oracle.mmq(synth.Q4_K, raw, 12, 512, q, dh, s)
     o2, a2 = oracle.mmq_rows(synth.Q4_K, raw, 12, 512, q, dh, s, 3, 10)
     assert np.array_equal(o2, out[:, 3:10]) and np.array_equal(a2, A[:, 3:10])
+    o4, a4 = oracle.mmq_parallel(synth.Q4_K, raw, 12, 512, q, dh, s, threads=3)
+    assert np.array_equal(o4, out) and np.array_equal(a4, A)
     ts = np.array([0, 8, 4, 4]); js = np.array([0, 0, 11, 5])
     o3, a3 = oracle.mmq_at(synth.Q4_K, raw, 12, 512, q, dh, s, ts, js)
     assert np.array_equal(o3, out[ts, js]) and np.array_equal(a3, A[ts, js])

@@ -37,6 +37,10 @@ MUTANTS = {
                                "idot(r->w6 + 16 * g, qrow + 16 * (g ^ 1), 16)"),
     "q4k chunk super-scale": ("(double)r->d[b] * (double)r->sc4[c] * dh",
                               "(double)r->d[c % 2] * (double)r->sc4[c] * dh"),
+    "q6k J scale index": ("(int32_t)(sc[2 * c] * d0 + sc[2 * c + 1] * d1)",
+                          "(int32_t)(sc[c] * d0 + sc[c + 1] * d1)"),
+    "q6k J halves' scales swapped": ("(int32_t)(sc[2 * c] * d0 + sc[2 * c + 1] * d1)",
+                                     "(int32_t)(sc[2 * c + 1] * d0 + sc[2 * c] * d1)"),
 }
 
 PIN_TESTS = ["tests/test_oracle_f16.py", "tests/test_oracle_decode.py",
