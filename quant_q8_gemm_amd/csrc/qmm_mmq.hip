@@ -273,8 +273,9 @@ __device__ __forceinline__ void store_block(float* __restrict__ out, const v16f&
 // kernel adds a tile's S partials in slice order and stores the tile.  The
 // tail is whole row tiles at the end, so the rows before it keep exactly the
 // summation order they have without a tail.
+// Every launch shape runs 16 waves per CU, 4 per SIMD: at most 128 VGPRs.
 template <int TYPE, int WR, int WT, int KC, int KS>
-__global__ void __launch_bounds__(64 * WR * WT * KS, 16 / (WR * WT * KS))
+__global__ void __launch_bounds__(64 * WR * WT * KS) __attribute__((amdgpu_waves_per_eu(4, 4)))
 mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
            const uint8_t* __restrict__ wmn, const uint8_t* __restrict__ wsc,
            const uint8_t* __restrict__ qq,
