@@ -44,7 +44,9 @@ MFMA_INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
 # bias, FMA with the scale product that comes from the matrix core, and per
 # super-block of 8 chunks two FMAs for d and the min term), at 256 CUs x 64
 # lanes x 2.4 GHz lane-instructions/s.
-EPILOGUE_INSTRS = {synth.Q6_K: 3, synth.Q4_K: 2.25}
+EPILOGUE_INSTRS = {synth.Q6_K: 3, synth.Q4_K: 2.25,
+                   # the packed-code registration: 4 more per 16 elements to unpack
+                   synth.Q4_K_PACKED: 2.5}
 VALU_LANE_OPS = 256 * 64 * 2.4e9
 
 
@@ -89,6 +91,19 @@ WORKLOADS = {
                ("ffn_up", synth.Q4_K, 11008, 4096, "ffn_in"),
                ("ffn_down", synth.Q6_K, 4096, 11008, "ffn_mid")],
               False),
+    # the same layer with the q4_K weights registered with their codes packed two
+    # per byte (0.5 instead of 1 byte per weight of code plane)
+    "layer_packed": ("LLaMA-7B q4_K_M-style layer, 3314 tokens, q4_K codes packed on the device",
+                     synth.LAYER_TOKENS,
+                     {"attn_in": 4096, "attn_out": 4096, "ffn_in": 4096, "ffn_mid": 11008},
+                     [("attn_q", synth.Q4_K_PACKED, 4096, 4096, "attn_in"),
+                      ("attn_k", synth.Q4_K_PACKED, 4096, 4096, "attn_in"),
+                      ("attn_v", synth.Q6_K, 4096, 4096, "attn_in"),
+                      ("attn_output", synth.Q4_K_PACKED, 4096, 4096, "attn_out"),
+                      ("ffn_gate", synth.Q4_K_PACKED, 11008, 4096, "ffn_in"),
+                      ("ffn_up", synth.Q4_K_PACKED, 11008, 4096, "ffn_in"),
+                      ("ffn_down", synth.Q6_K, 4096, 11008, "ffn_mid")],
+                     False),
     # the same layer with same-type GEMMs that share an input fused by row
     # concatenation at registration: q||k (od 8192) and gate||up (od 22016)
     "layer_fused": ("LLaMA-7B q4_K_M-style layer, 3314 tokens, q||k and gate||up fused",
@@ -478,7 +493,9 @@ def main():
             rl = result["roofline"]
             rl["measured_peak"] = cal["mfma_i8"]["tops"]
             rl["frac_of_measured_peak"] = round(mmq_tops / cal["mfma_i8"]["tops"], 4)
-            measured = {synth.Q6_K: cal["epilogue_valu"]["tops"], synth.Q4_K: cal["epilogue_valu_q4k"]["tops"]}
+            measured = {synth.Q6_K: cal["epilogue_valu"]["tops"], synth.Q4_K: cal["epilogue_valu_q4k"]["tops"],
+                        synth.Q4_K_PACKED: cal["epilogue_valu_q4k"]["tops"] * EPILOGUE_INSTRS[synth.Q4_K]
+                        / EPILOGUE_INSTRS[synth.Q4_K_PACKED]}
             epi_measured = epilogue_roof(gemms, T, measured.get)
             rl["epilogue_roof"]["measured"] = round(epi_measured, 1)
             rl["epilogue_roof"]["frac_of_measured"] = round(mmq_tops / epi_measured, 4)

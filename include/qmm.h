@@ -49,6 +49,11 @@ extern "C" {
                       qh[64] high 2 bits, int8 scales[16] (one per 16 weights),
                       f16 d; weight = d*scale*(code - 32)
                       (r56 sections 1, 3.2; r58 section 3.2). */
+#define QMM_Q4_K_PACKED 14 /* q4_K blocks (the same 144-byte input as QMM_Q4_K)
+                      registered with the 4-bit codes kept two per byte in the
+                      device plane, as the raw qs bytes hold them (r58 section
+                      2.2): 0.5 instead of 1 byte per weight, unpacked by the
+                      GEMM.  Results are bit-identical to QMM_Q4_K's. */
 
 /* Return codes. */
 #define QMM_OK 0
@@ -71,7 +76,7 @@ extern "C" {
 typedef struct qmm_weights qmm_weights;
 
 typedef struct {
-    int type;            /* QMM_Q4_K or QMM_Q6_K */
+    int type;            /* QMM_Q4_K, QMM_Q4_K_PACKED or QMM_Q6_K */
     int64_t od;          /* output rows */
     int64_t id;          /* inner dimension */
     int64_t od_pad;      /* rows padded with zeros to the row tile */
@@ -87,11 +92,13 @@ typedef struct {
  * qmm_register_weights -- copy one k-quant weight matrix to the device and
  * expand it once into the planes the GEMM reads (the registration-time planes
  * of r56 section 2.2 and r58 section 3.2; layout: see qmm_weights_export).
- *   type        QMM_Q4_K or QMM_Q6_K
+ *   type        QMM_Q4_K, QMM_Q4_K_PACKED (q4_K blocks, codes kept packed on
+ *               the device) or QMM_Q6_K
  *   od, id      the weight is od rows of id weights; id % 256 == 0.  Any od >= 1
  *               (odd included) is valid: rows are padded with zeros internally.
  *   host_bytes  host memory, od rows * (id/256) blocks, row major, exactly
- *               nbytes = od * (id/256) * (144 or 210) bytes.  Copied; the caller
+ *               nbytes = od * (id/256) * (144 for both q4_K types, 210 for
+ *               q6_K) bytes.  Copied; the caller
  *               keeps ownership and may free it when the call returns.
  *   stream      the copy and the expansion run on it; the call returns after
  *               both completed (it synchronizes the stream).
@@ -120,6 +127,11 @@ int qmm_weights_info(const qmm_weights *w, qmm_info *out);
  *                 q4_K: int8 [R][nchunk][2][32][16]: the 4-bit code (0..15)
  *                 of (row j, k) at byte (j/32*nchunk + k/32)*1024
  *                 + ((k%32)/16)*512 + (j%32)*16 + k%16
+ *                 q4_K packed: uint8 [R][nchunk][2][32][8]: the code of
+ *                 (row j, k) in the low nibble (k%16 < 8) or the high nibble
+ *                 (k%16 >= 8) of byte (j/32*nchunk + k/32)*512
+ *                 + ((k%32)/16)*256 + (j%32)*8 + k%8
+ *   the planes below are the same for both q4_K types
  *   at wd_offset  q6_K: f32 [R][nsb][32]: d of (row j, super-block b) at
  *                 element (j/32*nsb + b)*32 + j%32
  *                 q4_K: f32 [R][nsb][2][32]: d*2^25 (part 0) and -dmin

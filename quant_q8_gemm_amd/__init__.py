@@ -34,13 +34,14 @@ _lib = ctypes.CDLL(LIB_PATH)
 # keep in step with include/qmm.h
 Q4_K = 4
 Q6_K = 6
+Q4_K_PACKED = 14  # q4_K blocks, codes kept two per byte on the device
 OK = 0
 EINVAL = -1
 ESHAPE = -2
 ENOMEM = -3
 EHIP = -4
 TOKEN_PAD = 128
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210}
+BLOCK_BYTES = {Q4_K: 144, Q4_K_PACKED: 144, Q6_K: 210}
 
 # The full list of entry points include/qmm.h declares.
 EXPORTS = ("qmm_register_weights", "qmm_weights_info", "qmm_weights_export", "qmm_release_weights",

@@ -62,7 +62,11 @@ void ok() { g_last_error.clear(); }
 
 size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
 
-size_t block_bytes(int type) { return type == QMM_Q4_K ? 144 : 210; }
+size_t block_bytes(int type) { return qmm::is_q4k(type) ? 144 : 210; }
+
+const char* type_name(int type) {
+  return type == QMM_Q6_K ? "q6_K" : type == QMM_Q4_K ? "q4_K" : "q4_K (codes packed)";
+}
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -99,9 +103,9 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
                          void* stream, qmm_weights** out) {
   if (out == nullptr) return fail(QMM_EINVAL, "out is NULL");
   *out = nullptr;
-  if (type != QMM_Q4_K && type != QMM_Q6_K)
-    return fail(QMM_EINVAL, "type must be QMM_Q4_K (%d) or QMM_Q6_K (%d), got %d", QMM_Q4_K,
-                QMM_Q6_K, type);
+  if (type != QMM_Q4_K && type != QMM_Q4_K_PACKED && type != QMM_Q6_K)
+    return fail(QMM_EINVAL, "type must be QMM_Q4_K (%d), QMM_Q4_K_PACKED (%d) or QMM_Q6_K (%d), got %d",
+                QMM_Q4_K, QMM_Q4_K_PACKED, QMM_Q6_K, type);
   if (od < 1 || od > QMM_MAX_OD)
     return fail(QMM_EINVAL, "od must be in [1, %d], got %lld", QMM_MAX_OD, (long long)od);
   if (int rc = check_id(id)) return rc;
@@ -160,8 +164,8 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   }
   p.wq = (int8_t*)alloc;
   p.wd = (float*)((char*)alloc + off_wd);
-  p.wmn = type == QMM_Q4_K ? (uint16_t*)((char*)alloc + off_mn) : nullptr;
-  p.wsc = type == QMM_Q4_K ? (uint16_t*)((uint8_t*)alloc + off_sc) : nullptr;
+  p.wmn = qmm::is_q4k(type) ? (uint16_t*)((char*)alloc + off_mn) : nullptr;
+  p.wsc = qmm::is_q4k(type) ? (uint16_t*)((uint8_t*)alloc + off_sc) : nullptr;
   int rc = QMM_OK;
   if ((e = hipMemcpyAsync(raw, host_bytes, nbytes, hipMemcpyHostToDevice, s)) != hipSuccess)
     rc = fail_hip(e, "hipMemcpyAsync(weights)");
@@ -181,13 +185,13 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   w->raw_bytes = nbytes;
   w->plane_bytes = plane_bytes;
   w->wd_offset = off_wd;
-  w->mn_offset = type == QMM_Q4_K ? off_mn : plane_bytes;
+  w->mn_offset = qmm::is_q4k(type) ? off_mn : plane_bytes;
   w->dm_offset = plane_bytes;  // no plane of its own: q4_K's dmin sits in the d plane
-  w->sc_offset = type == QMM_Q4_K ? off_sc : plane_bytes;
+  w->sc_offset = qmm::is_q4k(type) ? off_sc : plane_bytes;
   w->alloc = alloc;
   if (getenv("QMM_LOG") != nullptr)
     fprintf(stderr, "qmm: registered %s od=%lld id=%lld od_pad=%lld raw=%zu planes=%zu device=%d\n",
-            type == QMM_Q4_K ? "q4_K" : "q6_K", (long long)od, (long long)id,
+            type_name(type), (long long)od, (long long)id,
             (long long)p.od_pad, nbytes, plane_bytes, device);
   *out = w;
   ok();

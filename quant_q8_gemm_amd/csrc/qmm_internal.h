@@ -11,7 +11,7 @@ namespace qmm {
 // Device planes of one registered weight matrix (layout documented in
 // qmm_repack.hip next to the repack kernel).
 struct Planes {
-  int type;          // QMM_Q4_K or QMM_Q6_K
+  int type;          // QMM_Q4_K, QMM_Q4_K_PACKED or QMM_Q6_K
   int64_t od, id;    // logical shape
   int64_t od_pad;    // rows padded to kRowPad
   int64_t nsb;       // id / 256
@@ -25,6 +25,10 @@ struct Planes {
 constexpr int kRowPad = 128;     // weight rows are padded to a multiple of this
 constexpr int kTokenPad = 128;   // tokens are padded to a multiple of this
 constexpr int kQ4CodeFrag = 1024; // q4_K code bytes per (32-row block, chunk): one code per byte
+constexpr int kQ4PackedFrag = 512; // the same, packed: two codes per byte
+
+// Both q4_K registrations share every plane but the codes'.
+constexpr bool is_q4k(int type) { return type == 4 || type == 14; }  // QMM_Q4_K, QMM_Q4_K_PACKED
 
 // Byte sizes of the planes for a shape (all offsets 256-byte aligned).
 size_t wq_bytes(int type, int64_t od_pad, int64_t id);

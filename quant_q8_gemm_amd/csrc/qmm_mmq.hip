@@ -83,11 +83,11 @@ __device__ __forceinline__ void copy16_lane(const void* src, uint32_t lds) {
 // Weight fragment bytes per (32-row block, chunk): q6_K hi and lo planes of
 // 1 KiB each; q4_K codes (16 bytes per lane).
 template <int TYPE>
-constexpr int kFragA = TYPE == QMM_Q6_K ? 2048 : kQ4CodeFrag;
+constexpr int kFragA = TYPE == QMM_Q6_K ? 2048 : TYPE == QMM_Q4_K_PACKED ? kQ4PackedFrag : kQ4CodeFrag;
 
 template <int TYPE, int WR, int WT, int KC>
 struct alignas(16) Stage {
-  static constexpr bool kQ4 = TYPE == QMM_Q4_K;
+  static constexpr bool kQ4 = is_q4k(TYPE);
   int8_t a[WR][KC][kFragA<TYPE>];    // weight fragments: [row block][chunk]
   int8_t b[WT][KC][1024];            // q8 codes: [token block][chunk][fragment]
   uint32_t s[WT][KC][32];            // (dh, s) pairs: [token block][chunk][token]
@@ -166,6 +166,20 @@ struct WeightOps<QMM_Q4_K> {
   __device__ static float val(const D& d, int i) {
     const v16f f = __builtin_bit_cast(v16f, d.c);
     return f[i] - __builtin_bit_cast(float, kQ4BiasBits);
+  }
+};
+
+// q4_K with the codes kept two per byte: a lane's 8 bytes hold its 16 codes,
+// code i in the low nibble of byte i and code i+8 in the high one (i < 8); two
+// masks and two shifts unpack them into the 16 code bytes the MFMA takes.
+// Everything after the load is q4_K's.
+template <>
+struct WeightOps<QMM_Q4_K_PACKED> : WeightOps<QMM_Q4_K> {
+  __device__ static A load(const int8_t* frag, int lane) {
+    const uint2 p = *(const uint2*)(frag + lane * 8);
+    const v4i c = {(int)(p.x & 0x0F0F0F0Fu), (int)(p.y & 0x0F0F0F0Fu), (int)((p.x >> 4) & 0x0F0F0F0Fu),
+                   (int)((p.y >> 4) & 0x0F0F0F0Fu)};
+    return {c};
   }
 };
 
@@ -293,7 +307,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
                     sizeof(St) == __builtin_offsetof(St, s) + 16 * St::kUnits,
                 "the small region is contiguous and ends the stage");
   // the q4_K min term collects a super-block's 8 chunks over two stages
-  static_assert(TYPE == QMM_Q6_K || KC == 4, "q4_K stages are half super-blocks");
+  constexpr bool kQ4 = is_q4k(TYPE);
+  static_assert(!kQ4 || KC == 4, "q4_K stages are half super-blocks");
   // k-group 1's sums pass to k-group 0 through k-group 0's two stages
   static_assert(KS == 1 || 2 * sizeof(St) >= (size_t)kWaves * 16 * 64 * 4, "room to combine k-groups");
   __shared__ St stage_all[KS][2];
@@ -357,7 +372,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   // per row block); per super-block, at its last stage: 4 q4_K mins (512
   // bytes), 2 q6_K d (128 bytes) or q4_K d and dmin (256 bytes)
   int small_kind = 0;
-  constexpr int kDBytes = TYPE == QMM_Q4_K ? 256 : 128;  // d plane bytes per (row block, super-block)
+  constexpr int kDBytes = kQ4 ? 256 : 128;  // d plane bytes per (row block, super-block)
   if (wave < St::kSmallJobs) {
     const int u = wave * 64 + lane;
     const int sb0g = gbeg / kStagesPerSb;
@@ -457,7 +472,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         // waits for the reads just issued.
         uint32_t dhr = st.s[wt][0][lane & 31], dhr_even = 0;
         v2i a_sc = {}, amin = {};
-        if constexpr (TYPE == QMM_Q4_K) {
+        if constexpr (kQ4) {
           if (h == kStagesPerSb - 1) amin = *(const v2i*)(&st.mn[wr][lane >> 5][lane & 31][0]);
           a_sc = *(const v2i*)(&st.sc[wr][lane & 31][0]);
         }
@@ -476,7 +491,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
           // v_fma_mix_f32 the compiler would otherwise fold the f16 operand into
           v16f sd;
           float dh = 0.0f;
-          if constexpr (TYPE == QMM_Q4_K) {
+          if constexpr (kQ4) {
             sd = scale_outer(a_sc, dhr, cc);
             pin(sd);
           }
@@ -501,7 +516,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
           }
           uint32_t dhr_next = 0;
           if (cc + 1 < KC) dhr_next = st.s[wt][cc + 1][lane & 31];
-          if constexpr (TYPE == QMM_Q4_K) {
+          if constexpr (kQ4) {
             if (cc & 1) {  // the scaled sums of chunks cc-1 and cc as an f16 pair
               const int sp = (int)__builtin_amdgcn_perm(dhr, dhr_even, 0x07060302u);
               if (lane_hi == (h == 1)) bs[cc >> 1] = sp;
@@ -514,7 +529,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
           }
           // element i's scale: q4_K the outer product's, q6_K the token's dh
           auto scale = [&](int i) __attribute__((always_inline)) {
-            if constexpr (TYPE == QMM_Q4_K) return sd[i];
+            if constexpr (kQ4) return sd[i];
             else return dh;
           };
           if (cc == 0 && starts_sb) {
@@ -533,7 +548,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
           }
           // order inside the step: MFMAs, stage copies, LDS reads, the vector epilogue
           // MFMA: q4_K's scale products of this chunk, then the next chunk's block dots
-          __builtin_amdgcn_sched_group_barrier(0x008, W::kMfma + (TYPE == QMM_Q4_K), 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, W::kMfma + kQ4, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);         // VMEM (stage copies)
           __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);         // DS reads
           __builtin_amdgcn_sched_group_barrier(0x002, 72, 0);        // VALU
@@ -541,7 +556,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         }
         if (h == kStagesPerSb - 1) {  // end of a super-block: apply its d (q4_K: d*2^25)
           v16f mt;
-          if constexpr (TYPE == QMM_Q4_K) {  // and q4_K's min term, times -dmin
+          if constexpr (kQ4) {  // and q4_K's min term, times -dmin
             typedef _Float16 v4h __attribute__((ext_vector_type(4)));
             const v16f zero = {};
             mt = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, amin), __builtin_bit_cast(v4h, bs),
@@ -555,7 +570,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
             acc[4 * q + 2] = fmaf(inner[4 * q + 2], d4.z, acc[4 * q + 2]);
             acc[4 * q + 3] = fmaf(inner[4 * q + 3], d4.w, acc[4 * q + 3]);
           }
-          if constexpr (TYPE == QMM_Q4_K) {
+          if constexpr (kQ4) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const float4 m4 = *(const float4*)(&st.d[wr][1][8 * q + 4 * (lane >> 5)]);
@@ -762,14 +777,15 @@ hipError_t launch_mmq(const Planes& p, const MmqPlan& plan, const uint8_t* qact,
                       int64_t t_pad, float* out, float* part, hipStream_t s) {
   constexpr Geometry q6 = kQ6Many, q4 = kQ4Many, f = kFew;
   if (p.type == QMM_Q6_K)
-    return plan.many ? launch_tiled<QMM_Q6_K, q6.wr, q6.wt, q6.kc, q6.ks>(p, plan, qact, n_tok, t_pad, out,
-                                                                         part, s)
-                     : launch_tiled<QMM_Q6_K, f.wr, f.wt, f.kc, f.ks>(p, plan, qact, n_tok, t_pad, out,
-                                                                     part, s);
-  return plan.many ? launch_tiled<QMM_Q4_K, q4.wr, q4.wt, q4.kc, q4.ks>(p, plan, qact, n_tok, t_pad, out,
-                                                                       part, s)
-                   : launch_tiled<QMM_Q4_K, f.wr, f.wt, f.kc, f.ks>(p, plan, qact, n_tok, t_pad, out, part,
-                                                                   s);
+    return plan.many ? launch_tiled<QMM_Q6_K, q6.wr, q6.wt, q6.kc, q6.ks>(p, plan, qact, n_tok, t_pad, out, part, s)
+                     : launch_tiled<QMM_Q6_K, f.wr, f.wt, f.kc, f.ks>(p, plan, qact, n_tok, t_pad, out, part, s);
+  if (p.type == QMM_Q4_K_PACKED)
+    return plan.many ? launch_tiled<QMM_Q4_K_PACKED, q4.wr, q4.wt, q4.kc, q4.ks>(p, plan, qact, n_tok, t_pad, out,
+                                                                               part, s)
+                     : launch_tiled<QMM_Q4_K_PACKED, f.wr, f.wt, f.kc, f.ks>(p, plan, qact, n_tok, t_pad, out,
+                                                                           part, s);
+  return plan.many ? launch_tiled<QMM_Q4_K, q4.wr, q4.wt, q4.kc, q4.ks>(p, plan, qact, n_tok, t_pad, out, part, s)
+                   : launch_tiled<QMM_Q4_K, f.wr, f.wt, f.kc, f.ks>(p, plan, qact, n_tok, t_pad, out, part, s);
 }
 
 // The tail partials of the allocation-free entry point (qmm_mmq_noalloc): one

@@ -28,6 +28,11 @@ namespace qmm {
 //       q4_K: int8 [R][nchunk][2 k-halves][32 rows][16 bytes]: the code of
 //             (row j, k) in [0, 15] at byte
 //             (j/32*nchunk + k/32)*1024 + ((k%32)/16)*512 + (j%32)*16 + k%16
+//       q4_K packed: [R][nchunk][2 k-halves][32 rows][8 bytes]: the code of
+//             (row j, k) in the low (k%16 < 8) or high (k%16 >= 8) nibble of
+//             byte (j/32*nchunk + k/32)*512 + ((k%32)/16)*256 + (j%32)*8 + k%8
+//             (one lane's 8 bytes unpack with two masks and two shifts into
+//             its 16 code bytes)
 //   wd  q6_K: f32 [R][nsb][32 rows]  d of (row, super-block)
 //       q4_K: f32 [R][nsb][2][32 rows]  of (row j, super-block b): part 0 is
 //             d*2^25, part 1 is -dmin, at element ((j/32*nsb + b)*2 + part)*32
@@ -42,17 +47,18 @@ namespace qmm {
 // Rows od..od_pad-1 are zero in every plane.
 // ---------------------------------------------------------------------------
 size_t wq_bytes(int type, int64_t od_pad, int64_t id) {
-  return type == QMM_Q6_K ? (size_t)od_pad * (size_t)id * 2 : (size_t)od_pad * (size_t)id;
+  const size_t n = (size_t)od_pad * (size_t)id;
+  return type == QMM_Q6_K ? n * 2 : type == QMM_Q4_K_PACKED ? n / 2 : n;
 }
 size_t wd_bytes(int type, int64_t od_pad, int64_t id) {
-  return (size_t)od_pad * (size_t)(id / 256) * 4 * (type == QMM_Q4_K ? 2 : 1);
+  return (size_t)od_pad * (size_t)(id / 256) * 4 * (is_q4k(type) ? 2 : 1);
 }
 size_t wmn_bytes(int type, int64_t od_pad, int64_t id) {
-  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) * 2 : 0;
+  return is_q4k(type) ? (size_t)od_pad * (size_t)(id / 32) * 2 : 0;
 }
 size_t wdm_bytes(int, int64_t, int64_t) { return 0; }
 size_t wsc_bytes(int type, int64_t od_pad, int64_t id) {
-  return type == QMM_Q4_K ? (size_t)od_pad * (size_t)(id / 32) * 2 : 0;
+  return is_q4k(type) ? (size_t)od_pad * (size_t)(id / 32) * 2 : 0;
 }
 
 // q4_K: the 6-bit scale and min of sub-block cl of a 144-byte block (ggml's
@@ -131,7 +137,7 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
       }
     }
   } else if (h == 0) {
-    if (type == QMM_Q4_K) {
+    if (is_q4k(type)) {
       const int64_t si = (((int64_t)rb * nsb + b) * 2 + (cl >> 2)) * 128 + jr * 4 + (cl & 3);
       wsc[si] = 0;
       wmn[si] = 0;
@@ -147,6 +153,9 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
     int8_t* dst = wq + ((int64_t)rb * nchunk + c) * 2048 + h * 512 + jr * 16;
     *(uint4*)dst = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     *(uint4*)(dst + 1024) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  } else if (type == QMM_Q4_K_PACKED) {  // codes i and i+8 share byte i
+    int8_t* dst = wq + ((int64_t)rb * nchunk + c) * kQ4PackedFrag + h * 256 + jr * 8;
+    *(uint2*)dst = make_uint2(lo[0] | (lo[2] << 4), lo[1] | (lo[3] << 4));
   } else {
     int8_t* dst = wq + ((int64_t)rb * nchunk + c) * kQ4CodeFrag + h * 512 + jr * 16;
     *(uint4*)dst = make_uint4(lo[0], lo[1], lo[2], lo[3]);

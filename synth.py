@@ -22,8 +22,9 @@ import numpy as np
 
 Q4_K = 4
 Q6_K = 6
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210}
-TYPE_NAMES = {Q4_K: "q4_K", Q6_K: "q6_K"}
+Q4_K_PACKED = 14  # the same q4_K input blocks, registered with packed codes
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, Q4_K_PACKED: 144}
+TYPE_NAMES = {Q4_K: "q4_K", Q6_K: "q6_K", Q4_K_PACKED: "q4_K packed"}
 
 
 def _f16_scale(rng: np.random.Generator, n: int) -> np.ndarray:
@@ -65,7 +66,7 @@ def q4k_weights(rng: np.random.Generator, od: int, id_: int) -> np.ndarray:
 def weights(rng: np.random.Generator, type_: int, od: int, id_: int) -> np.ndarray:
     if type_ == Q6_K:
         return q6k_weights(rng, od, id_)
-    if type_ == Q4_K:
+    if type_ in (Q4_K, Q4_K_PACKED):
         return q4k_weights(rng, od, id_)
     raise ValueError(f"unknown type {type_}")
 
@@ -78,6 +79,11 @@ def activations(rng: np.random.Generator, n_tok: int, id_: int,
         mask = rng.random((n_tok, id_)) < 0.01
         x = np.where(mask, x * np.float32(20.0), x).astype(np.float32)
     return x
+
+
+def block_format(type_: int) -> int:
+    """The block format a registration type reads (both q4_K types read q4_K)."""
+    return Q4_K if type_ == Q4_K_PACKED else type_
 
 
 def case(type_: int, od: int, id_: int, n_tok: int, seed: int = 0,

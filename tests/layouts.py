@@ -27,7 +27,8 @@ def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: i
     """exported planes -> dict.  q6_K: w [od_pad][id] int32 folded weights
     64*hi + lo, d [od_pad][nsb] f32.  q4_K: codes [od_pad][id] int32, d25
     [od_pad][nsb] f32 (d times 2^25), ndmin [od_pad][nsb] f32 (-dmin), sc and mn
-    [od_pad][nchunk] binary16 bit patterns."""
+    [od_pad][nchunk] binary16 bit patterns (type 14, packed q4_K: the same, its
+    codes read from the nibbles)."""
     nchunk, nsb = id_ // 32, id_ // 256
     R = od_pad // 32
     buf = np.asarray(buf, np.uint8)
@@ -39,9 +40,13 @@ def read_planes(buf: np.ndarray, type_: int, od_pad: int, id_: int, wd_offset: i
         w = hi * 64 + lo
         d = buf[wd_offset: wd_offset + od_pad * nsb * 4].view("<f4").reshape(R, nsb, 32)
         return {"w": w, "d": d.transpose(0, 2, 1).reshape(od_pad, nsb)}
-    # [R][nchunk][k-half h][row][16]: code k = 16h + byte
-    pk = buf[: od_pad * id_].view(np.int8).reshape(R, nchunk, 2, 32, 16)
-    codes = pk.transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
+    if type_ == 14:  # packed: [R][nchunk][k-half h][row][8]: codes 16h + b (low nibble), + b + 8 (high)
+        pk = buf[: od_pad * id_ // 2].reshape(R, nchunk, 2, 32, 8)
+        both = np.concatenate([pk & 15, pk >> 4], axis=4)        # [..][16]: k%16 = 0..7 low, 8..15 high
+        codes = both.transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
+    else:  # [R][nchunk][k-half h][row][16]: code k = 16h + byte
+        pk = buf[: od_pad * id_].view(np.int8).reshape(R, nchunk, 2, 32, 16)
+        codes = pk.transpose(0, 3, 1, 2, 4).reshape(od_pad, id_).astype(np.int32)
     assert codes.min() >= 0 and codes.max() <= 15
     # (d*2^25, -dmin): [R][nsb][part][row]
     dd = buf[wd_offset: wd_offset + od_pad * nsb * 8].view("<f4").reshape(R, nsb, 2, 32)

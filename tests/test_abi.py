@@ -34,6 +34,7 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     consts = dict(re.findall(r"#define (QMM_[A-Z0-9_]+) \(?(-?\d+)\)?", text))
     assert int(consts["QMM_Q4_K"]) == qmm.Q4_K and int(consts["QMM_Q6_K"]) == qmm.Q6_K
+    assert int(consts["QMM_Q4_K_PACKED"]) == qmm.Q4_K_PACKED
     assert int(consts["QMM_EINVAL"]) == qmm.EINVAL and int(consts["QMM_ESHAPE"]) == qmm.ESHAPE
     assert int(consts["QMM_ENOMEM"]) == qmm.ENOMEM and int(consts["QMM_EHIP"]) == qmm.EHIP
     assert int(consts["QMM_TOKEN_PAD"]) == qmm.TOKEN_PAD

@@ -162,12 +162,14 @@ def check_planes(w, type_, raw, od, id_):
         else:
             assert np.array_equal(g[:od], e), f"plane {k} differs"
         assert not g[od:].view(np.uint8).any(), f"plane {k}: padding rows not zero"
-    if type_ == synth.Q4_K:
+    if type_ != synth.Q6_K:
         assert w.dm_offset == w.plane_bytes
 
 
 @pytest.mark.parametrize("type_,od,id_,full", [(synth.Q6_K, 5, 512, False), (synth.Q6_K, 130, 768, True),
-                                               (synth.Q4_K, 37, 512, False), (synth.Q4_K, 129, 1024, False)])
+                                               (synth.Q4_K, 37, 512, False), (synth.Q4_K, 129, 1024, False),
+                                               (synth.Q4_K_PACKED, 37, 512, False),
+                                               (synth.Q4_K_PACKED, 129, 1024, False)])
 def test_planes_byte_exact(type_, od, id_, full):
     say(f"planes type={type_} od={od} id={id_}")
     rng = np.random.default_rng(od)
@@ -184,7 +186,7 @@ def _set_f16(raw, lo, bits):
     raw[:, lo:lo + 2] = np.asarray(bits, np.uint16).astype("<u2").view(np.uint8).reshape(nb, 2)
 
 
-@pytest.mark.parametrize("type_", [synth.Q4_K, synth.Q6_K], ids=["q4_K", "q6_K"])
+@pytest.mark.parametrize("type_", [synth.Q4_K, synth.Q6_K, synth.Q4_K_PACKED], ids=["q4_K", "q6_K", "q4_K packed"])
 def test_extreme_block_scales(type_):
     """Super-block scales of either sign, huge (60000) and subnormal (2^-24):
     the planes stay byte-exact and the MMQ stays within the tolerance.  Blocks
@@ -192,10 +194,10 @@ def test_extreme_block_scales(type_):
     od, id_, T = 90, 1024, 70
     say(f"extreme block scales {synth.TYPE_NAMES[type_]}")
     rng = np.random.default_rng(9)
-    bb = 144 if type_ == synth.Q4_K else 210
+    bb = synth.BLOCK_BYTES[type_]
     raw = synth.weights(rng, type_, od, id_).reshape(-1, bb).copy()
     nb = raw.shape[0]
-    fields = [0, 2] if type_ == synth.Q4_K else [208]
+    fields = [0, 2] if type_ != synth.Q6_K else [208]
     for lo in fields:
         bits = raw[:, lo:lo + 2].copy().view("<u2").reshape(-1)
         pick = rng.random(nb)
@@ -210,7 +212,7 @@ def test_extreme_block_scales(type_):
     qact = gpu_quantize(x)
     q, dh, s = check_prepass(x, qact)
     out = run_mmq(w, qact, T)
-    ref, A = oracle.mmq(type_, raw, od, id_, q, dh, s)
+    ref, A = oracle.mmq(synth.block_format(type_), raw, od, id_, q, dh, s)
     check_close(out, ref, A, "extreme block scales")
     w.release()
 
@@ -222,8 +224,9 @@ WIDE = [("few-tile 96x2048 T=70", 96, 2048, 70), ("many-tile 1030x1024 T=4000", 
         ("ragged tail 4160x1024 T=512", 4160, 1024, 512), ("all split 512x3072 T=300", 512, 3072, 300)]
 
 
+@pytest.mark.parametrize("type_", [synth.Q4_K, synth.Q4_K_PACKED], ids=["q4_K", "q4_K packed"])
 @pytest.mark.parametrize("case", WIDE, ids=[c[0] for c in WIDE])
-def test_q4k_wide_scale_range_rows(case):
+def test_q4k_wide_scale_range_rows(case, type_):
     """q4_K rows whose super-block scales span the whole f16 range: super-block
     0 of every row has d = 60000 (and dmin = 60000 on a third of the rows), the
     others d = k * 2^-24 for k in [1, 1023] (subnormal) and dmin either tiny
@@ -233,7 +236,7 @@ def test_q4k_wide_scale_range_rows(case):
     of its terms' magnitudes -- which a scale stored relative to the row's
     largest value cannot do."""
     name, od, id_, T = case
-    say(f"q4_K wide scale range {name}")
+    say(f"{synth.TYPE_NAMES[type_]} wide scale range {name}")
     rng = np.random.default_rng(31)
     nsb = id_ // 256
     raw = synth.q4k_weights(rng, od, id_).reshape(od, nsb, 144).copy()
@@ -252,8 +255,8 @@ def test_q4k_wide_scale_range_rows(case):
         keep = x[t, 256 * one[t]: 256 * one[t] + 256].copy()
         x[t] = 0.0
         x[t, 256 * one[t]: 256 * one[t] + 256] = keep
-    w = qmm.register_weights(synth.Q4_K, od, id_, raw)
-    check_planes(w, synth.Q4_K, raw, od, id_)
+    w = qmm.register_weights(type_, od, id_, raw)
+    check_planes(w, type_, raw, od, id_)
     qact = gpu_quantize(x)
     q, dh, s = check_prepass(x, qact)
     got = run_mmq(w, qact, T)
@@ -272,7 +275,7 @@ def _int_acts(rng, T, id_):
     return x
 
 
-@pytest.mark.parametrize("type_", [synth.Q6_K, synth.Q4_K])
+@pytest.mark.parametrize("type_", [synth.Q6_K, synth.Q4_K, synth.Q4_K_PACKED])
 def test_int_dots_exact_unit_scale(type_):
     od, id_, T = 200, 512, 77
     say(f"int dots unit type={type_} od={od} T={T}")
@@ -297,12 +300,12 @@ def test_int_dots_exact_unit_scale(type_):
     q, dh, s = check_prepass(x, qact)
     assert np.all(dh == 0x3C00)
     got = run_mmq(w, qact, T)
-    ref, _ = oracle.mmq(type_, raw, od, id_, q, dh, s)
+    ref, _ = oracle.mmq(synth.block_format(type_), raw, od, id_, q, dh, s)
     assert np.all(np.abs(ref) < 2 ** 24)
     assert np.array_equal(got.astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("type_", [synth.Q6_K, synth.Q4_K])
+@pytest.mark.parametrize("type_", [synth.Q6_K, synth.Q4_K, synth.Q4_K_PACKED])
 def test_int_dots_exact_full_range_one_chunk(type_):
     """Full-range scales; each token is non-zero in one 32-block only, so every
     output equals one scale-folded block dot J exactly."""
@@ -368,7 +371,11 @@ SMALL = [("q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          # token tile (1094 row tiles)
          ("q4_K 70000x256 T=1", synth.Q4_K, 70000, 256, 1, False),
          ("q6_K 70001x256 T=1", synth.Q6_K, 70001, 256, 1, True),
-         ("q4_K 1030x256 T=4000", synth.Q4_K, 1030, 256, 4000, False)]
+         ("q4_K 1030x256 T=4000", synth.Q4_K, 1030, 256, 4000, False),
+         # the packed-code registration: few tiles, a ragged split tail, many tiles
+         ("q4_K packed 300x768 T=77", synth.Q4_K_PACKED, 300, 768, 77, True),
+         ("q4_K packed 4160x1024 T=512", synth.Q4_K_PACKED, 4160, 1024, 512, False),
+         ("q4_K packed 1030x256 T=4000", synth.Q4_K_PACKED, 1030, 256, 4000, False)]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
@@ -380,12 +387,12 @@ def test_small_all_elements(case):
     qact = gpu_quantize(x)
     q, dh, s = check_prepass(x, qact)
     got = run_mmq(w, qact, T)
-    ref, A = oracle.mmq(type_, raw, od, id_, q, dh, s)
+    ref, A = oracle.mmq(synth.block_format(type_), raw, od, id_, q, dh, s)
     check_close(got, ref, A, name)
 
 
 @pytest.mark.parametrize("geometry", ["few", "many"])
-@pytest.mark.parametrize("type_", [synth.Q4_K, synth.Q6_K], ids=["q4_K", "q6_K"])
+@pytest.mark.parametrize("type_", [synth.Q4_K, synth.Q6_K, synth.Q4_K_PACKED], ids=["q4_K", "q6_K", "q4_K packed"])
 def test_subnormal_activation_scales(type_, geometry):
     """Activation scales that are f16 subnormals (amax below 127 * 2^-14) reach
     the matrix core (q4_K's scale outer product and min term take dh and s as
@@ -408,7 +415,7 @@ def test_subnormal_activation_scales(type_, geometry):
     assert np.any((d16 > 0) & (d16 < 2.0 ** -14)), "no subnormal scale in the input"
     w = qmm.register_weights(type_, od, id_, raw)
     got = run_mmq(w, qact, T)
-    ref, A = oracle.mmq(type_, raw, od, id_, q, dh, s)
+    ref, A = oracle.mmq(synth.block_format(type_), raw, od, id_, q, dh, s)
     check_close(got, ref, A, f"subnormal scales {geometry}")
     w.release()
 
@@ -461,7 +468,10 @@ LAYER = [(f"layer {synth.TYPE_NAMES[t]} {od}x{id_} T={synth.LAYER_TOKENS}", t, o
 SHARDS = [("q6_K ffn_down column shard 512x11008 T=512", synth.Q6_K, 512, 11008, 512, False),
           ("q6_K ffn_down row shard 4096x1536 T=512", synth.Q6_K, 4096, 1536, 512, False),
           ("q4_K ffn_gate column shard 1376x4096 T=512", synth.Q4_K, 1376, 4096, 512, False)]
-FULL = [synth.FFN_DOWN, synth.FFN_DOWN_ODD, synth.ATTN, synth.GATE_UP, synth.HEAD] + LAYER + SHARDS
+# the q4_K shapes registered with packed codes
+PACKED = [(c[0].replace("q4_K", "q4_K packed"), synth.Q4_K_PACKED) + tuple(c[2:])
+          for c in [synth.ATTN, synth.GATE_UP] + LAYER if c[1] == synth.Q4_K]
+FULL = [synth.FFN_DOWN, synth.FFN_DOWN_ODD, synth.ATTN, synth.GATE_UP, synth.HEAD] + LAYER + SHARDS + PACKED
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=[c[0] for c in FULL])
@@ -482,13 +492,30 @@ def test_full_size_all_elements(cfg):
     got = run_mmq(w, qact, T)
     w.release()
     say(f"full size {name}: oracle on {T * od} elements")
-    ref, A = oracle.mmq_parallel(type_, raw, od, id_, q, dh, s)
+    ref, A = oracle.mmq_parallel(synth.block_format(type_), raw, od, id_, q, dh, s)
     check_close(got, ref, A, name)
 
 
 # --------------------------------------------------------------------------
 # properties
 # --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("od,id_,T", [(300, 768, 77), (4160, 1024, 512), (1030, 256, 4000), (512, 3072, 300)])
+def test_packed_codes_bit_identical_to_byte_codes(od, id_, T):
+    """The packed-code registration feeds the matrix cores the same code bytes,
+    so its results equal the byte-code registration's bit for bit (both tile
+    geometries, a ragged split tail, an all-split launch)."""
+    say(f"packed vs byte codes {od}x{id_} T={T}")
+    raw, x = synth.case(synth.Q4_K, od, id_, T, seed=8)
+    qact = gpu_quantize(x)
+    w = qmm.register_weights(synth.Q4_K, od, id_, raw)
+    wp = qmm.register_weights(synth.Q4_K_PACKED, od, id_, raw)
+    assert wp.plane_bytes < w.plane_bytes
+    a, b = run_mmq(w, qact, T), run_mmq(wp, qact, T)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    w.release()
+    wp.release()
+
 
 def test_odd_rows_and_token_tail_are_prefixes_and_repeatable():
     name, type_, od, id_, T, _ = synth.FFN_DOWN
@@ -581,7 +608,7 @@ def test_tail_scratch_shared_across_shapes():
         qact = gpu_quantize(x)
         first = run_mmq(w, qact, T)
         q, dh, sm = oracle.quantize(x)
-        ref, A = oracle.mmq(type_, raw, od, id_, q, dh, sm)
+        ref, A = oracle.mmq(synth.block_format(type_), raw, od, id_, q, dh, sm)
         check_close(first, ref, A, f"type {type_} od {od} T {T}")
         runs.append((w, qact, T, od, first))
     for _ in range(3):
