@@ -17,9 +17,9 @@ struct Planes {
   int64_t nsb;       // id / 256
   int64_t nchunk;    // id / 32
   int8_t* wq;        // weight fragments in MFMA order: q6_K folded hi/lo, q4_K codes
-  float* wd;         // q6_K: d per (row, super-block); q4_K: the row's 2^-e
-  uint16_t* wmn;     // q4_K: -dmin*min*2^e per (row, chunk) as f16 hi + lo; else nullptr
-  uint16_t* wsc;     // q4_K: d*sc*2^e per (row, chunk) as f16 hi + lo; else nullptr
+  float* wd;         // q6_K: d per (row, super-block); q4_K: d*2^25 and -dmin per (row, super-block)
+  uint16_t* wmn;     // q4_K: the 6-bit min per (row, chunk) as an f16 integer; else nullptr
+  uint16_t* wsc;     // q4_K: the 6-bit scale per (row, chunk) as an f16 integer; else nullptr
 };
 
 constexpr int kRowPad = 128;     // weight rows are padded to a multiple of this

@@ -12,6 +12,7 @@ Word/byte stride mistakes in block and plane indexing are the bugs these guard
 against.  Neither build is the product: both live in a temporary directory.
 """
 import glob
+import importlib.util
 import os
 import subprocess
 import sys
@@ -83,7 +84,10 @@ def test_library_validation_paths_under_asan_and_ubsan(tmp_path):
     runtime = _clang_asan()
     if runtime is None or not os.path.exists(HIPCC):
         pytest.skip("hipcc or clang's AddressSanitizer runtime is not installed")
-    csrc = os.path.join(ROOT, "quant_q8_gemm_amd", "csrc")
+    # the library's own source list (the build module, loaded without importing the package)
+    spec = importlib.util.spec_from_file_location("qmm_build", os.path.join(ROOT, "quant_q8_gemm_amd", "_build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
     lib = str(tmp_path / "libqmm_san.so")
     # the sanitizers go to the host compilation only (each right after -Xarch_host)
     cmd = [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-shared",
@@ -91,7 +95,7 @@ def test_library_validation_paths_under_asan_and_ubsan(tmp_path):
            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
            "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(csrc, f) for f in ("qmm_api.cpp", "qmm_repack.hip", "qmm_prepass.hip", "qmm_mmq.hip")],
+           *build.SOURCES,
            "-o", lib]
     b = subprocess.run(cmd, capture_output=True, text=True)
     assert b.returncode == 0, b.stderr[-3000:]
