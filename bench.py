@@ -164,11 +164,13 @@ def measured_traffic(workload: str):
 
 
 def calibrate(torch, stream):
-    """Measured roofs on this GPU: the int8 MFMA rate and the vector-ALU rates of
+    """Measured roofs on this GPU: the int8 MFMA rate, the vector-ALU rates of
     the MMQ's scale epilogues (q6_K 3 and q4_K 2.25 instructions per (token,
-    row, 32-block), 64 int8 ops each), from the calibration kernels in libqmm_peak.so, with the shader
-    clock (s_memtime against the 100 MHz s_memrealtime) during each run.  Each
-    is the best over a few occupancies, timed with HIP events on `stream`."""
+    row, 32-block), 64 int8 ops each), the rates of the MMQ's whole chunk
+    steps without their memory traffic, and MFMAs with and without independent
+    FMAs beside them; from the calibration kernels in libqmm_peak.so, with the
+    shader clock (s_memtime against the 100 MHz s_memrealtime) during each run.
+    Each is the best over a few occupancies, timed with HIP events on `stream`."""
     import ctypes
     path = os.path.join(ROOT, "quant_q8_gemm_amd", "libqmm_peak.so")
     lib = ctypes.CDLL(path)
@@ -181,7 +183,11 @@ def calibrate(torch, stream):
     # kind, name, work-groups per CU tried, SIMD cycles per wave-iteration, int8 ops per wave-iteration
     for kind, name, per_cu, cyc, ops_it in ((0, "mfma_i8", (1, 2, 3), 128, 4 * 65536),
                                             (1, "epilogue_valu", (2, 4, 8), 192, 65536),
-                                            (2, "epilogue_valu_q4k", (2, 4, 8), 1152, 8 * 65536)):
+                                            (2, "epilogue_valu_q4k", (2, 4, 8), 1152, 8 * 65536),
+                                            (3, "chunk_q4k", (2, 4), 1600, 8 * 65536),
+                                            (4, "chunk_q6k", (2, 4), 1700, 8 * 65536),
+                                            (5, "mfma_with_fma", (1, 2, 3), 256, 4 * 65536),
+                                            (6, "fma_only", (1, 2, 3), 128, 0)):
         best = None
         for g in per_cu:
             grid = g * n_cu
@@ -203,16 +209,30 @@ def calibrate(torch, stream):
             t = float(np.median(times))
             cycles, ticks = (int(v) for v in clk.cpu())
             tops = grid * 4 * iters * ops_it / t / 1e12
+            ghz = cycles / (ticks / 100e6) / 1e9 if ticks > 0 else None
             rec = {"tops": round(tops, 1), "work_groups_per_cu": g, "ms": round(t * 1e3, 3),
-                   "clock_ghz": round(cycles / (ticks / 100e6) / 1e9, 3) if ticks > 0 else None}
-            if best is None or tops > best["tops"]:
-                best = rec
+                   "clock_ghz": round(ghz, 3) if ghz else None}
+            if ghz:  # SIMD cycles per wave-iteration: the launch's SIMD cycles over its wave-iterations
+                rec["simd_cycles_per_iteration"] = round(t * ghz * 1e9 * 4 * n_cu / (grid * 4 * iters), 1)
+            rate = tops if ops_it else -rec.get("simd_cycles_per_iteration", t)
+            if best is None or rate > best["_rate"]:
+                best = dict(rec, _rate=rate)
+        best.pop("_rate")
+        if not ops_it:
+            best.pop("tops")
         out[name] = best
     mf = out["mfma_i8"]
     mf["pct_of_spec"] = round(100 * mf["tops"] / MFMA_INT8_PEAK_TOPS, 1)
     if mf["clock_ghz"]:
         # 8192 int8 ops per clock per CU (4 SIMDs x 32x32x32 MAC x 2 / 32 cycles)
         mf["spec_at_clock_tops"] = round(n_cu * mf["clock_ghz"] * 1e9 * 8192 / 1e12, 1)
+    # do the matrix core and the vector ALU overlap?  Cycles per wave-iteration
+    # of 4 MFMAs alone, 64 FMAs alone, and both: overlap 1 means the longer of
+    # the two, 0 their sum
+    c = [out[k].get("simd_cycles_per_iteration") for k in ("mfma_i8", "fma_only", "mfma_with_fma")]
+    if all(c):
+        out["mfma_valu_overlap"] = {"mfma_cycles": c[0], "fma_cycles": c[1], "both_cycles": c[2],
+                                    "overlap": round((c[0] + c[1] - c[2]) / min(c[0], c[1]), 3)}
     return out
 
 
@@ -499,6 +519,18 @@ def main():
             epi_measured = epilogue_roof(gemms, T, measured.get)
             rl["epilogue_roof"]["measured"] = round(epi_measured, 1)
             rl["epilogue_roof"]["frac_of_measured"] = round(mmq_tops / epi_measured, 4)
+            # the MMQ's own chunk step (MFMAs, LDS operand reads, vector
+            # epilogue) without its global copies and barriers: on this GPU the
+            # matrix core's and the vector ALU's times add (mfma_valu_overlap),
+            # so this, not the epilogue alone, is the compute ceiling of the
+            # kernel's instruction mix.  The packed registration takes q4_K's
+            # (its unpack is not in it: a higher roof, a lower fraction).
+            chunk = {synth.Q6_K: cal["chunk_q6k"]["tops"], synth.Q4_K: cal["chunk_q4k"]["tops"],
+                     synth.Q4_K_PACKED: cal["chunk_q4k"]["tops"]}
+            chunk_roof = epilogue_roof(gemms, T, chunk.get)
+            rl["chunk_roof"] = {"bound": "mfma+alu", "measured": round(chunk_roof, 1),
+                                "unit": "TOP/s (int8-equivalent)",
+                                "frac_of_measured": round(mmq_tops / chunk_roof, 4)}
     if not args.no_cpu:
         threads, rule = cpu_threads(args.cpu_threads)
         result["cpu_baseline"] = cpu_baseline(gemms, raws, xs, T, threads, args.cpu_macs)

@@ -170,7 +170,7 @@ def test_calibration_library_loads_and_validates():
     f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_void_p]
     good = ctypes.c_void_p(4096)
-    assert f(3, 10, 1, good, good, None) == 1
+    assert f(7, 10, 1, good, good, None) == 1
     assert f(-1, 10, 1, good, good, None) == 1
     assert f(0, 0, 1, good, good, None) == 1
     assert f(1, 10, 0, good, good, None) == 1

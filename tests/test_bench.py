@@ -47,3 +47,9 @@ def test_bench_json_line_contract():
     cal = d["calibration"]
     assert cal["mfma_i8"]["tops"] > 0 and cal["epilogue_valu"]["tops"] > 0
     assert cal["epilogue_valu_q4k"]["tops"] > 0 and rl["epilogue_roof"]["measured"] > 0
+    # the chunk-step ceilings: below the MFMA peak, and the kernel below them
+    assert 0 < cal["chunk_q4k"]["tops"] < cal["mfma_i8"]["tops"]
+    assert 0 < cal["chunk_q6k"]["tops"] < cal["mfma_i8"]["tops"]
+    assert 0 < rl["chunk_roof"]["frac_of_measured"] < 1.05
+    ov = cal["mfma_valu_overlap"]
+    assert ov["both_cycles"] >= max(ov["mfma_cycles"], ov["fma_cycles"]) * 0.95
