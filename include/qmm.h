@@ -222,6 +222,20 @@ int qmm_mmq(const qmm_weights *w, const void *qact, size_t qact_bytes, int64_t n
             float *out, void *stream);
 
 /*
+ * qmm_stream_release -- give back the device memory qmm_mmq keeps for `stream`
+ * (the tail-partials scratch above, on every device it was allocated for), for
+ * callers that create and destroy streams: call it before destroying the
+ * stream.  It synchronizes `stream` first (an MMQ on it may still read the
+ * partials), then frees; a later qmm_mmq on the same stream allocates again.
+ *   freed_bytes  NULL, or receives the bytes freed (0 if the stream held none).
+ * A stream that holds nothing returns QMM_OK without any HIP call.  Not safe
+ * concurrently with a qmm_mmq on the same stream from another thread.
+ * Errors: QMM_EHIP (the stream's synchronization or the free failed; what was
+ * not freed stays held and *freed_bytes counts what was).
+ */
+int qmm_stream_release(void *stream, size_t *freed_bytes);
+
+/*
  * qmm_mmq_noalloc -- qmm_mmq for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation.  Same arguments, validation, kernels and results (bit for bit)

@@ -46,7 +46,7 @@ BLOCK_BYTES = {Q4_K: 144, Q4_K_PACKED: 144, Q6_K: 210}
 # The full list of entry points include/qmm.h declares.
 EXPORTS = ("qmm_register_weights", "qmm_weights_info", "qmm_weights_export", "qmm_release_weights",
            "qmm_set_memory_cap", "qmm_qact_bytes", "qmm_quantize_activations", "qmm_mmq",
-           "qmm_mmq_noalloc", "qmm_last_error")
+           "qmm_mmq_noalloc", "qmm_stream_release", "qmm_last_error")
 
 
 class Info(ctypes.Structure):
@@ -78,6 +78,8 @@ _lib.qmm_mmq.argtypes = [_P, _P, _SZ, _I64, _P, _P]
 _lib.qmm_mmq.restype = ctypes.c_int
 _lib.qmm_mmq_noalloc.argtypes = [_P, _P, _SZ, _I64, _P, _P]
 _lib.qmm_mmq_noalloc.restype = ctypes.c_int
+_lib.qmm_stream_release.argtypes = [_P, ctypes.POINTER(_SZ)]
+_lib.qmm_stream_release.restype = ctypes.c_int
 _lib.qmm_last_error.argtypes = []
 _lib.qmm_last_error.restype = ctypes.c_char_p
 
@@ -218,3 +220,11 @@ def mmq_noalloc(w: Weights, qact, n_tok: int, out, stream=None):
     _check(_lib.qmm_mmq_noalloc(ctypes.c_void_p(w.handle), ctypes.c_void_p(qact.data_ptr()), qact.numel(),
                                 int(n_tok), ctypes.c_void_p(out.data_ptr()), _stream(stream)))
     return out
+
+
+def stream_release(stream=None) -> int:
+    """Free the MMQ scratch the library keeps for `stream` (torch's current
+    stream if None); synchronizes the stream first.  Returns the bytes freed."""
+    freed = _SZ(0)
+    _check(_lib.qmm_stream_release(_stream(stream), ctypes.byref(freed)))
+    return int(freed.value)

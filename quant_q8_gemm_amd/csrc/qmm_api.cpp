@@ -34,12 +34,13 @@ std::atomic<size_t> g_cap{0};   // 0 = no cap
 
 // Scratch for the MMQ's tail partials: one buffer per (device, stream), of the
 // largest size any call can need on that device (64 KiB per compute unit).
-// Calls on one stream run in order, so they share it; it lives until the
-// process ends.
+// Calls on one stream run in order, so they share it; it lives until
+// qmm_stream_release(stream) or the process ends.
 struct Scratch {
   int device;
   hipStream_t stream;
   void* ptr;
+  size_t bytes;
 };
 std::mutex g_scratch_mu;
 std::vector<Scratch> g_scratch;
@@ -329,12 +330,42 @@ int qmm_mmq(const qmm_weights* w, const void* qact, size_t qact_bytes, int64_t n
                    ? fail(QMM_ENOMEM, "hipMalloc(%zu) for the tail partials failed", max_bytes)
                    : fail_hip(e, "hipMalloc(tail partials)");
       }
-      g_scratch.push_back({device, s, scratch});
+      g_scratch.push_back({device, s, scratch, max_bytes});
     }
   }
   hipError_t e = qmm::launch_mmq(w->p, plan, (const uint8_t*)qact, n_tok, token_pad(n_tok), out,
                                  (float*)scratch, s);
   if (e != hipSuccess) return fail_hip(e, "mmq launch");
+  ok();
+  return QMM_OK;
+}
+
+int qmm_stream_release(void* stream, size_t* freed_bytes) {
+  const hipStream_t s = (hipStream_t)stream;
+  if (freed_bytes != nullptr) *freed_bytes = 0;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  bool synced = false;
+  int cur = -1;
+  for (size_t i = 0; i < g_scratch.size();) {
+    if (g_scratch[i].stream != s) {
+      ++i;
+      continue;
+    }
+    // ---- first HIP call below this line (none when the stream holds nothing) ----
+    hipError_t e;
+    if (!synced) {  // the stream's MMQs may still read the partials
+      if ((e = hipStreamSynchronize(s)) != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+      if ((e = hipGetDevice(&cur)) != hipSuccess) return fail_hip(e, "hipGetDevice");
+      synced = true;
+    }
+    if ((e = hipSetDevice(g_scratch[i].device)) != hipSuccess) return fail_hip(e, "hipSetDevice");
+    e = hipFree(g_scratch[i].ptr);
+    const hipError_t e2 = hipSetDevice(cur);
+    if (e != hipSuccess) return fail_hip(e, "hipFree(tail partials)");
+    if (e2 != hipSuccess) return fail_hip(e2, "hipSetDevice(restore)");
+    if (freed_bytes != nullptr) *freed_bytes += g_scratch[i].bytes;
+    g_scratch.erase(g_scratch.begin() + (ptrdiff_t)i);
+  }
   ok();
   return QMM_OK;
 }

@@ -28,6 +28,7 @@ def main(path):
     L.qmm_quantize_activations.argtypes = [P, I64, I64, P, SZ, P]
     L.qmm_mmq.argtypes = [P, P, SZ, I64, P, P]
     L.qmm_mmq_noalloc.argtypes = [P, P, SZ, I64, P, P]
+    L.qmm_stream_release.argtypes = [P, P]
     L.qmm_last_error.restype = ctypes.c_char_p
     bad = []
 
@@ -73,6 +74,10 @@ def main(path):
     expect("info null", L.qmm_weights_info(None, good), EINVAL)
     expect("export null", L.qmm_weights_export(None, good, 10), EINVAL)
     L.qmm_release_weights(None)
+    # a stream that holds no scratch: nothing to free, no HIP call
+    expect("stream release, nothing held", L.qmm_stream_release(good, good), 0)
+    expect("stream release, freed count", ctypes.cast(good, ctypes.POINTER(SZ))[0], 0)
+    expect("stream release, null stream", L.qmm_stream_release(None, None), 0)
     if bad:
         print("\n".join(bad))
         return 1

@@ -185,3 +185,12 @@ def test_binding_rejects_wrong_qact_tensors():
         qmm._check_qact(torch.zeros(16, dtype=torch.float32))
     with pytest.raises(qmm.QmmError):
         qmm._check_qact(torch.zeros(16, dtype=torch.uint8))  # host memory
+
+
+def test_stream_release_of_a_stream_without_scratch_is_a_no_op():
+    """No scratch was allocated for these streams: the call returns QMM_OK
+    before any HIP call (so it works without a GPU)."""
+    freed = ctypes.c_size_t(7)
+    assert qmm._lib.qmm_stream_release(ctypes.c_void_p(0x1234), ctypes.byref(freed)) == 0
+    assert freed.value == 0
+    assert qmm._lib.qmm_stream_release(None, None) == 0

@@ -353,8 +353,10 @@ SMALL = [("q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          ("q6_K 70x256 T=33", synth.Q6_K, 70, 256, 33, True),
          ("q6_K 33x2304 T=130", synth.Q6_K, 33, 2304, 130, False),
          ("q4_K 520x1536 T=257", synth.Q4_K, 520, 1536, 257, False),
-         # a ragged last wave on 256 CUs (264 tiles of 64 x 128 each): the
-         # tail tiles are split along K and added by the fixup kernel
+         # a ragged last wave on 256 CUs (260 tiles of 64 x 128 each): the
+         # tail tiles are split along K (4 super-blocks: 2 slices) and added by
+         # the fixup kernel; with 3 super-blocks (4200x768, 264 tiles) the two
+         # k-groups leave no room to split, and the tail runs whole
          ("q4_K 4160x1024 T=512", synth.Q4_K, 4160, 1024, 512, False),
          ("q6_K 4200x768 T=500", synth.Q6_K, 4200, 768, 500, True),
          # far fewer tiles than CUs (24): every tile split along K
@@ -594,12 +596,12 @@ def test_concurrent_streams_share_a_handle():
 
 
 def test_tail_scratch_shared_across_shapes():
-    """Launches with different tail tile counts and splits (264 tiles on 256
-    CUs, 24 tiles all split, a q4_K shape with its own geometry) share one
-    stream's tail scratch in turn: each repeat gives its first result bit for
-    bit, which agrees with the oracle."""
+    """Launches with different tail tile counts and splits (260 tiles on 256
+    CUs with the tail split 4 ways, 24 tiles all split, a q4_K shape with its
+    own geometry) share one stream's tail scratch in turn: each repeat gives
+    its first result bit for bit, which agrees with the oracle."""
     say("tail scratch across shapes")
-    cases = [(synth.Q6_K, 4200, 768, 500, 21), (synth.Q6_K, 512, 2816, 300, 22),
+    cases = [(synth.Q6_K, 4097, 2048, 509, 21), (synth.Q6_K, 512, 2816, 300, 22),
              (synth.Q4_K, 4160, 1024, 512, 23)]
     runs = []
     for type_, od, id_, T, seed in cases:
@@ -616,6 +618,32 @@ def test_tail_scratch_shared_across_shapes():
             assert np.array_equal(run_mmq(w, qact, T), first)
     for w, *_ in runs:
         w.release()
+
+
+def test_stream_release_frees_the_scratch():
+    """qmm_stream_release gives a stream's tail scratch back (64 KiB per CU,
+    counted by the call), and a later MMQ on the same stream allocates it again
+    and gives the same bits; a stream that holds nothing releases nothing."""
+    say("stream release")
+    type_, od, id_, T = synth.Q6_K, 4097, 2048, 509  # 260 tiles on 256 CUs: the tail splits 4 ways
+    raw, x = synth.case(type_, od, id_, T, seed=31)
+    w = qmm.register_weights(type_, od, id_, raw)
+    qact = gpu_quantize(x)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = torch.empty((T, od), dtype=torch.float32, device="cuda")
+        qmm.mmq(w, qact, T, out=out, stream=s)
+    s.synchronize()
+    first = out.cpu().numpy()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert qmm.stream_release(s) == n_cu * 64 * 1024
+    assert qmm.stream_release(s) == 0                          # nothing left
+    with torch.cuda.stream(s):
+        qmm.mmq(w, qact, T, out=out, stream=s)
+    s.synchronize()
+    assert np.array_equal(out.cpu().numpy(), first)
+    assert qmm.stream_release(s) == n_cu * 64 * 1024
+    w.release()
 
 
 def test_writes_stay_inside_output():
