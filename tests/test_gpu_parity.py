@@ -361,8 +361,8 @@ SMALL = [("q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          ("q6_K 4200x768 T=500", synth.Q6_K, 4200, 768, 500, True),
          # far fewer tiles than CUs (24): every tile split along K
          ("q6_K 512x2816 T=300", synth.Q6_K, 512, 2816, 300, False),
-         # the same for q4_K: partials of the row-scaled accumulators, unscaled
-         # before the fixup adds them
+         # the same for q4_K (its d and dmin applied per super-block before the
+         # partials leave a slice)
          ("q4_K 512x3072 T=300", synth.Q4_K, 512, 3072, 300, True),
          # enough 64 x 64 tiles (>= 1024) to select the many-tile geometry;
          # q6_K there runs 64 x 128 tiles two per CU: 528 tiles on 512 slots
