@@ -473,7 +473,14 @@ SHARDS = [("q6_K ffn_down column shard 512x11008 T=512", synth.Q6_K, 512, 11008,
 # the q4_K shapes registered with packed codes
 PACKED = [(c[0].replace("q4_K", "q4_K packed"), synth.Q4_K_PACKED) + tuple(c[2:])
           for c in [synth.ATTN, synth.GATE_UP] + LAYER if c[1] == synth.Q4_K]
-FULL = [synth.FFN_DOWN, synth.FFN_DOWN_ODD, synth.ATTN, synth.GATE_UP, synth.HEAD] + LAYER + SHARDS + PACKED
+# LLaMA-13B widths (hidden 5120, FFN 13824): other super-block counts (20 and 54 per
+# row), other tile counts and odd token counts, in both types and both registrations
+WIDER = [("13B attn q4_K 5120x5120 T=777", synth.Q4_K, 5120, 5120, 777, False),
+         ("13B gate q4_K 13824x5120 T=1001", synth.Q4_K, 13824, 5120, 1001, True),
+         ("13B down q6_K 5120x13824 T=301", synth.Q6_K, 5120, 13824, 301, False),
+         ("13B v q6_K 5120x5120 T=2049", synth.Q6_K, 5120, 5120, 2049, True),
+         ("13B attn q4_K packed 5120x5120 T=777", synth.Q4_K_PACKED, 5120, 5120, 777, False)]
+FULL = [synth.FFN_DOWN, synth.FFN_DOWN_ODD, synth.ATTN, synth.GATE_UP, synth.HEAD] + LAYER + SHARDS + PACKED + WIDER
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=[c[0] for c in FULL])
@@ -482,7 +489,8 @@ def test_full_size_all_elements(cfg):
     the benchmark times, against the oracle (its rows split over the host's
     CPUs): ffn_down (also 4097 rows at 509 tokens), both attention/FFN q4_K
     shapes, the 2048-token output head, the four GEMM shapes of the 3314-token
-    layer, and the tensor-parallel shards."""
+    layer, the tensor-parallel shards, the packed-code q4_K shapes and five
+    13B-width shapes."""
     name, type_, od, id_, T, outl = cfg
     say(f"full size {name}: generating")
     raw, x = synth.case(type_, od, id_, T, seed=0, outliers=outl)
