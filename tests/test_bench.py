@@ -53,3 +53,24 @@ def test_bench_json_line_contract():
     assert 0 < rl["chunk_roof"]["frac_of_measured"] < 1.05
     ov = cal["mfma_valu_overlap"]
     assert ov["both_cycles"] >= max(ov["mfma_cycles"], ov["fma_cycles"]) * 0.95
+
+
+def test_step_roof_weights_each_gemm_by_its_ops():
+    """The roof of a step of several GEMMs (epilogue and chunk-step roofs) is
+    its total ops over the sum of each GEMM's time at its own type's roof: a
+    harmonic mean weighted by ops, checked on hand-computed cases (CPU)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import synth
+    g = [("a", synth.Q4_K, 4096, 4096, "x"), ("b", synth.Q6_K, 4096, 11008, "y")]
+    roofs = {synth.Q4_K: 1000.0, synth.Q6_K: 500.0}
+    ops = [2.0 * 64 * 4096 * 4096, 2.0 * 64 * 4096 * 11008]
+    want = sum(ops) / (ops[0] / 1000.0 + ops[1] / 500.0)
+    assert abs(bench.epilogue_roof(g, 64, roofs.get) - want) < 1e-9 * want
+    # one GEMM: its own roof; equal roofs: that roof
+    assert bench.epilogue_roof(g[:1], 64, roofs.get) == 1000.0
+    assert abs(bench.epilogue_roof(g, 64, lambda t: 700.0) - 700.0) < 1e-9
+    # the nominal vector-ALU roofs: 256 CUs x 64 lanes x 2.4 GHz lane-instructions,
+    # 64 int8 ops per (token, row, 32-block), 3 (q6_K) or 2.25 (q4_K) instructions each
+    assert abs(bench.nominal_epilogue_tops(synth.Q6_K) - 256 * 64 * 2.4e9 * 64 / 3 / 1e12) < 1e-9
+    assert abs(bench.nominal_epilogue_tops(synth.Q4_K) - 256 * 64 * 2.4e9 * 64 / 2.25 / 1e12) < 1e-9
