@@ -25,6 +25,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures as cf
 import hashlib
+import importlib.util
 import json
 import os
 import sys
@@ -146,7 +147,13 @@ def _parse():
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """The MMQ kernel's source and the device compiler flags it is built with."""
+    spec = importlib.util.spec_from_file_location("qmm_build", os.path.join(ROOT, "quant_q8_gemm_amd", "_build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
+    h = hashlib.sha256(open(KERNEL_SRC, "rb").read())
+    h.update(" ".join(build.LIB_FLAGS).encode())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
@@ -170,12 +177,16 @@ def calibrate(torch, stream):
     steps without their memory traffic, and MFMAs with and without independent
     FMAs beside them; from the calibration kernels in libqmm_peak.so, with the
     shader clock (s_memtime against the 100 MHz s_memrealtime) during each run.
-    Each is the best over a few occupancies, timed with HIP events on `stream`."""
+    Each is the best over a few occupancies and over the kernels built with the
+    backend's default and its max-ILP scheduling strategy, timed with HIP
+    events on `stream`."""
     import ctypes
-    path = os.path.join(ROOT, "quant_q8_gemm_amd", "libqmm_peak.so")
-    lib = ctypes.CDLL(path)
-    lib.qmm_peak_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                    ctypes.c_void_p, ctypes.c_void_p]
+    libs = []
+    for so in ("libqmm_peak.so", "libqmm_peak_ilp.so"):  # the two scheduling strategies
+        lib = ctypes.CDLL(os.path.join(ROOT, "quant_q8_gemm_amd", so))
+        lib.qmm_peak_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+        libs.append(lib)
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     clk = torch.zeros(2, dtype=torch.int64, device="cuda")
     sink = torch.empty(8 * n_cu * 256, dtype=torch.int32, device="cuda")
@@ -189,7 +200,8 @@ def calibrate(torch, stream):
                                             (5, "mfma_with_fma", (1, 2, 3), 256, 4 * 65536),
                                             (6, "fma_only", (1, 2, 3), 128, 0)):
         best = None
-        for g in per_cu:
+        for lib_i, g in ((li, g) for li in range(len(libs)) for g in per_cu):
+            lib = libs[lib_i]
             grid = g * n_cu
             iters = int(8e6 / (g * cyc))  # ~4 ms per launch
             def launch():
@@ -211,7 +223,8 @@ def calibrate(torch, stream):
             tops = grid * 4 * iters * ops_it / t / 1e12
             ghz = cycles / (ticks / 100e6) / 1e9 if ticks > 0 else None
             rec = {"tops": round(tops, 1), "work_groups_per_cu": g, "ms": round(t * 1e3, 3),
-                   "clock_ghz": round(ghz, 3) if ghz else None}
+                   "clock_ghz": round(ghz, 3) if ghz else None,
+                   "schedule": ("default", "max-ilp")[lib_i]}
             if ghz:  # SIMD cycles per wave-iteration: the launch's SIMD cycles over its wave-iterations
                 rec["simd_cycles_per_iteration"] = round(t * ghz * 1e9 * 4 * n_cu / (grid * 4 * iters), 1)
             rate = tops if ops_it else -rec.get("simd_cycles_per_iteration", t)

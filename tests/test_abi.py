@@ -161,11 +161,12 @@ def test_info_struct_matches_header():
     assert names == [f[0] for f in qmm.Info._fields_]
 
 
-def test_calibration_library_loads_and_validates():
+@pytest.mark.parametrize("so", ["libqmm_peak.so", "libqmm_peak_ilp.so"])
+def test_calibration_library_loads_and_validates(so):
     """The benchmark's calibration kernels (measured MFMA and epilogue roofs)
-    live in their own library; invalid arguments are refused before any HIP
-    call (hipErrorInvalidValue = 1)."""
-    lib = ctypes.CDLL(os.path.join(ROOT, "quant_q8_gemm_amd", "libqmm_peak.so"))
+    live in their own library, built under two scheduling strategies; invalid
+    arguments are refused before any HIP call (hipErrorInvalidValue = 1)."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "quant_q8_gemm_amd", so))
     f = lib.qmm_peak_launch
     f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_void_p]

@@ -51,6 +51,7 @@ def test_bench_json_line_contract():
     assert 0 < cal["chunk_q4k"]["tops"] < cal["mfma_i8"]["tops"]
     assert 0 < cal["chunk_q6k"]["tops"] < cal["mfma_i8"]["tops"]
     assert 0 < rl["chunk_roof"]["frac_of_measured"] < 1.05
+    assert all(cal[k]["schedule"] in ("default", "max-ilp") for k in ("mfma_i8", "chunk_q4k", "chunk_q6k"))
     ov = cal["mfma_valu_overlap"]
     assert ov["both_cycles"] >= max(ov["mfma_cycles"], ov["fma_cycles"]) * 0.95
 
