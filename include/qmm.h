@@ -82,10 +82,9 @@ typedef struct {
     int64_t od_pad;      /* rows padded with zeros to the row tile */
     size_t raw_bytes;    /* od * (id/256) * (144 or 210): the k-quant bytes */
     size_t plane_bytes;  /* device memory the handle holds */
-    size_t wd_offset;    /* byte offset of the d plane (q4_K: d and -dmin) */
-    size_t mn_offset;    /* byte offset of the min plane (q4_K; else == plane_bytes) */
-    size_t dm_offset;    /* no plane: always == plane_bytes (q4_K's dmin is in the d plane) */
-    size_t sc_offset;    /* byte offset of the f16 scale plane (q4_K; else == plane_bytes) */
+    size_t wd_offset;    /* byte offset of the d plane (q6_K; q4_K: == plane_bytes) */
+    size_t sm_offset;    /* byte offset of the stage-record plane of scales, mins,
+                            d and dmin (q4_K; q6_K: == plane_bytes) */
 } qmm_info;
 
 /*
@@ -131,17 +130,21 @@ int qmm_weights_info(const qmm_weights *w, qmm_info *out);
  *                 (row j, k) in the low nibble (k%16 < 8) or the high nibble
  *                 (k%16 >= 8) of byte (j/32*nchunk + k/32)*512
  *                 + ((k%32)/16)*256 + (j%32)*8 + k%8
- *   the planes below are the same for both q4_K types
- *   at wd_offset  q6_K: f32 [R][nsb][32]: d of (row j, super-block b) at
+ *   at wd_offset  q6_K only: f32 [R][nsb][32]: d of (row j, super-block b) at
  *                 element (j/32*nsb + b)*32 + j%32
- *                 q4_K: f32 [R][nsb][2][32]: d*2^25 (part 0) and -dmin
- *                 (part 1) of (row j, super-block b) at element
- *                 ((j/32*nsb + b)*2 + part)*32 + j%32; both exact in binary32,
- *                 zeros stored as +0
- *   q4_K only, the 6-bit scale and min of (row j, chunk c) as binary16 integers,
- *   each at element ((j/32*nsb + c/8)*2 + (c%8)/4)*128 + (j%32)*4 + c%4 of:
- *   at mn_offset  binary16 [R][nsb][2][32][4]: the mins
- *   at sc_offset  binary16 [R][nsb][2][32][4]: the scales
+ *   at sm_offset  q4_K only (both q4_K types): [R][nchunk/4][1024 bytes], one
+ *                 record per (row block, stage g of chunks 4g..4g+3) at byte
+ *                 (j/32*nchunk/4 + g)*1024, each holding
+ *                 +0    binary16 [32][4]: the 6-bit scale of (row j, chunk
+ *                       4g + i) as an integer at element (j%32)*4 + i
+ *                 +256  binary16 [2][32][4]: the 6-bit min of (row j, chunk
+ *                       8b + 4h + i) of the stage's super-block b = g/2 as an
+ *                       integer at element (h*32 + j%32)*4 + i
+ *                 +768  f32 [2][32]: d*2^25 (part 0) and -dmin (part 1) of
+ *                       (row j, super-block b) at element part*32 + j%32; both
+ *                       exact in binary32, zeros stored as +0
+ *                 (the two records of a super-block both hold its mins, d and
+ *                 dmin)
  * Errors: QMM_EINVAL (null pointers, bytes mismatch), QMM_EHIP.
  */
 int qmm_weights_export(const qmm_weights *w, void *host, size_t bytes);

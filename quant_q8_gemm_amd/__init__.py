@@ -53,8 +53,7 @@ class Info(ctypes.Structure):
     _fields_ = [("type", ctypes.c_int), ("od", ctypes.c_int64), ("id", ctypes.c_int64),
                 ("od_pad", ctypes.c_int64), ("raw_bytes", ctypes.c_size_t),
                 ("plane_bytes", ctypes.c_size_t), ("wd_offset", ctypes.c_size_t),
-                ("mn_offset", ctypes.c_size_t), ("dm_offset", ctypes.c_size_t),
-                ("sc_offset", ctypes.c_size_t)]
+                ("sm_offset", ctypes.c_size_t)]
 
 
 _P = ctypes.c_void_p
@@ -136,9 +135,7 @@ class Weights:
         self.raw_bytes = info.raw_bytes
         self.plane_bytes = info.plane_bytes
         self.wd_offset = info.wd_offset
-        self.mn_offset = info.mn_offset
-        self.dm_offset = info.dm_offset
-        self.sc_offset = info.sc_offset
+        self.sm_offset = info.sm_offset
 
     @property
     def handle(self) -> int:

@@ -20,9 +20,7 @@ struct qmm_weights {
   size_t raw_bytes;
   size_t plane_bytes;
   size_t wd_offset;
-  size_t mn_offset;
-  size_t dm_offset;
-  size_t sc_offset;
+  size_t sm_offset;
   void* alloc;  // one device allocation holding every plane
 };
 
@@ -122,11 +120,10 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   p.od_pad = (int64_t)round_up((size_t)od, qmm::kRowPad);
   p.nsb = id / 256;
   p.nchunk = id / 32;
+  // q6_K: codes, d; q4_K: codes, stage records (one of the last two is empty)
   const size_t off_wd = round_up(qmm::wq_bytes(type, p.od_pad, id), 256);
-  const size_t off_mn = off_wd + round_up(qmm::wd_bytes(type, p.od_pad, id), 256);
-  const size_t off_dm = off_mn + round_up(qmm::wmn_bytes(type, p.od_pad, id), 256);
-  const size_t off_sc = off_dm + round_up(qmm::wdm_bytes(type, p.od_pad, id), 256);
-  const size_t plane_bytes = off_sc + round_up(qmm::wsc_bytes(type, p.od_pad, id), 256);
+  const size_t off_sm = off_wd + round_up(qmm::wd_bytes(type, p.od_pad, id), 256);
+  const size_t plane_bytes = off_sm + round_up(qmm::wsm_bytes(type, p.od_pad, id), 256);
   // reserve the bytes against the cap before allocating, atomically, so that
   // registrations on several threads cannot overshoot it together; every
   // failure below gives them back
@@ -164,9 +161,8 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
                                     : fail_hip(e, "hipMalloc(raw)");
   }
   p.wq = (int8_t*)alloc;
-  p.wd = (float*)((char*)alloc + off_wd);
-  p.wmn = qmm::is_q4k(type) ? (uint16_t*)((char*)alloc + off_mn) : nullptr;
-  p.wsc = qmm::is_q4k(type) ? (uint16_t*)((uint8_t*)alloc + off_sc) : nullptr;
+  p.wd = qmm::is_q4k(type) ? nullptr : (float*)((char*)alloc + off_wd);
+  p.wsm = qmm::is_q4k(type) ? (uint8_t*)alloc + off_sm : nullptr;
   int rc = QMM_OK;
   if ((e = hipMemcpyAsync(raw, host_bytes, nbytes, hipMemcpyHostToDevice, s)) != hipSuccess)
     rc = fail_hip(e, "hipMemcpyAsync(weights)");
@@ -185,10 +181,8 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
   w->device = device;
   w->raw_bytes = nbytes;
   w->plane_bytes = plane_bytes;
-  w->wd_offset = off_wd;
-  w->mn_offset = qmm::is_q4k(type) ? off_mn : plane_bytes;
-  w->dm_offset = plane_bytes;  // no plane of its own: q4_K's dmin sits in the d plane
-  w->sc_offset = qmm::is_q4k(type) ? off_sc : plane_bytes;
+  w->wd_offset = qmm::is_q4k(type) ? plane_bytes : off_wd;
+  w->sm_offset = qmm::is_q4k(type) ? off_sm : plane_bytes;
   w->alloc = alloc;
   if (getenv("QMM_LOG") != nullptr)
     fprintf(stderr, "qmm: registered %s od=%lld id=%lld od_pad=%lld raw=%zu planes=%zu device=%d\n",
@@ -208,9 +202,7 @@ int qmm_weights_info(const qmm_weights* w, qmm_info* out) {
   out->raw_bytes = w->raw_bytes;
   out->plane_bytes = w->plane_bytes;
   out->wd_offset = w->wd_offset;
-  out->mn_offset = w->mn_offset;
-  out->dm_offset = w->dm_offset;
-  out->sc_offset = w->sc_offset;
+  out->sm_offset = w->sm_offset;
   ok();
   return QMM_OK;
 }

@@ -17,9 +17,9 @@ struct Planes {
   int64_t nsb;       // id / 256
   int64_t nchunk;    // id / 32
   int8_t* wq;        // weight fragments in MFMA order: q6_K folded hi/lo, q4_K codes
-  float* wd;         // q6_K: d per (row, super-block); q4_K: d*2^25 and -dmin per (row, super-block)
-  uint16_t* wmn;     // q4_K: the 6-bit min per (row, chunk) as an f16 integer; else nullptr
-  uint16_t* wsc;     // q4_K: the 6-bit scale per (row, chunk) as an f16 integer; else nullptr
+  float* wd;         // q6_K: d per (row, super-block); else nullptr
+  uint8_t* wsm;      // q4_K: one 1 KiB record per (32-row block, 4-chunk stage) of the
+                     // stage's scales and its super-block's mins, d*2^25 and -dmin; else nullptr
 };
 
 constexpr int kRowPad = 128;     // weight rows are padded to a multiple of this
@@ -30,12 +30,16 @@ constexpr int kQ4PackedFrag = 512; // the same, packed: two codes per byte
 // Both q4_K registrations share every plane but the codes'.
 constexpr bool is_q4k(int type) { return type == 4 || type == 14; }  // QMM_Q4_K, QMM_Q4_K_PACKED
 
+// q4_K's per-stage record: the 4 scales of each of the 32 rows (f16 integers,
+// [row][chunk]), the 8 mins of the stage's super-block ([chunk/4][row][chunk%4],
+// f16 integers) and its d*2^25 and -dmin ([part][row], f32) -- 1 KiB, one wave's
+// direct-to-LDS copy.  Both stages of a super-block carry its mins and d.
+constexpr int kQ4RecScOff = 0, kQ4RecMnOff = 256, kQ4RecDOff = 768, kQ4RecBytes = 1024;
+
 // Byte sizes of the planes for a shape (all offsets 256-byte aligned).
 size_t wq_bytes(int type, int64_t od_pad, int64_t id);
 size_t wd_bytes(int type, int64_t od_pad, int64_t id);
-size_t wmn_bytes(int type, int64_t od_pad, int64_t id);
-size_t wdm_bytes(int type, int64_t od_pad, int64_t id);
-size_t wsc_bytes(int type, int64_t od_pad, int64_t id);
+size_t wsm_bytes(int type, int64_t od_pad, int64_t id);
 
 // Kernel launchers: return the hipGetLastError() after the launch.
 hipError_t launch_repack(const uint8_t* raw, const Planes& p, hipStream_t s);

@@ -71,13 +71,28 @@ namespace qmm {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
-__device__ __forceinline__ void copy16_uniform(const void* base, uint32_t lane_off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(lane_off), "s"(base), "s"(lds) : "memory");
-}
-__device__ __forceinline__ void copy16_lane(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds) : "memory");
+// N consecutive 1 KiB copies (N <= 4) from base + lane_off + 1024*i to the LDS
+// bytes at lds + 1024*i: one M0 write, and the instruction offset, which the
+// load adds to both its global and its LDS address, steps through the run.
+template <int N>
+__device__ __forceinline__ void copy16_run(const void* base, uint32_t lane_off, uint32_t lds) {
+  static_assert(N >= 1 && N <= 4, "a run of 1 to 4 KiB (13-bit instruction offsets)");
+  if constexpr (N == 1)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(lane_off), "s"(base), "s"(lds) : "memory");
+  else if constexpr (N == 2)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:1024"
+                 :: "v"(lane_off), "s"(base), "s"(lds) : "memory");
+  else if constexpr (N == 3)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:1024\n\tglobal_load_lds_dwordx4 %0, %1 offset:2048"
+                 :: "v"(lane_off), "s"(base), "s"(lds) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:1024\n\tglobal_load_lds_dwordx4 %0, %1 offset:2048\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:3072"
+                 :: "v"(lane_off), "s"(base), "s"(lds) : "memory");
 }
 
 // Weight fragment bytes per (32-row block, chunk): q6_K hi and lo planes of
@@ -85,24 +100,31 @@ __device__ __forceinline__ void copy16_lane(const void* src, uint32_t lds) {
 template <int TYPE>
 constexpr int kFragA = TYPE == QMM_Q6_K ? 2048 : TYPE == QMM_Q4_K_PACKED ? kQ4PackedFrag : kQ4CodeFrag;
 
+// q4_K's stage record of one 32-row block (the wsm plane's 1 KiB record): the
+// stage's 4 scales and the super-block's 8 mins as f16 integers, d*2^25 and
+// -dmin in f32.
+struct Q4Rec {
+  uint16_t sc[32][4];     // [row][chunk of the stage]
+  uint16_t mn[2][32][4];  // [chunk/4][row][chunk%4] of the super-block
+  float d[2][32];         // [d*2^25, -dmin][row]
+};
+static_assert(sizeof(Q4Rec) == kQ4RecBytes && __builtin_offsetof(Q4Rec, mn) == kQ4RecMnOff &&
+                  __builtin_offsetof(Q4Rec, d) == kQ4RecDOff,
+              "the record as the repack writes it");
+
 template <int TYPE, int WR, int WT, int KC>
 struct alignas(16) Stage {
   static constexpr bool kQ4 = is_q4k(TYPE);
   int8_t a[WR][KC][kFragA<TYPE>];    // weight fragments: [row block][chunk]
   int8_t b[WT][KC][1024];            // q8 codes: [token block][chunk][fragment]
+  // The small region, copied in whole 1 KiB jobs of one kind each:
   uint32_t s[WT][KC][32];            // (dh, s) pairs: [token block][chunk][token]
-  // q4_K: the stage's 4 scales as f16 integers: [row block][row][chunk]
-  uint16_t sc[kQ4 ? WR : 0][32][4];
-  // q4_K: the super-block's 8 mins as f16 integers: [row block][chunk/4][row][chunk%4]
-  uint16_t mn[kQ4 ? WR : 0][2][32][4];
-  // q6_K: super-block d: [row block][row]; q4_K: [row block][d*2^25, -dmin][row]
-  float d[WR][kQ4 ? 2 : 1][32];
-  // s, sc, mn and d are contiguous: the "small" region, copied in 16-byte units
-  // (s and sc with every stage, mn and d with a super-block's last).
-  static constexpr int kUnitsS = WT * KC * 8, kUnitsSc = kQ4 ? WR * 16 : 0, kUnitsMn = kQ4 ? WR * 32 : 0,
-                       kUnitsD = kQ4 ? WR * 16 : WR * 8;
-  static constexpr int kUnits = kUnitsS + kUnitsSc + kUnitsMn + kUnitsD;
-  static constexpr int kSmallJobs = (kUnits + 63) / 64;
+  Q4Rec rec[kQ4 ? WR : 0];           // q4_K: the row blocks' stage records
+  float d[kQ4 ? 0 : WR][32];         // q6_K: super-block d: [row block][row]
+  // jobs: pairs (8/KC token blocks each), then q4_K one per record, or q6_K
+  // one for the d of all row blocks (WR*8 lanes, with a super-block's last stage)
+  static constexpr int kPairJobs = WT * KC * 128 / 1024;
+  static constexpr int kSmallJobs = kPairJobs + (kQ4 ? WR : 1);
 };
 
 // The weight side of one chunk: the MFMA operand(s) read from a stage, the
@@ -119,7 +141,7 @@ struct WeightOps<QMM_Q6_K> {
   __device__ static A load(const int8_t* frag, int lane) {
     return {*(const v4i*)(frag + lane * 16), *(const v4i*)(frag + 1024 + lane * 16)};
   }
-  __device__ static D mma(const A& a, v4i bq, int) {
+  __device__ static D mma(const A& a, v4i bq) {
     const v16i zero = {};
     return {__builtin_amdgcn_mfma_i32_32x32x32_i8(a.hi, bq, zero, 0, 0, 0),
             __builtin_amdgcn_mfma_i32_32x32x32_i8(a.lo, bq, zero, 0, 0, 0)};
@@ -137,10 +159,11 @@ struct WeightOps<QMM_Q6_K> {
 // is kQ4Bias + D*2^-26 exactly.  Subtracting kQ4Bias is exact (both within a
 // factor of two), so val() = D*2^-26 with one full-rate subtraction.
 // The compiler encodes the splat as the inline constant only for an MFMA whose
-// accumulator input is used by no other instruction of its basic block; a
-// uniform branch that is always taken (live != 0) gives every such MFMA a block
-// of its own, for two scalar instructions.  Shared, the splat is materialized
-// in 16 registers, which the kernel does not have.
+// accumulator input is used by no other instruction of its basic block; an
+// empty asm goto after each such MFMA ends its block without emitting an
+// instruction (an always-taken uniform branch did the same for two scalar
+// instructions per MFMA).  Shared, the splat is materialized in 16 registers,
+// which the kernel does not have.
 constexpr uint32_t kQ4BiasBits = 0x3E22F983u;
 
 template <>
@@ -149,13 +172,12 @@ struct WeightOps<QMM_Q4_K> {
   struct D { v16i c; };
   static constexpr int kMfma = 1;
   __device__ static A load(const int8_t* frag, int lane) { return {*(const v4i*)(frag + lane * 16)}; }
-  //   live  nonzero (the launch's chunk count); the result is undefined otherwise
-  __device__ static D mma(const A& a, v4i bq, int live) {
+  __device__ static D mma(const A& a, v4i bq) {
+    const v16i bias = (v16i)(int)kQ4BiasBits;
     D r;
-    if (live) {
-      const v16i bias = (v16i)(int)kQ4BiasBits;
-      r.c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a.c, bq, bias, 0, 0, 0);
-    }
+    r.c = __builtin_amdgcn_mfma_i32_32x32x32_i8(a.c, bq, bias, 0, 0, 0);
+    asm goto("" :::: block_end);
+  block_end:
     return r;
   }
   __device__ static void keep(D& d) { pin(d.c); }
@@ -291,8 +313,7 @@ __device__ __forceinline__ void store_block(float* __restrict__ out, const v16f&
 template <int TYPE, int WR, int WT, int KC, int KS>
 __global__ void __launch_bounds__(64 * WR * WT * KS) __attribute__((amdgpu_waves_per_eu(4, 4)))
 mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
-           const uint8_t* __restrict__ wmn, const uint8_t* __restrict__ wsc,
-           const uint8_t* __restrict__ qq,
+           const uint8_t* __restrict__ wsm, const uint8_t* __restrict__ qq,
            const uint8_t* __restrict__ qs, int nchunk, int nsb, int od, int n_tok,
            int tok_tiles, int dp_row_tiles, int split, int vec_store, float* __restrict__ out,
            float* __restrict__ part) {
@@ -302,10 +323,12 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   constexpr int kJobsA = WR * KC * kFragA<TYPE> / 1024, kJobsB = WT * KC;
   static_assert(KC == 2 || KC == 4 || KC == 8, "a stage is a quarter, half or a whole super-block");
   static_assert(KS == 1 || KS == 2, "one or two k-groups");
-  static_assert(__builtin_offsetof(St, d) ==
-                        __builtin_offsetof(St, s) + 16 * (St::kUnitsS + St::kUnitsSc + St::kUnitsMn) &&
-                    sizeof(St) == __builtin_offsetof(St, s) + 16 * St::kUnits,
-                "the small region is contiguous and ends the stage");
+  static_assert((WT * KC * 128) % 1024 == 0, "whole pair jobs");
+  static_assert((St::kQ4 ? __builtin_offsetof(St, rec) : __builtin_offsetof(St, d)) ==
+                        __builtin_offsetof(St, s) + 1024 * St::kPairJobs &&
+                    sizeof(St) == __builtin_offsetof(St, s) + 1024 * St::kPairJobs +
+                                      (St::kQ4 ? 1024 * WR : 128 * WR),
+                "the small region's jobs are contiguous 1 KiB units and end the stage");
   // the q4_K min term collects a super-block's 8 chunks over two stages
   constexpr bool kQ4 = is_q4k(TYPE);
   static_assert(!kQ4 || KC == 4, "q4_K stages are half super-blocks");
@@ -367,74 +390,65 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   const uint8_t* srcB = qq + (size_t)(tb0 + kb0 / KC) * nchunk * 1024 + (kb0 % KC) * 1024 +
                         (size_t)gbeg * KC * 1024;
   const uint32_t lane_off = (uint32_t)lane * 16;
-  const uint8_t* small_src = nullptr;
-  // 0 none; per stage: 1 pairs (128 bytes per chunk), 3 q4_K scales (256 bytes
-  // per row block); per super-block, at its last stage: 4 q4_K mins (512
-  // bytes), 2 q6_K d (128 bytes) or q4_K d and dmin (256 bytes)
-  int small_kind = 0;
-  constexpr int kDBytes = kQ4 ? 256 : 128;  // d plane bytes per (row block, super-block)
-  if (wave < St::kSmallJobs) {
-    const int u = wave * 64 + lane;
-    const int sb0g = gbeg / kStagesPerSb;
-    constexpr int eSc = St::kUnitsS + St::kUnitsSc, eMn = eSc + St::kUnitsMn;
-    if (u < St::kUnitsS) {
-      small_src = qs + ((size_t)(tb0 + u / (KC * 8)) * nchunk + gbeg * KC) * 128 + (u % (KC * 8)) * 16;
-      small_kind = 1;
-    } else if (u < eSc) {
-      const int v = u - St::kUnitsS;
-      small_src = wsc + ((size_t)(rb0 + v / 16) * nsb * 2 + gbeg) * 256 + (v % 16) * 16;
-      small_kind = 3;
-    } else if (u < eMn) {
-      const int v = u - eSc;
-      small_src = wmn + ((size_t)(rb0 + v / 32) * nsb + sb0g) * 512 + (v % 32) * 16;
-      small_kind = 4;
-    } else if (u < St::kUnits) {
-      const int v = u - eMn;
-      small_src = (const uint8_t*)wd + ((size_t)(rb0 + v / (kDBytes / 16)) * nsb + sb0g) * kDBytes +
-                  (v % (kDBytes / 16)) * 16;
-      small_kind = 2;
-    }
+  // This wave's small-region job (a wave-uniform kind: wave < kSmallJobs),
+  // as a scalar source at the k-group's first stage plus a lane offset:
+  //   pair job k: the pairs of token blocks tb0 + (8/KC)*k + lane/(8*KC),
+  //     KC*128 bytes each per stage;
+  //   q4_K record job r: row block rb0 + r's stage records, 1 KiB per stage;
+  //   q6_K d job: lanes 0..8*WR-1, row block rb0 + lane/8's d, 128 bytes per
+  //     super-block.
+  constexpr int kTokPerJob = 8 / KC;
+  const bool pair_job = wave < St::kPairJobs;
+  const uint8_t* small_src;
+  uint32_t small_off;
+  if (pair_job) {
+    small_src = qs + ((size_t)(tb0 + wave * kTokPerJob) * nchunk + gbeg * KC) * 128;
+    small_off = (uint32_t)(lane / (8 * KC)) * (uint32_t)nchunk * 128 + (uint32_t)(lane % (8 * KC)) * 16;
+  } else if constexpr (kQ4) {
+    small_src = wsm + ((size_t)(rb0 + wave - St::kPairJobs) * (nchunk / 4) + gbeg) * kQ4RecBytes;
+    small_off = lane_off;
+  } else {
+    small_src = (const uint8_t*)wd + ((size_t)rb0 * nsb + gbeg / kStagesPerSb) * 128;
+    small_off = (uint32_t)(lane / 8) * (uint32_t)nsb * 128 + (uint32_t)(lane % 8) * 16;
   }
 
   // This wave's copy jobs for one stage, numbered: its weight run, its code run,
   // its small-region job.  The jobs of stage g+1 are spread over the chunk steps
-  // of stage g (a few per step) rather than issued in one burst, so the copies'
+  // of stage g (one per step) rather than issued in one burst, so the copies'
   // LDS writes interleave with the steps' LDS reads instead of stalling them.
-  constexpr int kWaveJobs = kRunA + kRunB + 1;
-  // One 1 KiB copy job: a wave-uniform source (weight or code fragments) or a
-  // per-lane source (the small region), into stage buffer buf of this k-group.
-  // Sources and LDS destinations are formed from values made scalar once here,
-  // so a copy costs no vector instruction.
+  // Every job is a run of whole-wave 1 KiB copies from a wave-uniform scalar
+  // source plus a lane offset: the kind of job is uniform per wave and whether
+  // it runs in a stage is known at compile time, so a copy costs no vector
+  // instruction and no divergent branch.
+  constexpr int kWaveJobs = 3;
   const uint8_t* const srcA_u = (const uint8_t*)uniform_ptr(srcA);
   const uint8_t* const srcB_u = (const uint8_t*)uniform_ptr(srcB);
+  const uint8_t* const small_u = (const uint8_t*)uniform_ptr(small_src);
   const uint32_t lds_k = __builtin_amdgcn_readfirstlane(lds_addr(stage));
-  auto issue_job = [&](int g, int buf, int j) __attribute__((always_inline)) {
+  //   ends_sb  stage g is the last of its super-block (q6_K's d comes with it)
+  auto issue_job = [&](int g, int buf, int j, bool ends_sb) __attribute__((always_inline)) {
     const uint32_t lds_buf = lds_k + (uint32_t)buf * (uint32_t)sizeof(St);
-    if (j < kRunA) {
+    if (j == 0) {
       if (has_a)
-        copy16_uniform(srcA_u + (size_t)g * KC * kFrag + j * 1024, lane_off,
-                       lds_buf + (uint32_t)__builtin_offsetof(St, a) + (ka0 + j) * 1024);
-    } else if (j < kRunA + kRunB) {
-      const int u = j - kRunA;
+        copy16_run<kRunA>(srcA_u + (size_t)g * KC * kFrag, lane_off,
+                          lds_buf + (uint32_t)__builtin_offsetof(St, a) + ka0 * 1024);
+    } else if (j == 1) {
       if (has_b)
-        copy16_uniform(srcB_u + (size_t)g * KC * 1024 + u * 1024, lane_off,
-                       lds_buf + (uint32_t)__builtin_offsetof(St, b) + (kb0 + u) * 1024);
+        copy16_run<kRunB>(srcB_u + (size_t)g * KC * 1024, lane_off,
+                          lds_buf + (uint32_t)__builtin_offsetof(St, b) + kb0 * 1024);
     } else if (wave < St::kSmallJobs) {
       const uint32_t ls = lds_buf + (uint32_t)__builtin_offsetof(St, s) + wave * 1024;
-      const bool ends_sb = ((g + 1) * KC) % 8 == 0;
-      if (small_kind == 1)
-        copy16_lane(small_src + (size_t)g * KC * 128, ls);
-      else if (small_kind == 3)
-        copy16_lane(small_src + (size_t)g * 256, ls);
-      else if (small_kind == 2 && ends_sb)
-        copy16_lane(small_src + (size_t)((g * KC) / 8) * kDBytes, ls);
-      else if (small_kind == 4 && ends_sb)
-        copy16_lane(small_src + (size_t)((g * KC) / 8) * 512, ls);
+      if (pair_job)
+        copy16_run<1>(small_u + (size_t)g * KC * 128, small_off, ls);
+      else if constexpr (kQ4)
+        copy16_run<1>(small_u + (size_t)g * kQ4RecBytes, small_off, ls);
+      else if (ends_sb && lane < 8 * WR)
+        copy16_run<1>(small_u + (size_t)((g * KC) / 8) * 128, small_off, ls);
     }
   };
-  auto issue_stage = [&](int g, int buf) __attribute__((always_inline)) {  // all at once (prologue)
+  auto issue_stage = [&](int g, int buf, bool ends_sb) __attribute__((always_inline)) {  // all at once
 #pragma unroll
-    for (int j = 0; j < kWaveJobs; ++j) issue_job(g, buf, j);
+    for (int j = 0; j < kWaveJobs; ++j) issue_job(g, buf, j, ends_sb);
   };
 
   v16f acc, inner;
@@ -450,7 +464,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   v2i bs = {};
   const bool lane_hi = lane >= 32;
 
-  if (nstages > 0) issue_stage(0, 0);
+  if (nstages > 0) issue_stage(0, 0, kStagesPerSb == 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -473,14 +487,14 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
         uint32_t dhr = st.s[wt][0][lane & 31], dhr_even = 0;
         v2i a_sc = {}, amin = {};
         if constexpr (kQ4) {
-          if (h == kStagesPerSb - 1) amin = *(const v2i*)(&st.mn[wr][lane >> 5][lane & 31][0]);
-          a_sc = *(const v2i*)(&st.sc[wr][lane & 31][0]);
+          if (h == kStagesPerSb - 1) amin = *(const v2i*)(&st.rec[wr].mn[lane >> 5][lane & 31][0]);
+          a_sc = *(const v2i*)(&st.rec[wr].sc[lane & 31][0]);
         }
         typename W::A a0 = W::load(st.a[wr][0], lane);
         v4i bq0 = *(const v4i*)(st.b[wt][0] + lane * 16);
         typename W::A a1 = W::load(st.a[wr][1], lane);
         v4i bq1 = *(const v4i*)(st.b[wt][1] + lane * 16);
-        typename W::D dj = W::mma(a0, bq0, nchunk);
+        typename W::D dj = W::mma(a0, bq0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int cc = 0; cc < KC; ++cc) {
@@ -497,16 +511,17 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
           }
           typename W::D dj_next;
           if (cc + 1 < KC) {
-            dj_next = W::mma(a1, bq1, nchunk);
+            dj_next = W::mma(a1, bq1);
             W::keep(dj_next);
           }
           // stage (g+1)&1 was last read in iteration g-1, which every wave finished
           // before the barrier that ended it
           if (g + 1 < nstages) {
             constexpr int per = (kWaveJobs + KC - 1) / KC;
+            const bool next_ends_sb = (h + 1) % kStagesPerSb == kStagesPerSb - 1;
 #pragma unroll
             for (int q = 0; q < per; ++q)
-              if (cc * per + q < kWaveJobs) issue_job(g + 1, (g + 1) & 1, cc * per + q);
+              if (cc * per + q < kWaveJobs) issue_job(g + 1, (g + 1) & 1, cc * per + q, next_ends_sb);
           }
           typename W::A a2;
           v4i bq2;
@@ -562,9 +577,12 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
             mt = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(v4h, amin), __builtin_bit_cast(v4h, bs),
                                                       zero, 0, 0, 0);
           }
+          const float* dw;  // the row block's d (q4_K: d*2^25), then q4_K's -dmin
+          if constexpr (kQ4) dw = st.rec[wr].d[0];
+          else dw = st.d[wr];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 d4 = *(const float4*)(&st.d[wr][0][8 * q + 4 * (lane >> 5)]);
+            const float4 d4 = *(const float4*)(&dw[8 * q + 4 * (lane >> 5)]);
             acc[4 * q + 0] = fmaf(inner[4 * q + 0], d4.x, acc[4 * q + 0]);
             acc[4 * q + 1] = fmaf(inner[4 * q + 1], d4.y, acc[4 * q + 1]);
             acc[4 * q + 2] = fmaf(inner[4 * q + 2], d4.z, acc[4 * q + 2]);
@@ -573,7 +591,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
           if constexpr (kQ4) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float4 m4 = *(const float4*)(&st.d[wr][1][8 * q + 4 * (lane >> 5)]);
+              const float4 m4 = *(const float4*)(&dw[32 + 8 * q + 4 * (lane >> 5)]);
               acc[4 * q + 0] = fmaf(mt[4 * q + 0], m4.x, acc[4 * q + 0]);
               acc[4 * q + 1] = fmaf(mt[4 * q + 1], m4.y, acc[4 * q + 1]);
               acc[4 * q + 2] = fmaf(mt[4 * q + 2], m4.z, acc[4 * q + 2]);
@@ -679,7 +697,7 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
   const int vec_store = (p.od % 4 == 0) && ((uintptr_t)out % 16 == 0);
   const int64_t wgs = plan.work_groups;
   mmq_kernel<TYPE, WR, WT, KC, KS><<<dim3((unsigned)wgs), dim3(64 * WR * WT * KS), 0, s>>>(
-      p.wq, p.wd, (const uint8_t*)p.wmn, (const uint8_t*)p.wsc, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
+      p.wq, p.wd, p.wsm, qact, qs, (int)p.nchunk, (int)p.nsb, (int)p.od, (int)n_tok, plan.tok_tiles,
       plan.dp_row_tiles, plan.split, vec_store, out, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_tail == 0) return e;

@@ -170,7 +170,7 @@ struct alignas(16) CalStage {
 // four chunk steps.
 template <bool Q6>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
-peak_chunk(int iters, int live, unsigned long long* clk, int* sink) {
+peak_chunk(int iters, unsigned long long* clk, int* sink) {
   __shared__ CalStage st2[2];
   const int lane = threadIdx.x & 63;
   // codes 0..15 (q4_K) or -64..63 / 0..63 (q6_K), activations -64..63, dh = 1/64,
@@ -200,9 +200,11 @@ peak_chunk(int iters, int live, unsigned long long* clk, int* sink) {
       const v16i z = {};
       o.d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq, z, 0, 0, 0);
       o.d2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a2, bq, z, 0, 0, 0);
-    } else if (live) {  // the bias as the instruction's inline constant (see the MMQ)
+    } else {  // the bias as the instruction's inline constant: the MFMA ends its block (see the MMQ)
       const v16i bias = (v16i)(int)kBiasBits;
       o.d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bq, bias, 0, 0, 0);
+      asm goto("" :::: block_end);
+    block_end:;
     }
     return o;
   };
@@ -371,8 +373,8 @@ extern "C" int qmm_peak_launch(int kind, int iters, int grid, void* clk, void* s
     case 0: peak_mfma_i8<<<g, b, 0, s>>>(iters, c, k); break;
     case 1: peak_epilogue<<<g, b, 0, s>>>(iters, c, k); break;
     case 2: peak_epilogue_q4<<<g, b, 0, s>>>(iters, c, k); break;
-    case 3: peak_chunk<false><<<g, b, 0, s>>>(iters, 1, c, k); break;
-    case 4: peak_chunk<true><<<g, b, 0, s>>>(iters, 1, c, k); break;
+    case 3: peak_chunk<false><<<g, b, 0, s>>>(iters, c, k); break;
+    case 4: peak_chunk<true><<<g, b, 0, s>>>(iters, c, k); break;
     case 5: peak_overlap<true><<<g, b, 0, s>>>(iters, c, k); break;
     default: peak_overlap<false><<<g, b, 0, s>>>(iters, c, k); break;
   }

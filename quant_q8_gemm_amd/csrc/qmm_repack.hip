@@ -10,7 +10,9 @@
 // its 6-bit scales and mins become f16 integers (exact), the operands from which
 // the GEMM's f16 matrix-core products form scale*dh and the min term; its d and
 // dmin stay per super-block f32 values, applied once per super-block, so every
-// stored value is exact whatever the spread of d and dmin along a row.
+// stored value is exact whatever the spread of d and dmin along a row.  q4_K's
+// scales, mins, d and dmin are grouped into one 1 KiB record per 32-row block
+// and GEMM stage, which one wave copies to LDS with a single uniform load.
 #include "qmm_internal.h"
 #include "qmm_common.h"
 
@@ -33,17 +35,20 @@ namespace qmm {
 //             byte (j/32*nchunk + k/32)*512 + ((k%32)/16)*256 + (j%32)*8 + k%8
 //             (one lane's 8 bytes unpack with two masks and two shifts into
 //             its 16 code bytes)
-//   wd  q6_K: f32 [R][nsb][32 rows]  d of (row, super-block)
-//       q4_K: f32 [R][nsb][2][32 rows]  of (row j, super-block b): part 0 is
-//             d*2^25, part 1 is -dmin, at element ((j/32*nsb + b)*2 + part)*32
-//             + j%32 (both exact in f32; a zero is stored as +0)
-//   wmn f16   [R][nsb][2][32 rows][4]  q4_K only: the 6-bit min of (row j,
-//             chunk c) as an f16 integer at element ((j/32*nsb + c/8)*2
-//             + (c%8)/4)*128 + (j%32)*4 + c%4 (lane half h of the min-term
-//             MFMA reads chunks 4h..4h+3 of its row as one 8-byte word)
-//   wsc f16   [R][nsb][2][32 rows][4]  q4_K only: the 6-bit scale of (row j,
-//             chunk c) as an f16 integer, same element index as wmn (one 8-byte
-//             word per row and 4-chunk stage)
+//   wd  q6_K only: f32 [R][nsb][32 rows]  d of (row, super-block)
+//   wsm q4_K only: [R][nchunk/4 stages][1024 bytes], one record per (32-row
+//             block, stage of chunks 4g..4g+3), at byte (j/32*nchunk/4 + g)*1024:
+//             +0    f16 [32 rows][4]: the 6-bit scale of (row j, chunk 4g + i)
+//                   as an f16 integer at element (j%32)*4 + i (one 8-byte word
+//                   per row: the A operand of the scale outer product)
+//             +256  f16 [2][32 rows][4]: the 6-bit mins of the stage's
+//                   super-block b = g/2, (row j, chunk 8b + 4h + i) at element
+//                   (h*32 + j%32)*4 + i (lane half h of the min-term MFMA reads
+//                   chunks 4h..4h+3 of its row as one 8-byte word)
+//             +768  f32 [2][32 rows]: d*2^25 (part 0) and -dmin (part 1) of
+//                   (row j, super-block b) at element part*32 + j%32 (both exact
+//                   in f32; a zero is stored as +0)
+//             the mins, d and dmin of super-block b are in both its records
 // Rows od..od_pad-1 are zero in every plane.
 // ---------------------------------------------------------------------------
 size_t wq_bytes(int type, int64_t od_pad, int64_t id) {
@@ -51,14 +56,10 @@ size_t wq_bytes(int type, int64_t od_pad, int64_t id) {
   return type == QMM_Q6_K ? n * 2 : type == QMM_Q4_K_PACKED ? n / 2 : n;
 }
 size_t wd_bytes(int type, int64_t od_pad, int64_t id) {
-  return (size_t)od_pad * (size_t)(id / 256) * 4 * (is_q4k(type) ? 2 : 1);
+  return is_q4k(type) ? 0 : (size_t)od_pad * (size_t)(id / 256) * 4;
 }
-size_t wmn_bytes(int type, int64_t od_pad, int64_t id) {
-  return is_q4k(type) ? (size_t)od_pad * (size_t)(id / 32) * 2 : 0;
-}
-size_t wdm_bytes(int, int64_t, int64_t) { return 0; }
-size_t wsc_bytes(int type, int64_t od_pad, int64_t id) {
-  return is_q4k(type) ? (size_t)od_pad * (size_t)(id / 32) * 2 : 0;
+size_t wsm_bytes(int type, int64_t od_pad, int64_t id) {
+  return is_q4k(type) ? (size_t)(od_pad / 32) * (size_t)(id / 128) * kQ4RecBytes : 0;
 }
 
 // q4_K: the 6-bit scale and min of sub-block cl of a 144-byte block (ggml's
@@ -74,11 +75,32 @@ __device__ __forceinline__ void q4k_scale_min(const uint8_t* B, int cl, int& sc,
   }
 }
 
+// q4_K: the values of (row jr of row block rb, chunk c) in the stage record of
+// the chunk (its scale) and in both records of its super-block (its min; d25
+// and ndmin, from the thread of the super-block's first chunk).
+__device__ __forceinline__ void q4k_record(uint8_t* wsm, int rb, int nchunk, int c, int jr, uint16_t sc,
+                                           uint16_t mn, float d25, float ndmin) {
+  const int cl = c & 7;
+  uint8_t* const rec0 = wsm + ((int64_t)rb * (nchunk / 4) + 2 * (c >> 3)) * kQ4RecBytes;
+  uint8_t* const rec1 = rec0 + kQ4RecBytes;
+  uint8_t* const rec = cl < 4 ? rec0 : rec1;
+  ((uint16_t*)(rec + kQ4RecScOff))[jr * 4 + (cl & 3)] = sc;
+  const int mi = ((cl >> 2) * 32 + jr) * 4 + (cl & 3);
+  ((uint16_t*)(rec0 + kQ4RecMnOff))[mi] = mn;
+  ((uint16_t*)(rec1 + kQ4RecMnOff))[mi] = mn;
+  if (cl == 0) {
+    for (uint8_t* r : {rec0, rec1}) {
+      ((float*)(r + kQ4RecDOff))[jr] = d25;
+      ((float*)(r + kQ4RecDOff))[32 + jr] = ndmin;
+    }
+  }
+}
+
 // One thread per (row j in [0, od_pad), chunk c, k-half h): 16 weights.
 __global__ void __launch_bounds__(256)
 repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nchunk,
               int64_t total, int8_t* __restrict__ wq, float* __restrict__ wd,
-              uint16_t* __restrict__ wmn, uint16_t* __restrict__ wsc) {
+              uint8_t* __restrict__ wsm) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total) return;
   const int h = (int)(gid & 1);
@@ -126,28 +148,16 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
         // the scale and min as f16 integers (6 bits: exact); d and dmin once per
         // super-block, d times 2^25 (the GEMM's scale products and block dots
         // carry 2^-25 between them; a power of two, so the product stays exact)
-        const int64_t si = (((int64_t)rb * nsb + b) * 2 + (cl >> 2)) * 128 + jr * 4 + (cl & 3);
-        wsc[si] = __builtin_bit_cast(uint16_t, (_Float16)sc);
-        wmn[si] = __builtin_bit_cast(uint16_t, (_Float16)mn);
-        if (cl == 0) {
-          const float d = f16_bits_to_float(B[0] | (B[1] << 8)), dmin = f16_bits_to_float(B[2] | (B[3] << 8));
-          wd[(((int64_t)rb * nsb + b) * 2 + 0) * 32 + jr] = ldexpf(d, 25) + 0.0f;
-          wd[(((int64_t)rb * nsb + b) * 2 + 1) * 32 + jr] = -dmin + 0.0f;
-        }
+        const float d = f16_bits_to_float(B[0] | (B[1] << 8)), dmin = f16_bits_to_float(B[2] | (B[3] << 8));
+        q4k_record(wsm, rb, nchunk, c, jr, __builtin_bit_cast(uint16_t, (_Float16)sc),
+                   __builtin_bit_cast(uint16_t, (_Float16)mn), ldexpf(d, 25) + 0.0f, -dmin + 0.0f);
       }
     }
   } else if (h == 0) {
-    if (is_q4k(type)) {
-      const int64_t si = (((int64_t)rb * nsb + b) * 2 + (cl >> 2)) * 128 + jr * 4 + (cl & 3);
-      wsc[si] = 0;
-      wmn[si] = 0;
-      if (cl == 0) {
-        wd[(((int64_t)rb * nsb + b) * 2 + 0) * 32 + jr] = 0.0f;
-        wd[(((int64_t)rb * nsb + b) * 2 + 1) * 32 + jr] = 0.0f;
-      }
-    } else if (cl == 0) {
+    if (is_q4k(type))
+      q4k_record(wsm, rb, nchunk, c, jr, 0, 0, 0.0f, 0.0f);
+    else if (cl == 0)
       wd[((int64_t)rb * nsb + b) * 32 + jr] = 0.0f;
-    }
   }
   if (type == QMM_Q6_K) {
     int8_t* dst = wq + ((int64_t)rb * nchunk + c) * 2048 + h * 512 + jr * 16;
@@ -166,7 +176,7 @@ hipError_t launch_repack(const uint8_t* raw, const Planes& p, hipStream_t s) {
   const int64_t total = p.od_pad * p.nchunk * 2;
   const int64_t blocks = (total + 255) / 256;
   repack_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
-      raw, p.type, (int)p.od, (int)p.nsb, (int)p.nchunk, total, p.wq, p.wd, p.wmn, p.wsc);
+      raw, p.type, (int)p.od, (int)p.nsb, (int)p.nchunk, total, p.wq, p.wd, p.wsm);
   return hipGetLastError();
 }
 

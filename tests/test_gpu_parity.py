@@ -151,8 +151,7 @@ def expected_planes(type_, raw, od, id_):
 
 
 def check_planes(w, type_, raw, od, id_):
-    got = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.mn_offset,
-                              w.dm_offset, w.sc_offset)
+    got = layouts.read_planes(w.export(), type_, w.od_pad, id_, w.wd_offset, w.sm_offset)
     exp = expected_planes(type_, raw, od, id_)
     assert set(got) == set(exp)
     for k, e in exp.items():
@@ -162,8 +161,6 @@ def check_planes(w, type_, raw, od, id_):
         else:
             assert np.array_equal(g[:od], e), f"plane {k} differs"
         assert not g[od:].view(np.uint8).any(), f"plane {k}: padding rows not zero"
-    if type_ != synth.Q6_K:
-        assert w.dm_offset == w.plane_bytes
 
 
 @pytest.mark.parametrize("type_,od,id_,full", [(synth.Q6_K, 5, 512, False), (synth.Q6_K, 130, 768, True),
