@@ -710,21 +710,24 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
 //  * many tiles (at least four 64 x 64 tiles per CU, e.g. the 3314-token layer,
 //    the 2048-token head): several work-groups per CU, so one group's barrier
 //    wait is covered by the others.  q4_K: 2 x 2 waves (64 x 64 tiles), four
-//    per CU, half-super-block stages (30 KiB of LDS, 110 VGPRs).  q6_K: 2 x 4
-//    waves (64 rows x 128 tokens), two per CU, half-super-block stages (69 KiB,
-//    124 VGPRs): each weight fragment a work-group copies serves four waves
+//    per CU, half-super-block stages (38 KiB of LDS, 114 VGPRs; packed codes
+//    30 KiB, 112).  q6_K: 2 x 4 waves (64 rows x 128 tokens), two per CU,
+//    half-super-block stages (68.5 KiB, 120 VGPRs): each weight fragment a
+//    work-group copies serves four waves
 //    instead of two, a third fewer copied bytes per output block, which is
 //    what q6_K's 2-byte weights are short of (3-8% faster than 2 x 2 waves with
 //    quarter stages; 4 x 4 and 4 x 2 waves were slower, and the 2 x 4 shape
 //    was 4-9% slower for q4_K, whose copies are a quarter the size);
 //  * few tiles (e.g. 512 tokens x 4096 rows = 256 64 x 128 tiles): 2 x 4 waves
 //    (64 rows x 128 tokens) in two k-groups, half-super-block stages, 137 KiB
-//    (q6_K) or 95 KiB (q4_K) of LDS, one work-group per CU; the second k-group
-//    doubles the waves per CU.
+//    (q6_K), 112 KiB (q4_K) or 96 KiB (packed q4_K) of LDS, one work-group per
+//    CU; the second k-group doubles the waves per CU.
 // In all, a ragged second wave (tiles = slots + r with r <= slots / 2, the
 // slots being the work-groups resident at once; e.g. 4097 rows x 512 tokens:
 // 264 tiles on 256 CUs, 11008 rows x 512 tokens: 1376 tiles on 1024 slots) is
-// split along K.
+// split along K, and so is, with two work-groups per CU, a last wave of at most
+// a quarter of the slots behind several full ones (the q6_K GEMMs of a layer
+// at 3314 tokens).
 // The switch point (about four 64 x 64 tiles per CU) was chosen by timing both
 // on the 512-token shapes, the 3314-token layer shapes and the 2048-token head.
 namespace {
@@ -762,12 +765,17 @@ MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
   const int64_t tiles = (int64_t)plan.row_tiles * plan.tok_tiles;
   // work-groups resident at once
   const int64_t slots = (int64_t)num_cus * g.per_cu;
-  // Only after at most one full wave: behind several (e.g. 3328 tiles on 1024
-  // slots) the tail's work-groups already overlap the last full wave's end, and
-  // the split measured 0.5-1% slower there instead of 9% faster.  With no full
-  // wave (at most half the slots filled, e.g. one GPU's 512-row share of a
-  // layer), every tile is a tail tile.
-  if (num_cus > 0 && tiles != slots && tiles < 2 * slots) {
+  // After at most one full wave; behind several, only for a tail of at most a
+  // quarter of the slots with two work-groups per CU: there half the CUs or
+  // more would idle through the last wave (q6_K 4096 x 11008 at 3314 tokens:
+  // 1664 tiles on 512 slots, 2.2% faster split).  Behind several waves with
+  // four work-groups per CU (e.g. 3328 tiles on 1024 slots) the tail's
+  // work-groups already overlap the last full wave's end, and the split
+  // measured 0.5-1% slower there instead of 9% faster.  With no full wave (at
+  // most half the slots filled, e.g. one GPU's 512-row share of a layer),
+  // every tile is a tail tile.
+  const bool short_tail = tiles > 2 * slots && (tiles % slots) * 4 <= slots && g.per_cu <= 2;
+  if (num_cus > 0 && tiles != slots && (tiles < 2 * slots || short_tail)) {
     // the full wave stays data-parallel (whole row tiles), the row tiles after
     // it form the tail
     const int dp_rows = (int)((tiles / slots) * slots / plan.tok_tiles);

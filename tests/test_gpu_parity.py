@@ -366,6 +366,10 @@ SMALL = [("q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          # (a split tail), and 1088 tiles (two full waves and a ragged third)
          ("q6_K 1000x512 T=4100", synth.Q6_K, 1000, 512, 4100, True),
          ("q6_K 2100x256 T=4000", synth.Q6_K, 2100, 256, 4000, False),
+         # three full waves of 512 tiles and a last wave of 89 (at most a quarter
+         # of the slots, two work-groups per CU): the 100 tiles after the 61st
+         # row tile split 4 ways along K, the last row tile and token tile ragged
+         ("q6_K 4097x1024 T=3199", synth.Q6_K, 4097, 1024, 3199, True),
          # one token against 70000 rows: the many-tile geometry with a single
          # token tile (1094 row tiles)
          ("q4_K 70000x256 T=1", synth.Q4_K, 70000, 256, 1, False),
