@@ -25,6 +25,7 @@ from __future__ import annotations
 import argparse
 import concurrent.futures as cf
 import hashlib
+import re
 import importlib.util
 import json
 import os
@@ -147,11 +148,14 @@ def _parse():
 
 
 def kernel_hash() -> str:
-    """The MMQ kernel's source and the device compiler flags it is built with."""
+    """The MMQ kernel's code (its source without comments and blank space, so
+    that a comment edit keeps counters taken on the same code valid) and the
+    device compiler flags it is built with."""
     spec = importlib.util.spec_from_file_location("qmm_build", os.path.join(ROOT, "quant_q8_gemm_amd", "_build.py"))
     build = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(build)
-    h = hashlib.sha256(open(KERNEL_SRC, "rb").read())
+    code = re.sub(r"//[^\n]*|/\*.*?\*/", " ", open(KERNEL_SRC).read(), flags=re.S)
+    h = hashlib.sha256(" ".join(code.split()).encode())
     h.update(" ".join(build.LIB_FLAGS).encode())
     return h.hexdigest()[:16]
 

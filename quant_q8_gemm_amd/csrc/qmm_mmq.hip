@@ -48,12 +48,12 @@ namespace qmm {
 // stages of KC chunks of 32 (KC = 2, 4 or 8: a quarter, half or whole 256-wide
 // super-block).  Each stage's operands -- the weight fragments of the WR row
 // blocks, the q8 codes and scale pairs of the WT token blocks, and q6_K's d or
-// q4_K's scale and min pairs -- are copied once per
-// work-group into LDS with direct global->LDS loads (global_load_lds_dwordx4
-// puts lane l's 16 bytes at the LDS base + 16*l, so one wave instruction moves
-// 1 KiB), and read from there by every wave that shares them.  Two LDS stages
-// alternate: the loads of stage g+1 are issued during stage g, a few per chunk
-// step; one barrier per stage.
+// q4_K's stage records (scales, mins, d and dmin) of the row blocks -- are
+// copied once per work-group into LDS with direct global->LDS loads
+// (global_load_lds_dwordx4 puts lane l's 16 bytes at the LDS base + 16*l, so
+// one wave instruction moves 1 KiB), and read from there by every wave that
+// shares them.  Two LDS stages alternate: the loads of stage g+1 are issued
+// during stage g, one job of a wave per chunk step; one barrier per stage.
 // A small tile and a small LDS footprint let several work-groups share a CU, so
 // one group's barrier wait is covered by the others' work.
 // MFMA orientation: A = weights (rows j), B = activations (columns t), so each
@@ -384,7 +384,7 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   const bool has_a = kJobsA >= kWaves || wave < kJobsA;
   const bool has_b = kJobsB >= kWaves || wave < kJobsB;
   const int ka0 = wave * kRunA, kb0 = wave * kRunB;
-  // wave-uniform sources (see copy_uniform below)
+  // wave-uniform sources (see copy16_run)
   const int8_t* srcA = wq + (size_t)(rb0 + ka0 / kPerRbA) * nchunk * kFrag + (ka0 % kPerRbA) * 1024 +
                       (size_t)gbeg * KC * kFrag;
   const uint8_t* srcB = qq + (size_t)(tb0 + kb0 / KC) * nchunk * 1024 + (kb0 % KC) * 1024 +
@@ -419,7 +419,8 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   // Every job is a run of whole-wave 1 KiB copies from a wave-uniform scalar
   // source plus a lane offset: the kind of job is uniform per wave and whether
   // it runs in a stage is known at compile time, so a copy costs no vector
-  // instruction and no divergent branch.
+  // instruction and no divergent branch (q6_K's d job masks its lanes past
+  // 8*WR).
   constexpr int kWaveJobs = 3;
   const uint8_t* const srcA_u = (const uint8_t*)uniform_ptr(srcA);
   const uint8_t* const srcB_u = (const uint8_t*)uniform_ptr(srcB);

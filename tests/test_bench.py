@@ -75,3 +75,20 @@ def test_step_roof_weights_each_gemm_by_its_ops():
     # 64 int8 ops per (token, row, 32-block), 3 (q6_K) or 2.25 (q4_K) instructions each
     assert abs(bench.nominal_epilogue_tops(synth.Q6_K) - 256 * 64 * 2.4e9 * 64 / 3 / 1e12) < 1e-9
     assert abs(bench.nominal_epilogue_tops(synth.Q4_K) - 256 * 64 * 2.4e9 * 64 / 2.25 / 1e12) < 1e-9
+
+
+def test_kernel_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    """The kernel hash that ties the committed counters to the MMQ code stays
+    the same when only comments or blank space change, and changes with the
+    code (CPU)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    src = open(bench.KERNEL_SRC).read()
+    h0 = bench.kernel_hash()
+    k = tmp_path / "k.hip"
+    k.write_text("// a comment\n\n" + src.replace("namespace qmm {", "namespace qmm {  /* a note */", 1))
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(k))
+    assert bench.kernel_hash() == h0
+    assert "constexpr int kGroupRows = 8;" in src
+    k.write_text(src.replace("constexpr int kGroupRows = 8;", "constexpr int kGroupRows = 4;"))
+    assert bench.kernel_hash() != h0
