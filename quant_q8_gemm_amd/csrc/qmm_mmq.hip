@@ -726,9 +726,9 @@ static hipError_t launch_tiled(const Planes& p, const MmqPlan& plan, const uint8
 // In all, a ragged second wave (tiles = slots + r with r <= slots / 2, the
 // slots being the work-groups resident at once; e.g. 4097 rows x 512 tokens:
 // 264 tiles on 256 CUs, 11008 rows x 512 tokens: 1376 tiles on 1024 slots) is
-// split along K, and so is, with two work-groups per CU, a last wave of at most
-// a quarter of the slots behind several full ones (the q6_K GEMMs of a layer
-// at 3314 tokens).
+// split along K, and so is, with one or two work-groups per CU, a last wave of
+// at most a quarter of the slots behind several full ones (the q6_K GEMMs of a
+// layer at 3314 tokens).
 // The switch point (about four 64 x 64 tiles per CU) was chosen by timing both
 // on the 512-token shapes, the 3314-token layer shapes and the 2048-token head.
 namespace {
@@ -767,9 +767,9 @@ MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
   // work-groups resident at once
   const int64_t slots = (int64_t)num_cus * g.per_cu;
   // After at most one full wave; behind several, only for a tail of at most a
-  // quarter of the slots with two work-groups per CU: there half the CUs or
-  // more would idle through the last wave (q6_K 4096 x 11008 at 3314 tokens:
-  // 1664 tiles on 512 slots, 2.2% faster split).  Behind several waves with
+  // quarter of the slots with one or two work-groups per CU: there half the
+  // CUs or more would idle through the last wave (q6_K 4096 x 11008 at 3314
+  // tokens: 1664 tiles on 512 slots, 2.2% faster split).  Behind several waves with
   // four work-groups per CU (e.g. 3328 tiles on 1024 slots) the tail's
   // work-groups already overlap the last full wave's end, and the split
   // measured 0.5-1% slower there instead of 9% faster.  With no full wave (at

@@ -370,6 +370,10 @@ SMALL = [("q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          # of the slots, two work-groups per CU): the 100 tiles after the 61st
          # row tile split 4 ways along K, the last row tile and token tile ragged
          ("q6_K 4097x1024 T=3199", synth.Q6_K, 4097, 1024, 3199, True),
+         # the same in the few-tile geometry (64 x 128 tiles, one work-group per
+         # CU): 520 tiles on 256 slots, the 13 tiles after the 39th row tile
+         # split 8 ways, the last row tile ragged
+         ("q4_K 2527x4352 T=1572", synth.Q4_K, 2527, 4352, 1572, False),
          # one token against 70000 rows: the many-tile geometry with a single
          # token tile (1094 row tiles)
          ("q4_K 70000x256 T=1", synth.Q4_K, 70000, 256, 1, False),
