@@ -214,8 +214,8 @@ int qmm_quantize_activations(const float *x, int64_t n_tok, int64_t id, void *qa
  * dimension into partial sums that a second kernel adds in a fixed order.  Their
  * scratch is one device buffer per (device, stream) of 64 KiB per compute unit
  * (16 MiB on MI355X), allocated with hipMalloc by the first call on that stream
- * that needs it and kept until the process ends; calls on one stream share it
- * in stream order.  Synchronize a stream before destroying it if an MMQ on it
+ * that needs it and kept until qmm_stream_release or the end of the process;
+ * calls on one stream share it in stream order.  Synchronize a stream before destroying it if an MMQ on it
  * may still run.  Results are deterministic: the same call gives the same bits.
  * Errors: QMM_EINVAL (also for a shape whose tiles exceed one launch: n_tok * od
  * beyond about 6.9e10, i.e. an output of 275 GB), QMM_ESHAPE, QMM_ENOMEM (the
