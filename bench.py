@@ -518,6 +518,18 @@ def main():
         "plane_bytes": sum(w.plane_bytes for w in weights.values()),
         "raw_weight_bytes": sum(w.raw_bytes for w in weights.values()),
     }
+    # per weight type (registration type): its GEMMs' ops over their
+    # back-to-back times, against the int8 peak (and below, its chunk-step roof)
+    per_type = {}
+    for k, (_, t, od, id_, _) in enumerate(gemms):
+        e = per_type.setdefault(synth.TYPE_NAMES[t], {"type": t, "ops": 0.0, "ms": 0.0})
+        e["ops"] += 2.0 * T * od * id_
+        e["ms"] += float(per[n_in + k])
+    result["roofline"]["per_type"] = {
+        name: {"ops_per_step": e["ops"], "ms_back_to_back": round(e["ms"], 4),
+               "tops": round(e["ops"] / (e["ms"] / 1e3) / 1e12, 2),
+               "frac": round(e["ops"] / (e["ms"] / 1e3) / 1e12 / MFMA_INT8_PEAK_TOPS, 4)}
+        for name, e in per_type.items()}
     if not args.no_calib:
         # the measured roofs are context for the MMQ's figures: a failure here
         # is reported in the line, not allowed to lose the measurement above
@@ -548,6 +560,8 @@ def main():
             rl["chunk_roof"] = {"bound": "mfma+alu", "measured": round(chunk_roof, 1),
                                 "unit": "TOP/s (int8-equivalent)",
                                 "frac_of_measured": round(mmq_tops / chunk_roof, 4)}
+            for name, e in per_type.items():
+                rl["per_type"][name]["chunk_roof_frac"] = round(rl["per_type"][name]["tops"] / chunk[e["type"]], 4)
     if not args.no_cpu:
         threads, rule = cpu_threads(args.cpu_threads)
         result["cpu_baseline"] = cpu_baseline(gemms, raws, xs, T, threads, args.cpu_macs)

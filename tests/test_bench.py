@@ -52,6 +52,12 @@ def test_bench_json_line_contract():
     assert 0 < cal["chunk_q6k"]["tops"] < cal["mfma_i8"]["tops"]
     assert 0 < rl["chunk_roof"]["frac_of_measured"] < 1.05
     assert all(cal[k]["schedule"] in ("default", "max-ilp") for k in ("mfma_i8", "chunk_q4k", "chunk_q6k"))
+    # per weight type: its GEMMs' rate against the int8 peak and its own chunk-step roof
+    pt = rl["per_type"]
+    assert pt and set(pt) <= {"q4_K", "q6_K", "q4_K packed"}, pt
+    for v in pt.values():
+        assert v["tops"] > 0 and abs(v["frac"] - v["tops"] / rl["peak"]) < 1e-3
+        assert 0 < v["chunk_roof_frac"] < 1.05
     ov = cal["mfma_valu_overlap"]
     assert ov["both_cycles"] >= max(ov["mfma_cycles"], ov["fma_cycles"]) * 0.95
 
