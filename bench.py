@@ -29,6 +29,9 @@ import re
 import importlib.util
 import json
 import os
+import shutil
+import subprocess
+import threading
 import sys
 import time
 
@@ -145,6 +148,57 @@ def _parse():
     ap.add_argument("--cpu-macs", type=float, default=2.4e10,
                     help="multiply-accumulates of the oracle sample (about 20 s of CPU work)")
     return ap.parse_args()
+
+
+class Telemetry:
+    """Socket power and shader clock of GPU 0 while the benchmark runs, from
+    `amd-smi metric` started as a child process in a background thread (about
+    three samples per second); absent tool or unparsable output: no samples."""
+
+    def __init__(self):
+        exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+        self.exe = exe if os.path.exists(exe) else None
+        self.samples = []
+        self.stop = threading.Event()
+        self.thread = None
+
+    def start(self):
+        if self.exe is not None:
+            self.thread = threading.Thread(target=self._run, daemon=True)
+            self.thread.start()
+
+    def _run(self):
+        while not self.stop.is_set():
+            t = time.perf_counter()
+            try:
+                r = subprocess.run([self.exe, "metric", "-g", "0", "--power", "--clock", "--json"],
+                                   capture_output=True, text=True, timeout=10)
+                d = json.loads(r.stdout)
+                d = d[0] if isinstance(d, list) else d
+                g = d["gpu_data"][0] if "gpu_data" in d else d
+                watts = float(g["power"]["socket_power"]["value"])
+                clks = [float(v["clk"]["value"]) for k, v in g["clock"].items()
+                        if k.startswith("gfx_") and isinstance(v, dict)
+                        and isinstance(v.get("clk", {}).get("value"), (int, float))]
+                if clks:
+                    self.samples.append((t, watts, float(np.median(clks))))
+            except (OSError, ValueError, KeyError, TypeError, IndexError, subprocess.SubprocessError):
+                pass
+            self.stop.wait(0.2)
+
+    def summary(self, t_from, t_to):
+        """Medians over the samples taken in [t_from, t_to] (perf_counter
+        seconds), or None; stops the sampling."""
+        self.stop.set()
+        if self.thread is not None:
+            self.thread.join(timeout=15)
+        sel = [(w, c) for t, w, c in self.samples if t_from <= t <= t_to]
+        if not sel:
+            return None
+        return {"socket_w_median": round(float(np.median([w for w, _ in sel])), 1),
+                "gfx_mhz_median": round(float(np.median([c for _, c in sel])), 1),
+                "samples": len(sel),
+                "source": "amd-smi metric, GPU 0: socket power; shader clock, median over the XCDs"}
 
 
 def kernel_hash() -> str:
@@ -365,6 +419,8 @@ def main():
     # ~40 ms while the GPU raises its clocks; the timed steps measure the rate a
     # loaded GPU sustains, whatever --warmup asks for.
     settle_steps = 0
+    telemetry = Telemetry()
+    telemetry.start()
     torch.cuda.synchronize()
     t_settle = time.perf_counter()
     while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
@@ -403,6 +459,8 @@ def main():
             gemm(g)
         evs[k][1].record(stream)
     torch.cuda.synchronize()
+    # power and clock over the timed steps and the event-timed ones
+    power = telemetry.summary(t0, time.perf_counter())
     span = np.array([e[0].elapsed_time(e[1]) for e in evs])
     mmq_in_step = np.array([e[2].elapsed_time(e[1]) for e in evs])
 
@@ -517,6 +575,7 @@ def main():
         },
         "plane_bytes": sum(w.plane_bytes for w in weights.values()),
         "raw_weight_bytes": sum(w.raw_bytes for w in weights.values()),
+        "telemetry": power,
     }
     # per weight type (registration type): its GEMMs' ops over their
     # back-to-back times, against the int8 peak (and below, its chunk-step roof)
@@ -562,6 +621,20 @@ def main():
                                 "frac_of_measured": round(mmq_tops / chunk_roof, 4)}
             for name, e in per_type.items():
                 rl["per_type"][name]["chunk_roof_frac"] = round(rl["per_type"][name]["tops"] / chunk[e["type"]], 4)
+            # the same roofs at the shader clock the steps ran at (the chunk-step
+            # kernels run near 2.3 GHz; a loaded GPU at its power limit runs
+            # lower): each type's roof scaled by the clock ratio
+            cal_ghz = {synth.Q6_K: cal["chunk_q6k"].get("clock_ghz"), synth.Q4_K: cal["chunk_q4k"].get("clock_ghz"),
+                       synth.Q4_K_PACKED: cal["chunk_q4k"].get("clock_ghz")}
+            if power is not None and all(cal_ghz[t] for _, t, _, _, _ in gemms):
+                f = power["gfx_mhz_median"] / 1e3
+                at_clock = {t: chunk[t] * f / cal_ghz[t] for t in chunk if cal_ghz[t]}
+                roof_f = epilogue_roof(gemms, T, at_clock.get)
+                rl["chunk_roof"]["at_step_clock"] = {"clock_ghz": round(f, 3), "measured": round(roof_f, 1),
+                                                     "frac": round(mmq_tops / roof_f, 4)}
+                for name, e in per_type.items():
+                    rl["per_type"][name]["chunk_roof_frac_at_step_clock"] = round(
+                        rl["per_type"][name]["tops"] / at_clock[e["type"]], 4)
     if not args.no_cpu:
         threads, rule = cpu_threads(args.cpu_threads)
         result["cpu_baseline"] = cpu_baseline(gemms, raws, xs, T, threads, args.cpu_macs)

@@ -52,6 +52,10 @@ def test_bench_json_line_contract():
     assert 0 < cal["chunk_q6k"]["tops"] < cal["mfma_i8"]["tops"]
     assert 0 < rl["chunk_roof"]["frac_of_measured"] < 1.05
     assert all(cal[k]["schedule"] in ("default", "max-ilp") for k in ("mfma_i8", "chunk_q4k", "chunk_q6k"))
+    # power and clock samples (null where amd-smi is missing or the run too short to sample)
+    assert "telemetry" in d
+    if d["telemetry"] is not None:
+        assert d["telemetry"]["samples"] > 0 and d["telemetry"]["gfx_mhz_median"] > 0
     # per weight type: its GEMMs' rate against the int8 peak and its own chunk-step roof
     pt = rl["per_type"]
     assert pt and set(pt) <= {"q4_K", "q6_K", "q4_K packed"}, pt
