@@ -370,9 +370,9 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   // fragments, then the code fragments, split into equal contiguous runs per
   // wave (a run stays inside one row / token block, so its source is one
   // uniform base plus immediate 1 KiB steps; with fewer weight jobs than waves,
-  // the first waves take one each); then the small region (activation scale
-  // pairs, q4_K scale and min pairs, q6_K d) in 16-byte units per lane, one job
-  // each for the first waves.
+  // the first waves take one each); then the small region in whole 1 KiB jobs
+  // of one kind each (activation scale pairs, q4_K stage records, q6_K d), one
+  // for each of the first waves.
   constexpr int kFrag = kFragA<TYPE>;
   constexpr int kPerRbA = KC * kFrag / 1024;  // weight jobs per row block and stage
   static_assert(kJobsA % kWaves == 0 || kJobsA < kWaves, "equal weight runs per wave");
@@ -459,9 +459,9 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   // min(row, c) * s(token, c), on one f16 MFMA (32x32x8) at its end (products
   // of a 6-bit integer and an f16 value: exact in f32), then times -dmin into
   // acc.  Lane half hh supplies chunks 4*hh..4*hh+3: the mins from the
-  // super-block's mins region, the scaled sums (bs) collected from the chunks'
-  // scale pairs as they pass, half hh of the lanes during the super-block's
-  // stage hh.
+  // super-block's last stage record (which holds all 8), the scaled sums (bs)
+  // collected from the chunks' scale pairs as they pass, half hh of the lanes
+  // during the super-block's stage hh.
   v2i bs = {};
   const bool lane_hi = lane >= 32;
 
