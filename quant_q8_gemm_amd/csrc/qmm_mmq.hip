@@ -775,15 +775,16 @@ MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
   // measured 0.5-1% slower there instead of 9% faster.  With no full wave (at
   // most half the slots filled, e.g. one GPU's 512-row share of a layer),
   // every tile is a tail tile.
-  const bool short_tail = tiles > 2 * slots && (tiles % slots) * 4 <= slots && g.per_cu <= 2;
+  const int64_t last = num_cus > 0 ? tiles % slots : 0;  // tiles of a partial last wave
+  const bool short_tail = tiles > 2 * slots && last > 0 && last * 4 <= slots && g.per_cu <= 2;
   if (num_cus > 0 && tiles != slots && (tiles < 2 * slots || short_tail)) {
     // the full wave stays data-parallel (whole row tiles), the row tiles after
     // it form the tail
     const int dp_rows = (int)((tiles / slots) * slots / plan.tok_tiles);
-    const int n_tail = (plan.row_tiles - dp_rows) * plan.tok_tiles;
+    const int n_tail = (plan.row_tiles - dp_rows) * plan.tok_tiles;  // > 0: tiles is no multiple of slots
     // at least one super-block per k-group in every slice: a k-group without
     // one would only wait
-    const int split = (int)std::min<int64_t>(slots / n_tail, p.nsb / g.ks);
+    const int split = n_tail > 0 ? (int)std::min<int64_t>(slots / n_tail, p.nsb / g.ks) : 1;
     if (split >= 2) {
       plan.dp_row_tiles = dp_rows;
       plan.n_tail = n_tail;

@@ -370,6 +370,8 @@ SMALL = [("q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          # of the slots, two work-groups per CU): the 100 tiles after the 61st
          # row tile split 4 ways along K, the last row tile and token tile ragged
          ("q6_K 4097x1024 T=3199", synth.Q6_K, 4097, 1024, 3199, True),
+         # exactly three full waves (1536 tiles on 512 slots): no tail at all
+         ("q6_K 4096x1024 T=3072", synth.Q6_K, 4096, 1024, 3072, False),
          # the same in the few-tile geometry (64 x 128 tiles, one work-group per
          # CU): 520 tiles on 256 slots, the 13 tiles after the 39th row tile
          # split 8 ways, the last row tile ragged
