@@ -6,7 +6,8 @@
   integer activations make every output an exact integer below 2^24);
 * f32 results within 1e-4 * sum|terms| of the oracle on every element: at small
   sizes spanning several tiles and a ragged tail, and at the full workload
-  sizes in the same launch configuration the benchmark times;
+  sizes in the same launch configuration the benchmark times, and on row
+  subsets of seeded random shapes at any size;
 * odd row counts / token tails are bit-identical prefixes, repeat runs are
   bit-identical, nothing outside the output is written.
 """
@@ -455,6 +456,60 @@ RANDOM = _random_shapes(8)
 @pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
 def test_random_shapes_all_elements(case):
     test_small_all_elements(case)
+
+
+def _sweep_shapes(n, seed=29):
+    """Seeded random shapes over the whole size range (up to 12000 rows, 12288
+    inner, 4200 tokens, log-uniform), all three registration types: every
+    geometry and tail plan turns up (many and few tiles, split ragged waves,
+    split short last waves, whole tiles)."""
+    rng = np.random.default_rng(seed)
+    types = [synth.Q4_K, synth.Q6_K, synth.Q4_K_PACKED]
+    out = []
+    for i in range(n):
+        type_ = types[i % 3]
+        big = i % 2 == 1
+        od = int(np.exp(rng.uniform(np.log(2000) if big else 0.0, np.log(12000))))
+        id_ = 256 * int(rng.integers(1, 49))
+        T = int(np.exp(rng.uniform(np.log(1000) if big else 0.0, np.log(4200))))
+        while od * T * id_ > 6e10 and T > 1:
+            T //= 2
+        out.append((f"sweep {synth.TYPE_NAMES[type_]} {od}x{id_} T={T}", type_, od, id_, T, bool(rng.integers(0, 2))))
+    return out
+
+
+SWEEP = _sweep_shapes(24)
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[c[0] for c in SWEEP])
+def test_sweep_row_subsets(case):
+    """Random shapes at any size: every token of the first and last 64 rows and
+    of two random 32-row blocks against the oracle; every output written; the
+    allocation-free entry point and a repeat call bit-identical to the first."""
+    name, type_, od, id_, T, outl = case
+    say(f"{name}: generating")
+    raw, x = synth.case(type_, od, id_, T, seed=od * 7 + T, outliers=outl)
+    w = qmm.register_weights(type_, od, id_, raw)
+    qact = gpu_quantize(x)
+    q, dh, s = check_prepass(x, qact)
+    say(f"{name}: mmq")
+    got = run_mmq(w, qact, T)
+    again = run_mmq(w, qact, T)
+    na = torch.full((T, od), float("nan"), dtype=torch.float32, device="cuda")
+    qmm.mmq_noalloc(w, qact, T, na)
+    torch.cuda.synchronize()
+    w.release()
+    assert np.array_equal(again.view(np.uint32), got.view(np.uint32)), "repeat call differs"
+    assert np.array_equal(na.cpu().numpy().view(np.uint32), got.view(np.uint32)), "noalloc differs"
+    rng = np.random.default_rng(od + T)
+    blocks = {(0, min(64, od)), (max(0, od - 64), od)}
+    for _ in range(2):
+        j0 = int(rng.integers(0, od)) // 32 * 32
+        blocks.add((j0, min(od, j0 + 32)))
+    say(f"{name}: oracle on {len(blocks)} row blocks")
+    for j0, j1 in sorted(blocks):
+        ref, A = oracle.mmq_rows(synth.block_format(type_), raw, od, id_, q, dh, s, j0, j1)
+        check_close(got[:, j0:j1], ref, A, f"{name} rows {j0}:{j1}")
 
 
 def _stratified_pairs(rng, T, od):
