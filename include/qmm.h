@@ -70,6 +70,9 @@ extern "C" {
 #define QMM_MAX_ID (1 << 20)
 #define QMM_MAX_TOKENS (1 << 20)
 
+/* Compute units a launch plan (qmm_mmq_plan) may be asked for: 1 .. QMM_MAX_CUS. */
+#define QMM_MAX_CUS 65536
+
 /* Tokens are padded to a multiple of this many in the qact buffer. */
 #define QMM_TOKEN_PAD 128
 
@@ -257,6 +260,62 @@ int qmm_stream_release(void *stream, size_t *freed_bytes);
  */
 int qmm_mmq_noalloc(const qmm_weights *w, const void *qact, size_t qact_bytes, int64_t n_tok,
                     float *out, void *stream);
+
+/* The launch plan of one MMQ (qmm_mmq, qmm_mmq_noalloc): how its output tiles
+ * map onto work-groups on a GPU of a given size, and the tail partials it needs.
+ * The tiles of the first whole waves (row tiles dp_row_tiles of them, all tokens)
+ * run one work-group each; when the tiles fill the GPU's work-group slots a
+ * whole number of times plus a small remainder, the remaining row tiles' tiles
+ * are each split along the inner dimension into `split` slices of whole
+ * super-blocks, computed by separate work-groups as f32 partial tiles that a
+ * second kernel adds. */
+typedef struct {
+    int64_t work_groups;   /* work-groups of the MMQ launch (0: an empty batch) */
+    size_t scratch_bytes;  /* tail partials the call needs, n_tail * split partial
+                              tiles of f32 (0: none); qmm_mmq_noalloc refuses a
+                              call that needs more than its 16 MiB */
+    int32_t threads;       /* threads per work-group */
+    int32_t many;          /* 1: the many-tile geometry (several work-groups per
+                              compute unit); 0: the few-tile one */
+    int32_t tile_rows;     /* output rows per tile */
+    int32_t tile_tokens;   /* tokens per tile */
+    int32_t k_groups;      /* wave groups per work-group, each taking its share
+                              of the work-group's super-blocks */
+    int32_t per_cu;        /* work-groups resident per compute unit */
+    int32_t row_tiles;     /* tiles covering the od rows ... */
+    int32_t tok_tiles;     /* ... and the n_tok tokens */
+    int32_t dp_row_tiles;  /* row tiles computed whole (== row_tiles without a tail) */
+    int32_t n_tail;        /* tiles split along the inner dimension:
+                              (row_tiles - dp_row_tiles) * tok_tiles */
+    int32_t split;         /* slices per tail tile (1: no tail) */
+    int32_t nsb;           /* super-blocks along the inner dimension, id / 256 */
+} qmm_plan;
+
+/*
+ * qmm_mmq_plan -- the plan qmm_mmq follows for a handle of this type, od and id
+ * at n_tok tokens on a GPU with num_cus compute units (the device attribute
+ * hipDeviceAttributeMultiprocessorCount; 256 on MI355X).  Host arithmetic only:
+ * no HIP call, no device needed.  For callers that size work ahead, e.g. that
+ * check that a qmm_mmq_noalloc call fits its scratch (scratch_bytes).
+ *   type, od, id, n_tok  as for qmm_register_weights and qmm_mmq
+ *   num_cus     1 .. QMM_MAX_CUS
+ *   out         receives the plan (zeroed, nsb set, for n_tok == 0)
+ * Errors: QMM_EINVAL (arguments out of range, as the other entry points check
+ * them; a shape whose tiles exceed one launch).
+ */
+int qmm_mmq_plan(int type, int64_t od, int64_t id, int64_t n_tok, int num_cus, qmm_plan *out);
+
+/*
+ * qmm_mmq_plan_work -- what work-group wg (0 <= wg < plan->work_groups) of a
+ * plan's MMQ launch computes, by the kernel's own mapping: the tile of row tile
+ * *row_tile (rows tile_rows * row_tile ...) and token tile *tok_tile, over
+ * super-blocks [*sb_begin, *sb_end) of the inner dimension (all nsb of them for
+ * a whole tile).  Host arithmetic only.  For inspection and tests of the plan.
+ * Errors: QMM_EINVAL (NULL pointers, wg out of range, a plan whose fields do
+ * not fit together).
+ */
+int qmm_mmq_plan_work(const qmm_plan *plan, int64_t wg, int32_t *row_tile, int32_t *tok_tile,
+                      int32_t *sb_begin, int32_t *sb_end);
 
 /* qmm_last_error -- message for the calling thread's last failed call ("" if
  * none).  Valid until the thread's next call into the library. */

@@ -46,7 +46,8 @@ BLOCK_BYTES = {Q4_K: 144, Q4_K_PACKED: 144, Q6_K: 210}
 # The full list of entry points include/qmm.h declares.
 EXPORTS = ("qmm_register_weights", "qmm_weights_info", "qmm_weights_export", "qmm_release_weights",
            "qmm_set_memory_cap", "qmm_qact_bytes", "qmm_quantize_activations", "qmm_mmq",
-           "qmm_mmq_noalloc", "qmm_stream_release", "qmm_last_error")
+           "qmm_mmq_noalloc", "qmm_stream_release", "qmm_mmq_plan", "qmm_mmq_plan_work", "qmm_last_error")
+MAX_CUS = 65536
 
 
 class Info(ctypes.Structure):
@@ -54,6 +55,14 @@ class Info(ctypes.Structure):
                 ("od_pad", ctypes.c_int64), ("raw_bytes", ctypes.c_size_t),
                 ("plane_bytes", ctypes.c_size_t), ("wd_offset", ctypes.c_size_t),
                 ("sm_offset", ctypes.c_size_t)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("work_groups", ctypes.c_int64), ("scratch_bytes", ctypes.c_size_t),
+                ("threads", ctypes.c_int32), ("many", ctypes.c_int32), ("tile_rows", ctypes.c_int32),
+                ("tile_tokens", ctypes.c_int32), ("k_groups", ctypes.c_int32), ("per_cu", ctypes.c_int32),
+                ("row_tiles", ctypes.c_int32), ("tok_tiles", ctypes.c_int32), ("dp_row_tiles", ctypes.c_int32),
+                ("n_tail", ctypes.c_int32), ("split", ctypes.c_int32), ("nsb", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -79,6 +88,11 @@ _lib.qmm_mmq_noalloc.argtypes = [_P, _P, _SZ, _I64, _P, _P]
 _lib.qmm_mmq_noalloc.restype = ctypes.c_int
 _lib.qmm_stream_release.argtypes = [_P, ctypes.POINTER(_SZ)]
 _lib.qmm_stream_release.restype = ctypes.c_int
+_lib.qmm_mmq_plan.argtypes = [ctypes.c_int, _I64, _I64, _I64, ctypes.c_int, ctypes.POINTER(Plan)]
+_lib.qmm_mmq_plan.restype = ctypes.c_int
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_lib.qmm_mmq_plan_work.argtypes = [ctypes.POINTER(Plan), _I64, _I32P, _I32P, _I32P, _I32P]
+_lib.qmm_mmq_plan_work.restype = ctypes.c_int
 _lib.qmm_last_error.argtypes = []
 _lib.qmm_last_error.restype = ctypes.c_char_p
 
@@ -225,3 +239,19 @@ def stream_release(stream=None) -> int:
     freed = _SZ(0)
     _check(_lib.qmm_stream_release(_stream(stream), ctypes.byref(freed)))
     return int(freed.value)
+
+
+def mmq_plan(type_: int, od: int, id_: int, n_tok: int, num_cus: int) -> Plan:
+    """The launch plan qmm_mmq follows for this shape on a GPU with num_cus
+    compute units (host arithmetic only; no device needed)."""
+    plan = Plan()
+    _check(_lib.qmm_mmq_plan(int(type_), int(od), int(id_), int(n_tok), int(num_cus), ctypes.byref(plan)))
+    return plan
+
+
+def mmq_plan_work(plan: Plan, wg: int):
+    """(row tile, token tile, first super-block, end super-block) that
+    work-group wg of the plan's launch computes."""
+    out = [ctypes.c_int32() for _ in range(4)]
+    _check(_lib.qmm_mmq_plan_work(ctypes.byref(plan), int(wg), *[ctypes.byref(o) for o in out]))
+    return tuple(o.value for o in out)

@@ -85,6 +85,41 @@ int check_tokens(int64_t n_tok) {
 
 int64_t token_pad(int64_t n_tok) { return (n_tok + qmm::kTokenPad - 1) / qmm::kTokenPad * qmm::kTokenPad; }
 
+int check_type(int type) {
+  if (type != QMM_Q4_K && type != QMM_Q4_K_PACKED && type != QMM_Q6_K)
+    return fail(QMM_EINVAL, "type must be QMM_Q4_K (%d), QMM_Q4_K_PACKED (%d) or QMM_Q6_K (%d), got %d",
+                QMM_Q4_K, QMM_Q4_K_PACKED, QMM_Q6_K, type);
+  return QMM_OK;
+}
+
+int check_od(int64_t od) {
+  if (od < 1 || od > QMM_MAX_OD)
+    return fail(QMM_EINVAL, "od must be in [1, %d], got %lld", QMM_MAX_OD, (long long)od);
+  return QMM_OK;
+}
+
+// The geometry part of a handle's planes (no memory): what the plan needs.
+qmm::Planes plane_shape(int type, int64_t od, int64_t id) {
+  qmm::Planes p{};
+  p.type = type;
+  p.od = od;
+  p.id = id;
+  p.od_pad = (int64_t)round_up((size_t)od, qmm::kRowPad);
+  p.nsb = id / 256;
+  p.nchunk = id / 32;
+  return p;
+}
+
+// one-dimensional launch: work-groups x threads must stay below 2^32
+int check_launch(const qmm::MmqPlan& plan, int64_t n_tok, int64_t od, int num_cus) {
+  if ((uint64_t)plan.work_groups * (uint64_t)plan.threads >= (1ull << 32))
+    return fail(QMM_EINVAL, "n_tok=%lld x od=%lld needs %lld work-groups, more than one launch holds",
+                (long long)n_tok, (long long)od, (long long)plan.work_groups);
+  if (plan.scratch_bytes > qmm::mmq_scratch_max_bytes(num_cus))
+    return fail(QMM_EINVAL, "internal: tail scratch exceeds its bound");
+  return QMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,24 +137,15 @@ int qmm_register_weights(int type, int64_t od, int64_t id, const void* host_byte
                          void* stream, qmm_weights** out) {
   if (out == nullptr) return fail(QMM_EINVAL, "out is NULL");
   *out = nullptr;
-  if (type != QMM_Q4_K && type != QMM_Q4_K_PACKED && type != QMM_Q6_K)
-    return fail(QMM_EINVAL, "type must be QMM_Q4_K (%d), QMM_Q4_K_PACKED (%d) or QMM_Q6_K (%d), got %d",
-                QMM_Q4_K, QMM_Q4_K_PACKED, QMM_Q6_K, type);
-  if (od < 1 || od > QMM_MAX_OD)
-    return fail(QMM_EINVAL, "od must be in [1, %d], got %lld", QMM_MAX_OD, (long long)od);
+  if (int rc = check_type(type)) return rc;
+  if (int rc = check_od(od)) return rc;
   if (int rc = check_id(id)) return rc;
   if (host_bytes == nullptr) return fail(QMM_EINVAL, "host_bytes is NULL");
   const size_t expect = (size_t)od * (size_t)(id / 256) * block_bytes(type);
   if (nbytes != expect)
     return fail(QMM_EINVAL, "nbytes %zu != od*(id/256)*%zu = %zu", nbytes, block_bytes(type), expect);
 
-  qmm::Planes p{};
-  p.type = type;
-  p.od = od;
-  p.id = id;
-  p.od_pad = (int64_t)round_up((size_t)od, qmm::kRowPad);
-  p.nsb = id / 256;
-  p.nchunk = id / 32;
+  qmm::Planes p = plane_shape(type, od, id);
   // q6_K: codes, d; q4_K: codes, stage records (one of the last two is empty)
   const size_t off_wd = round_up(qmm::wq_bytes(type, p.od_pad, id), 256);
   const size_t off_sm = off_wd + round_up(qmm::wd_bytes(type, p.od_pad, id), 256);
@@ -283,12 +309,7 @@ int prepare_mmq(const qmm_weights* w, const void* qact, size_t qact_bytes, int64
   e = hipDeviceGetAttribute(num_cus, hipDeviceAttributeMultiprocessorCount, *device);
   if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(multiprocessor count)");
   *plan = qmm::plan_mmq(w->p, n_tok, *num_cus);
-  // one-dimensional launch: work-groups x threads must stay below 2^32
-  if ((uint64_t)plan->work_groups * (uint64_t)plan->threads >= (1ull << 32))
-    return fail(QMM_EINVAL, "n_tok=%lld x od=%lld needs %lld work-groups, more than one launch holds",
-                (long long)n_tok, (long long)w->p.od, (long long)plan->work_groups);
-  if (plan->scratch_bytes > qmm::mmq_scratch_max_bytes(*num_cus))
-    return fail(QMM_EINVAL, "internal: tail scratch exceeds its bound");
+  if (int rc = check_launch(*plan, n_tok, w->p.od, *num_cus)) return rc;
   *launch = true;
   return QMM_OK;
 }
@@ -383,6 +404,68 @@ int qmm_mmq_noalloc(const qmm_weights* w, const void* qact, size_t qact_bytes, i
   hipError_t e = qmm::launch_mmq(w->p, plan, (const uint8_t*)qact, n_tok, token_pad(n_tok), out, part,
                                  (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "mmq launch");
+  ok();
+  return QMM_OK;
+}
+
+int qmm_mmq_plan(int type, int64_t od, int64_t id, int64_t n_tok, int num_cus, qmm_plan* out) {
+  if (out == nullptr) return fail(QMM_EINVAL, "out is NULL");
+  std::memset(out, 0, sizeof *out);
+  if (int rc = check_type(type)) return rc;
+  if (int rc = check_od(od)) return rc;
+  if (int rc = check_id(id)) return rc;
+  if (int rc = check_tokens(n_tok)) return rc;
+  if (num_cus < 1 || num_cus > QMM_MAX_CUS)
+    return fail(QMM_EINVAL, "num_cus must be in [1, %d], got %d", QMM_MAX_CUS, num_cus);
+  out->nsb = (int32_t)(id / 256);
+  if (n_tok == 0) {  // an empty batch launches nothing
+    ok();
+    return QMM_OK;
+  }
+  const qmm::MmqPlan plan = qmm::plan_mmq(plane_shape(type, od, id), n_tok, num_cus);
+  if (int rc = check_launch(plan, n_tok, od, num_cus)) return rc;
+  out->work_groups = plan.work_groups;
+  out->scratch_bytes = plan.scratch_bytes;
+  out->threads = plan.threads;
+  out->many = plan.many ? 1 : 0;
+  out->tile_rows = plan.tile_rows;
+  out->tile_tokens = plan.tile_tokens;
+  out->k_groups = plan.k_groups;
+  out->per_cu = plan.per_cu;
+  out->row_tiles = plan.row_tiles;
+  out->tok_tiles = plan.tok_tiles;
+  out->dp_row_tiles = plan.dp_row_tiles;
+  out->n_tail = plan.n_tail;
+  out->split = plan.split;
+  ok();
+  return QMM_OK;
+}
+
+int qmm_mmq_plan_work(const qmm_plan* plan, int64_t wg, int32_t* row_tile, int32_t* tok_tile, int32_t* sb_begin,
+                      int32_t* sb_end) {
+  if (plan == nullptr || row_tile == nullptr || tok_tile == nullptr || sb_begin == nullptr || sb_end == nullptr)
+    return fail(QMM_EINVAL, "plan or an output pointer is NULL");
+  const qmm_plan& q = *plan;
+  const bool consistent = q.nsb >= 1 && q.tok_tiles >= 1 && q.dp_row_tiles >= 0 && q.n_tail >= 0 &&
+                          q.split >= 1 && (q.n_tail > 0) == (q.split > 1) && q.split <= q.nsb &&
+                          q.n_tail % q.tok_tiles == 0 && q.dp_row_tiles + q.n_tail / q.tok_tiles == q.row_tiles &&
+                          q.work_groups == (int64_t)q.dp_row_tiles * q.tok_tiles + (int64_t)q.n_tail * q.split &&
+                          q.work_groups < ((int64_t)1 << 31);
+  if (!consistent) return fail(QMM_EINVAL, "plan is not one qmm_mmq_plan wrote");
+  if (wg < 0 || wg >= q.work_groups)
+    return fail(QMM_EINVAL, "work-group %lld outside the launch's %lld", (long long)wg, (long long)q.work_groups);
+  qmm::MmqPlan p{};
+  p.row_tiles = q.row_tiles;
+  p.tok_tiles = q.tok_tiles;
+  p.dp_row_tiles = q.dp_row_tiles;
+  p.n_tail = q.n_tail;
+  p.split = q.split;
+  int rt = 0, tt = 0, s0 = 0, s1 = 0;
+  qmm::plan_work(p, q.nsb, wg, &rt, &tt, &s0, &s1);
+  *row_tile = rt;
+  *tok_tile = tt;
+  *sb_begin = s0;
+  *sb_end = s1;
   ok();
   return QMM_OK;
 }

@@ -49,6 +49,9 @@ hipError_t launch_quantize(const float* x, int64_t n_tok, int64_t t_pad, int64_t
 // tail tiles and the scratch they need (n_tail tiles x split partials).
 struct MmqPlan {
   bool many;          // many tiles: the many-tile shapes, else 64 x 128 tiles in two k-groups
+  int tile_rows, tile_tokens;  // output rows and tokens per tile
+  int k_groups;       // wave groups per work-group, each over its share of a tile's super-blocks
+  int per_cu;         // work-groups resident per compute unit
   int row_tiles, tok_tiles;
   int dp_row_tiles;   // row tiles computed whole
   int n_tail;         // tiles after them, each split along K
@@ -58,6 +61,10 @@ struct MmqPlan {
   int threads;          // per work-group
 };
 MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus);
+// What work-group wg (0 <= wg < plan.work_groups) of the plan's MMQ launch
+// computes, by the kernel's own mapping: tile (rt, tt) over super-blocks
+// [sb0, sb1) of nsb.
+void plan_work(const MmqPlan& plan, int nsb, int64_t wg, int* rt, int* tt, int* sb0, int* sb1);
 // Upper bound of MmqPlan::scratch_bytes on a device with num_cus compute units.
 size_t mmq_scratch_max_bytes(int num_cus);
 hipError_t launch_mmq(const Planes& p, const MmqPlan& plan, const uint8_t* qact, int64_t n_tok,

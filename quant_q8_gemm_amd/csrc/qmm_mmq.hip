@@ -235,18 +235,46 @@ __device__ __forceinline__ v16f scale_outer(v2i a_sc, uint32_t dh_bits, int cc) 
 // share both their weight rows and their activations in that L2.
 constexpr int kGroupRows = 8;
 
-__device__ __forceinline__ int xcd_swizzle(int i, int n) {
+__host__ __device__ __forceinline__ int xcd_swizzle(int i, int n) {
   const int q = n / 8, r = n % 8;
   const int x = i % 8, slot = i / 8;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + slot;
 }
 
-__device__ __forceinline__ void tile_of(int pos, int row_tiles, int tok_tiles, int& rt, int& tt) {
+__host__ __device__ __forceinline__ void tile_of(int pos, int row_tiles, int tok_tiles, int& rt, int& tt) {
   const int per_group = kGroupRows * tok_tiles;
   const int g = pos / per_group, idx = pos % per_group;
-  const int rows_here = min(kGroupRows, row_tiles - g * kGroupRows);  // last group may be short
+  const int left = row_tiles - g * kGroupRows;
+  const int rows_here = left < kGroupRows ? left : kGroupRows;  // last group may be short
   rt = g * kGroupRows + idx % rows_here;
   tt = idx / rows_here;
+}
+
+// What work-group wg computes: a whole tile of the data-parallel part (the
+// first dp_row_tiles * tok_tiles work-groups, walked as above), or one K slice
+// of a tail tile -- the tail's work-groups take its tiles in order, split
+// consecutive slices each, slice sl holding super-blocks
+// [sl*nsb/split, (sl+1)*nsb/split).  tail: the work-group's index among the
+// tail's (its partial tile's slot in the scratch), negative for a whole tile.
+struct Work {
+  int rt, tt, sb0, sb1, tail;
+};
+__host__ __device__ __forceinline__ Work work_of(int wg, int dp_row_tiles, int tok_tiles, int split, int nsb) {
+  Work w;
+  const int dp_tiles = dp_row_tiles * tok_tiles;
+  w.tail = wg - dp_tiles;
+  if (w.tail < 0) {
+    tile_of(xcd_swizzle(wg, dp_tiles), dp_row_tiles, tok_tiles, w.rt, w.tt);
+    w.sb0 = 0;
+    w.sb1 = nsb;
+  } else {
+    const int u = w.tail / split, sl = w.tail % split;
+    w.rt = dp_row_tiles + u / tok_tiles;
+    w.tt = u % tok_tiles;
+    w.sb0 = sl * nsb / split;
+    w.sb1 = (sl + 1) * nsb / split;
+  }
+  return w;
 }
 
 // Output layout of a wave's 32 x 32 block: lane holds token (lane & 31) and,
@@ -344,18 +372,9 @@ mmq_kernel(const int8_t* __restrict__ wq, const float* __restrict__ wd,
   const int wr = wave / WT, wt = wave % WT;
   St* stage = stage_all[ks];
   // role: a whole tile of the data-parallel part, or one K slice of a tail tile
-  const int dp_tiles = dp_row_tiles * tok_tiles;
-  const int tail_idx = (int)blockIdx.x - dp_tiles;  // >= 0: index into the partials
-  int rt, tt, sb0 = 0, sb1 = nsb;
-  if (tail_idx < 0) {
-    tile_of(xcd_swizzle(blockIdx.x, dp_tiles), dp_row_tiles, tok_tiles, rt, tt);
-  } else {
-    const int u = tail_idx / split, sl = tail_idx % split;
-    rt = dp_row_tiles + u / tok_tiles;
-    tt = u % tok_tiles;
-    sb0 = sl * nsb / split;
-    sb1 = (sl + 1) * nsb / split;
-  }
+  const Work work = work_of((int)blockIdx.x, dp_row_tiles, tok_tiles, split, nsb);
+  const int tail_idx = work.tail;  // >= 0: index into the partials
+  const int rt = work.rt, tt = work.tt, sb0 = work.sb0, sb1 = work.sb1;
   const int rb0 = rt * WR, tb0 = tt * WT;
   // k-group ks owns super-blocks [sb0 + ks*n/KS, sb0 + (ks+1)*n/KS) of the n in
   // this work-group's range; the last group has the most, so every wave runs its
@@ -794,7 +813,19 @@ MmqPlan plan_mmq(const Planes& p, int64_t n_tok, int num_cus) {
   }
   plan.work_groups = (int64_t)plan.dp_row_tiles * plan.tok_tiles + (int64_t)plan.n_tail * plan.split;
   plan.threads = 64 * g.wr * g.wt * g.ks;
+  plan.tile_rows = 32 * g.wr;
+  plan.tile_tokens = 32 * g.wt;
+  plan.k_groups = g.ks;
+  plan.per_cu = g.per_cu;
   return plan;
+}
+
+void plan_work(const MmqPlan& plan, int nsb, int64_t wg, int* rt, int* tt, int* sb0, int* sb1) {
+  const Work w = work_of((int)wg, plan.dp_row_tiles, plan.tok_tiles, plan.split, nsb);
+  *rt = w.rt;
+  *tt = w.tt;
+  *sb0 = w.sb0;
+  *sb1 = w.sb1;
 }
 
 // n_tail * split work-groups, at most one per slot, each with one partial tile:

@@ -7,10 +7,12 @@ return code (a sanitizer report aborts the process by itself).
     python abi_driver.py <path to libqmm build>
 """
 import ctypes
+import math
+import random
 import sys
 
 EINVAL, ESHAPE, ENOMEM = -1, -2, -3
-Q4_K, Q6_K = 4, 6
+Q4_K, Q6_K, Q4_K_PACKED = 4, 6, 14
 
 
 def main(path):
@@ -78,11 +80,44 @@ def main(path):
     expect("stream release, nothing held", L.qmm_stream_release(good, good), 0)
     expect("stream release, freed count", ctypes.cast(good, ctypes.POINTER(SZ))[0], 0)
     expect("stream release, null stream", L.qmm_stream_release(None, None), 0)
+    # the launch planner, host arithmetic only: seeded shapes over the accepted
+    # range on several GPU sizes, every work-group of the small launches mapped
+    # (undefined behaviour -- a division by zero, an overflow -- aborts)
+    L.qmm_mmq_plan.argtypes = [ctypes.c_int, I64, I64, I64, ctypes.c_int, ctypes.POINTER(Plan)]
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    L.qmm_mmq_plan_work.argtypes = [ctypes.POINTER(Plan), I64, I32P, I32P, I32P, I32P]
+    rng = random.Random(7)
+    plan = Plan()
+    out = [ctypes.c_int32() for _ in range(4)]
+    mapped = 0
+    for i in range(3000):
+        type_ = (Q4_K, Q6_K, Q4_K_PACKED)[i % 3]
+        od = int(math.exp(rng.uniform(0, math.log(1 << 21))))
+        id_ = 256 * int(math.exp(rng.uniform(0, math.log(4096))))
+        n_tok = int(math.exp(rng.uniform(0, math.log(20000))))
+        cus = rng.choice((1, 3, 80, 256, 304))
+        rc = L.qmm_mmq_plan(type_, od, id_, n_tok, cus, ctypes.byref(plan))
+        expect(f"plan {type_} {od}x{id_} T={n_tok} cus={cus}", rc, 0)
+        if rc == 0 and plan.work_groups <= 4000:
+            for wg in range(plan.work_groups):
+                expect("plan work", L.qmm_mmq_plan_work(ctypes.byref(plan), wg, *[ctypes.byref(o) for o in out]), 0)
+            mapped += 1
+    expect("plans mapped", mapped > 100, True)
+    expect("plan bad cus", L.qmm_mmq_plan(Q4_K, 4096, 4096, 512, 0, ctypes.byref(plan)), EINVAL)
+    expect("plan too big", L.qmm_mmq_plan(Q4_K, 1 << 21, 256, 1 << 20, 256, ctypes.byref(plan)), EINVAL)
+    expect("plan null", L.qmm_mmq_plan(Q4_K, 4096, 4096, 512, 256, None), EINVAL)
+    expect("plan work null", L.qmm_mmq_plan_work(None, 0, *[ctypes.byref(o) for o in out]), EINVAL)
     if bad:
         print("\n".join(bad))
         return 1
     print("abi driver: all validation paths returned the documented codes")
     return 0
+
+
+class Plan(ctypes.Structure):  # qmm_plan
+    _fields_ = [("work_groups", ctypes.c_int64), ("scratch_bytes", ctypes.c_size_t)] + [
+        (n, ctypes.c_int32) for n in ("threads", "many", "tile_rows", "tile_tokens", "k_groups", "per_cu",
+                                      "row_tiles", "tok_tiles", "dp_row_tiles", "n_tail", "split", "nsb")]
 
 
 def buf_addr(buf):

@@ -364,7 +364,8 @@ SMALL = [("q6_K 256x512 T=64", synth.Q6_K, 256, 512, 64, False),
          ("q4_K 512x3072 T=300", synth.Q4_K, 512, 3072, 300, True),
          # enough 64 x 64 tiles (>= 1024) to select the many-tile geometry;
          # q6_K there runs 64 x 128 tiles two per CU: 528 tiles on 512 slots
-         # (a split tail), and 1088 tiles (two full waves and a ragged third)
+         # (a split tail), and 1056 tiles (two full waves and a last of 32,
+         # whole: one super-block leaves nothing to split)
          ("q6_K 1000x512 T=4100", synth.Q6_K, 1000, 512, 4100, True),
          ("q6_K 2100x256 T=4000", synth.Q6_K, 2100, 256, 4000, False),
          # three full waves of 512 tiles and a last wave of 89 (at most a quarter
@@ -647,7 +648,7 @@ def test_concurrent_streams_share_a_handle():
     needs the tail scratch (one buffer per stream): both results equal the
     single-stream result, repeatedly."""
     say("two streams, one handle, tail scratch")
-    type_, od, id_, T = synth.Q6_K, 4200, 768, 500
+    type_, od, id_, T = synth.Q6_K, 4097, 2048, 509  # 260 tiles on 256 CUs: the tail splits 4 ways
     raw, x = synth.case(type_, od, id_, T, seed=5)
     w = qmm.register_weights(type_, od, id_, raw)
     qact = gpu_quantize(x)
@@ -662,6 +663,9 @@ def test_concurrent_streams_share_a_handle():
         torch.cuda.synchronize()
         for o in outs:
             assert np.array_equal(o.cpu().numpy(), ref)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    if qmm.mmq_plan(type_, od, id_, T, n_cu).scratch_bytes:  # each stream held its own scratch
+        assert [qmm.stream_release(st) for st in streams] == [n_cu * 64 * 1024] * 2
     w.release()
 
 
