@@ -140,6 +140,8 @@ def _parse():
     ap.add_argument("--workload", default="layer", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-weights pass")
+    ap.add_argument("--no-telemetry", action="store_true",
+                    help="do not sample power and clock (never sampled under rocprofv3)")
     ap.add_argument("--no-calib", action="store_true",
                     help="skip the measured MFMA and epilogue roofs (calibration kernels)")
     ap.add_argument("--cpu-threads", type=int, default=0,
@@ -155,15 +157,18 @@ class Telemetry:
     `amd-smi metric` started as a child process in a background thread (about
     three samples per second); absent tool or unparsable output: no samples."""
 
-    def __init__(self):
+    def __init__(self, enabled=True):
         exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
-        self.exe = exe if os.path.exists(exe) else None
+        exe = os.path.realpath(exe) if os.path.exists(exe) else None
+        # the tool is a Python script: run it with this interpreter rather than
+        # through its "#!/usr/bin/env" line, one program start fewer
+        self.cmd = None if exe is None or not enabled else ([sys.executable, exe] if exe.endswith(".py") else [exe])
         self.samples = []
         self.stop = threading.Event()
         self.thread = None
 
     def start(self):
-        if self.exe is not None:
+        if self.cmd is not None:
             self.thread = threading.Thread(target=self._run, daemon=True)
             self.thread.start()
 
@@ -171,7 +176,7 @@ class Telemetry:
         while not self.stop.is_set():
             t = time.perf_counter()
             try:
-                r = subprocess.run([self.exe, "metric", "-g", "0", "--power", "--clock", "--json"],
+                r = subprocess.run(self.cmd + ["metric", "-g", "0", "--power", "--clock", "--json"],
                                    capture_output=True, text=True, timeout=10)
                 d = json.loads(r.stdout)
                 d = d[0] if isinstance(d, list) else d
@@ -419,7 +424,10 @@ def main():
     # ~40 ms while the GPU raises its clocks; the timed steps measure the rate a
     # loaded GPU sustains, whatever --warmup asks for.
     settle_steps = 0
-    telemetry = Telemetry()
+    # no sampler under a profiler: its preloaded library would initialise the GPU
+    # in every child process too
+    profiled = any(k.startswith("ROCPROF") for k in os.environ)
+    telemetry = Telemetry(enabled=not (args.no_telemetry or profiled))
     telemetry.start()
     torch.cuda.synchronize()
     t_settle = time.perf_counter()
