@@ -669,6 +669,48 @@ def test_concurrent_streams_share_a_handle():
     w.release()
 
 
+def test_noalloc_under_graph_capture():
+    """The allocation-free MMQ inside a captured HIP graph, the use it exists
+    for: the prepass and a launch whose tail tiles are split into the static
+    scratch, captured once and replayed three times, with eager work (poisoning
+    the output and the qact buffer) and a synchronization between replays;
+    every replay gives the eager result bit for bit."""
+    say("noalloc under graph capture")
+    type_, od, id_, T = synth.Q6_K, 4097, 2048, 509  # 260 tiles on 256 CUs: the tail splits 4 ways
+    raw, x = synth.case(type_, od, id_, T, seed=61)
+    w = qmm.register_weights(type_, od, id_, raw)
+    xt = torch.from_numpy(x).cuda()
+    qact = torch.empty(qmm.qact_bytes(T, id_), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, od), dtype=torch.float32, device="cuda")
+    # eager reference; the first call on the device also looks up the static
+    # scratch's address, outside the capture
+    qmm.quantize_activations(xt, qact)
+    qmm.mmq_noalloc(w, qact, T, out)
+    torch.cuda.synchronize()
+    ref = out.cpu().numpy().copy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream before capturing
+        qmm.quantize_activations(xt, qact, stream=side)
+        qmm.mmq_noalloc(w, qact, T, out, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        qmm.quantize_activations(xt, qact)
+        qmm.mmq_noalloc(w, qact, T, out)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        qact.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)), f"replay {i} differs"
+    del graph
+    w.release()
+
+
 def test_tail_scratch_shared_across_shapes():
     """Launches with different tail tile counts and splits (260 tiles on 256
     CUs with the tail split 4 ways, 24 tiles all split, a q4_K shape with its
