@@ -13,6 +13,8 @@
 // stored value is exact whatever the spread of d and dmin along a row.  q4_K's
 // scales, mins, d and dmin are grouped into one 1 KiB record per 32-row block
 // and GEMM stage, which one wave copies to LDS with a single uniform load.
+#include <algorithm>
+
 #include "qmm_internal.h"
 #include "qmm_common.h"
 
@@ -97,12 +99,10 @@ __device__ __forceinline__ void q4k_record(uint8_t* wsm, int rb, int nchunk, int
 }
 
 // One thread per (row j in [0, od_pad), chunk c, k-half h): 16 weights.
-__global__ void __launch_bounds__(256)
-repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nchunk,
-              int64_t total, int8_t* __restrict__ wq, float* __restrict__ wd,
-              uint8_t* __restrict__ wsm) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= total) return;
+// One (row, 32-block, 16-weight half) of the planes: item gid.
+__device__ __forceinline__ void repack_one(int64_t gid, const uint8_t* __restrict__ raw, int type, int od, int nsb,
+                                           int nchunk, int8_t* __restrict__ wq, float* __restrict__ wd,
+                                           uint8_t* __restrict__ wsm) {
   const int h = (int)(gid & 1);
   const int64_t rc = gid >> 1;
   const int c = (int)(rc % nchunk);
@@ -172,9 +172,26 @@ repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nc
   }
 }
 
+// Items [0, total) over a grid of at most kRepackMaxBlocks work-groups (4M
+// threads, eight times what the GPU holds at once), each thread striding by the
+// grid's size: a launch stays far inside the 2^32 work-items one dispatch
+// holds, whatever the matrix (2^37 items at the largest od and id), and every
+// matrix above 4M items (e.g. a 32000 x 4096 output head: 8.2M) takes the
+// stride.
+constexpr int64_t kRepackMaxBlocks = 1 << 14;
+
+__global__ void __launch_bounds__(256)
+repack_kernel(const uint8_t* __restrict__ raw, int type, int od, int nsb, int nchunk,
+              int64_t total, int8_t* __restrict__ wq, float* __restrict__ wd,
+              uint8_t* __restrict__ wsm) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < total; gid += stride)
+    repack_one(gid, raw, type, od, nsb, nchunk, wq, wd, wsm);
+}
+
 hipError_t launch_repack(const uint8_t* raw, const Planes& p, hipStream_t s) {
   const int64_t total = p.od_pad * p.nchunk * 2;
-  const int64_t blocks = (total + 255) / 256;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, kRepackMaxBlocks);
   repack_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
       raw, p.type, (int)p.od, (int)p.nsb, (int)p.nchunk, total, p.wq, p.wd, p.wsm);
   return hipGetLastError();

@@ -167,7 +167,10 @@ def check_planes(w, type_, raw, od, id_):
 @pytest.mark.parametrize("type_,od,id_,full", [(synth.Q6_K, 5, 512, False), (synth.Q6_K, 130, 768, True),
                                                (synth.Q4_K, 37, 512, False), (synth.Q4_K, 129, 1024, False),
                                                (synth.Q4_K_PACKED, 37, 512, False),
-                                               (synth.Q4_K_PACKED, 129, 1024, False)])
+                                               (synth.Q4_K_PACKED, 129, 1024, False),
+                                               # above the repack grid's 4M items: threads stride
+                                               (synth.Q6_K, 16400, 8192, False), (synth.Q4_K, 16400, 8192, False),
+                                               (synth.Q4_K_PACKED, 8193, 8192, False)])
 def test_planes_byte_exact(type_, od, id_, full):
     say(f"planes type={type_} od={od} id={id_}")
     rng = np.random.default_rng(od)
