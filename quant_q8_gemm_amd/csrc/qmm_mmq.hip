@@ -157,7 +157,11 @@ struct WeightOps<QMM_Q6_K> {
 // |D| <= 32*15*127 = 60960 is far inside the 2291075 steps below and 6097533
 // above it that its binade [1/8, 1/4) holds, the f32 value of the result's bits
 // is kQ4Bias + D*2^-26 exactly.  Subtracting kQ4Bias is exact (both within a
-// factor of two), so val() = D*2^-26 with one full-rate subtraction.
+// factor of two), so val() = D*2^-26 with one full-rate subtraction, written
+// as -(kQ4Bias - x): the subtraction then takes kQ4Bias as an inline constant
+// (x - kQ4Bias would need -1/(2 pi), a 32-bit literal in every instruction),
+// and the negation folds into the scale FMA's operand (it cannot be folded back
+// into x - kQ4Bias: the two differ in the sign of a zero result).
 // The compiler encodes the splat as the inline constant only for an MFMA whose
 // accumulator input is used by no other instruction of its basic block; an
 // empty asm goto after each such MFMA ends its block without emitting an
@@ -187,7 +191,7 @@ struct WeightOps<QMM_Q4_K> {
   // element of an ext-vector reads element 0 whatever the index)
   __device__ static float val(const D& d, int i) {
     const v16f f = __builtin_bit_cast(v16f, d.c);
-    return f[i] - __builtin_bit_cast(float, kQ4BiasBits);
+    return -(__builtin_bit_cast(float, kQ4BiasBits) - f[i]);
   }
 };
 

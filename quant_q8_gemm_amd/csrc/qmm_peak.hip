@@ -8,9 +8,10 @@
 //           and accumulate with the activation scale held as f32 (v_fmac_f32)
 //           -- on 16 elements per lane;
 //   kind 2: the q4_K MMQ's epilogue over one 256-wide super-block (8 chunks):
-//           per chunk and element, subtract the accumulator bias from the block
-//           dot (v_add_f32 with a literal) and multiply by the element's own f32
-//           scale product and accumulate (v_fmac_f32); per super-block and
+//           per chunk and element, subtract the block dot from the accumulator
+//           bias (v_sub_f32 with the bias as an inline constant), multiply the
+//           negated difference by the element's own f32 scale product and
+//           accumulate (v_fma_f32 with a negated operand); per super-block and
 //           element, two more FMAs (apply d, add the min term times -dmin) --
 //           2.25 instructions per (token, row, 32-block), on 16 elements per lane;
 //   kind 3: the q4_K MMQ's whole chunk step without its memory traffic: the
@@ -116,7 +117,7 @@ __global__ void __launch_bounds__(256) peak_epilogue_q4(int iters, unsigned long
     for (int c = 0; c < 8; ++c) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)  // the "block dot" is inner's own value: it changes every step
-        inner[i] = fmaf(inner[i] - c0, sc[i], inner[i]);
+        inner[i] = fmaf(-(c0 - inner[i]), sc[i], inner[i]);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -263,13 +264,13 @@ peak_chunk(int iters, unsigned long long* clk, int* sink) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             if constexpr (Q6) inner[i] = (float)((dj.d[i] << 6) + dj.d2[i]) * dh;
-            else inner[i] = (df[i] - __builtin_bit_cast(float, kBiasBits)) * sd[i];
+            else inner[i] = -(__builtin_bit_cast(float, kBiasBits) - df[i]) * sd[i];
           }
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             if constexpr (Q6) inner[i] = fmaf((float)((dj.d[i] << 6) + dj.d2[i]), dh, inner[i]);
-            else inner[i] = fmaf(df[i] - __builtin_bit_cast(float, kBiasBits), sd[i], inner[i]);
+            else inner[i] = fmaf(-(__builtin_bit_cast(float, kBiasBits) - df[i]), sd[i], inner[i]);
           }
         }
         pin(inner);
