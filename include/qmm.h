@@ -263,12 +263,16 @@ int qmm_mmq_noalloc(const qmm_weights *w, const void *qact, size_t qact_bytes, i
 
 /* The launch plan of one MMQ (qmm_mmq, qmm_mmq_noalloc): how its output tiles
  * map onto work-groups on a GPU of a given size, and the tail partials it needs.
- * The tiles of the first whole waves (row tiles dp_row_tiles of them, all tokens)
- * run one work-group each; when the tiles fill the GPU's work-group slots a
- * whole number of times plus a small remainder, the remaining row tiles' tiles
- * are each split along the inner dimension into `split` slices of whole
- * super-blocks, computed by separate work-groups as f32 partial tiles that a
- * second kernel adds. */
+ * The slots are the work-groups resident at once (per_cu per compute unit).  The
+ * tiles of the whole waves, rounded down to whole row tiles (dp_row_tiles of
+ * them, all tokens), run one work-group each.  The remaining row tiles' tiles
+ * are split along the inner dimension into `split` slices of whole super-blocks,
+ * computed by separate work-groups as f32 partial tiles that a second kernel
+ * adds, when they form a partial wave: after at most one full wave (none
+ * included: a launch filling at most half the GPU splits every tile), or, with
+ * one or two work-groups per compute unit, a last wave of at most a quarter of
+ * the slots behind several full ones -- and when there are at least two slices
+ * to make (every wave group of a slice keeps a super-block). */
 typedef struct {
     int64_t work_groups;   /* work-groups of the MMQ launch (0: an empty batch) */
     size_t scratch_bytes;  /* tail partials the call needs, n_tail * split partial
