@@ -572,6 +572,40 @@ def test_full_size_all_elements(cfg):
     check_close(got, ref, A, name)
 
 
+# The API's maximum sizes, each on every element: QMM_MAX_OD rows (32,768 row
+# tiles), QMM_MAX_ID inner (4,096 super-blocks; one tile, split 256 ways along
+# K, also through the allocation-free entry point), QMM_MAX_TOKENS tokens
+# (16,384 token tiles).
+MAXIMA = [("q6_K od=2^21 id=256 T=3", synth.Q6_K, 1 << 21, 256, 3),
+          ("q4_K packed od=2^21 id=256 T=1", synth.Q4_K_PACKED, 1 << 21, 256, 1),
+          ("q4_K od=33 id=2^20 T=5", synth.Q4_K, 33, 1 << 20, 5),
+          ("q6_K od=33 id=2^20 T=5", synth.Q6_K, 33, 1 << 20, 5),
+          ("q4_K od=1 id=256 T=2^20", synth.Q4_K, 1, 256, 1 << 20)]
+
+
+@pytest.mark.parametrize("case", MAXIMA, ids=[c[0] for c in MAXIMA])
+def test_maximum_sizes_all_elements(case):
+    name, type_, od, id_, T = case
+    assert max(od, 1) <= 1 << 21 and id_ <= 1 << 20 and T <= 1 << 20
+    say(f"maximum size {name}: generating")
+    raw, x = synth.case(type_, od, id_, T, seed=3)
+    say(f"maximum size {name}: register + prepass")
+    w = qmm.register_weights(type_, od, id_, raw)
+    qact = gpu_quantize(x)
+    q, dh, s = check_prepass(x, qact)
+    say(f"maximum size {name}: mmq")
+    got = run_mmq(w, qact, T)
+    if id_ == 1 << 20:
+        na = torch.full((T, od), float("nan"), dtype=torch.float32, device="cuda")
+        qmm.mmq_noalloc(w, qact, T, na)
+        torch.cuda.synchronize()
+        assert np.array_equal(na.cpu().numpy().view(np.uint32), got.view(np.uint32)), "noalloc differs"
+    w.release()
+    say(f"maximum size {name}: oracle")
+    ref, A = oracle.mmq_parallel(synth.block_format(type_), raw, od, id_, q, dh, s)
+    check_close(got, ref, A, name)
+
+
 # --------------------------------------------------------------------------
 # properties
 # --------------------------------------------------------------------------
