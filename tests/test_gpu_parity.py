@@ -189,9 +189,10 @@ def _set_f16(raw, lo, bits):
 
 @pytest.mark.parametrize("type_", [synth.Q4_K, synth.Q6_K, synth.Q4_K_PACKED], ids=["q4_K", "q6_K", "q4_K packed"])
 def test_extreme_block_scales(type_):
-    """Super-block scales of either sign, huge (60000) and subnormal (2^-24):
-    the planes stay byte-exact and the MMQ stays within the tolerance.  Blocks
-    are drawn as usual, then their f16 d (and q4_K dmin) bits are rewritten."""
+    """Super-block scales of either sign, huge (60000), subnormal (2^-24) and
+    zero of either sign (a super-block that contributes nothing): the planes
+    stay byte-exact and the MMQ stays within the tolerance.  Blocks are drawn
+    as usual, then their f16 d (and q4_K dmin) bits are rewritten."""
     od, id_, T = 90, 1024, 70
     say(f"extreme block scales {synth.TYPE_NAMES[type_]}")
     rng = np.random.default_rng(9)
@@ -205,6 +206,8 @@ def test_extreme_block_scales(type_):
         bits = np.where(pick < 0.3, bits | 0x8000, bits)                 # negative
         bits = np.where((pick >= 0.3) & (pick < 0.35), 0x7B53, bits)     # 60000
         bits = np.where((pick >= 0.35) & (pick < 0.40), 0x0001, bits)    # 2^-24
+        bits = np.where((pick >= 0.40) & (pick < 0.44), 0x0000, bits)    # +0
+        bits = np.where((pick >= 0.44) & (pick < 0.47), 0x8000, bits)    # -0
         _set_f16(raw, lo, bits)
     raw = raw.reshape(-1)
     w = qmm.register_weights(type_, od, id_, raw)
